@@ -1,0 +1,365 @@
+"""Float64 CPU oracle for per-KV-head attention-matching KV compaction.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or links this
+package: only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
+It shares no code with the HIP path; both sides receive the same seeded inputs.
+
+What is computed, per head problem (all arithmetic in float64; bf16 inputs are upcast
+exactly before they arrive here):
+
+  S1  full-cache statistics. Scores s_ij = scale * q_i . k_j over the keys visible to query
+      i; lse_i = log sum_j exp(s_ij); O_i = sum_j exp(s_ij - lse_i) v_j.
+      ("Latent Compaction with Test-Time Training", §3 Preliminaries, Eq. 1: attention
+      output A(q) and normalizer Z(q); App. A.2 "Normalizer Computation and Storage":
+      masked scores, logsumexp and softmax in a wider float type.)
+  S2  per-key attention statistics of p_ij = exp(s_ij - lse_i): the column sum, sum of
+      squares and maximum over queries. The selection score is the RMS over queries by
+      default (same paper, App. A.3: the Attention Matching baseline uses RMS
+      attention-based key selection); MEAN and MAX (Eq. 6) are options.
+  S3  C_k = the t keys of highest score ("Compaction" blog, §Fast KV Compaction via
+      Attention Matching, step 1; C_k is a subset of K). Ties go to the lower key index;
+      indices are returned ascending because compacted entries keep their positions
+      (Latent Compaction, §3.1 "Handling Subsequent Tokens": no renumbering).
+  S4/S5  beta from the mass equations by non-negative least squares on w = exp(beta)
+      (blog, §Choosing beta, mass-matching equation for every reference query). The
+      default divides equation i by its full-cache mass Z_i, so the design entries are
+      M_ij = p_{i, idx_j} and the target is 1; the literal (absolute) form is an option.
+  S6/S7  C_v from the output equations by ridge least squares (blog, §Choosing C_v):
+      A_i = softmax over the visible selected keys of (scale q_i . C_k + beta), and
+      C_v = argmin ||A C - O||_F^2 + lambda ||C||_F^2.
+  E   the compacted attention itself, to evaluate any (idx, beta, C_v): biased scores
+      l(q) = scale K_cmp q + b (Latent Compaction §3.1, Eq. 2), output Eq. 3 and
+      normalizer Z_cmp = 1^T exp(l) (Eq. 4), plus the residuals compared in parity.
+
+Readings where the pages are silent (each is listed with its reason in the design notes):
+masked keys are excluded (exp(-inf) = 0), which equals the pseudocode's finfo.min fill
+whenever a row keeps at least one visible entry (key 0 is visible to every query); the
+RMS divisor is n for every key; w_j = 0 gives beta_j = -inf; a query with no visible
+selected key contributes a zero row to A; lambda is absolute on the summed normal
+equations; natural log/exp throughout, with the 1/sqrt(d) scale applied to q.k.
+
+Parity pins live in tests/test_oracle_*.py. The weights w themselves are parity unpinned
+on rank-deficient designs (the minimiser is not unique there; the fitted mass vector Mw
+is, and that is what is pinned and compared).
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.linalg
+import scipy.optimize
+
+SCORE_MODES = ("rms", "mean", "max")
+MASS_MODES = ("relative", "absolute")
+
+
+# --------------------------------------------------------------------------------------
+# visibility
+# --------------------------------------------------------------------------------------
+def visible(rows: np.ndarray, keys: np.ndarray, causal: bool, group: int) -> np.ndarray:
+    """Boolean [len(rows), len(keys)]: key position keys[j] is visible to query rows[i].
+
+    Causal workloads place query i at position i // group (group = query heads per KV
+    head, queries ordered position-major) and let it see keys at positions <= its own
+    (Latent Compaction §3 Preliminaries: the index set I of causally visible entries).
+    """
+    rows = np.asarray(rows)
+    keys = np.asarray(keys)
+    if not causal:
+        return np.ones((rows.size, keys.size), dtype=bool)
+    return keys[None, :] <= (rows // group)[:, None]
+
+
+def _chunks(n: int, T: int, budget: int = 1 << 24):
+    step = max(1, min(n, budget // max(T, 1)))
+    for a in range(0, n, step):
+        yield a, min(n, a + step)
+
+
+# --------------------------------------------------------------------------------------
+# S1 + S2: full-cache statistics
+# --------------------------------------------------------------------------------------
+def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True):
+    """lse [n], O [n, d] (or None) and per-key (sum p, sum p^2, max p) over queries.
+
+    Q [n, d], K and V [T, d], all float64. p_ij = exp(s_ij - lse_i) for visible pairs, 0
+    otherwise. Queries are processed in chunks only to bound memory.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    n, T = Q.shape[0], K.shape[0]
+    lse = np.empty(n)
+    O = np.empty((n, V.shape[1])) if want_O else None
+    colsum = np.zeros(T)
+    colsq = np.zeros(T)
+    colmax = np.zeros(T)
+    keys = np.arange(T)
+    for a, b in _chunks(n, T):
+        s = scale * (Q[a:b] @ K.T)
+        vis = visible(np.arange(a, b), keys, causal, group)
+        s = np.where(vis, s, -np.inf)
+        m = s.max(axis=1)
+        lse[a:b] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        p = np.exp(s - lse[a:b, None])
+        if want_O:
+            O[a:b] = p @ V
+        colsum += p.sum(axis=0)
+        colsq += (p * p).sum(axis=0)
+        np.maximum(colmax, p.max(axis=0), out=colmax)
+    return lse, O, (colsum, colsq, colmax)
+
+
+def attention_rows(Q, K, V, scale, rows, causal=False, group=1):
+    """lse and O for selected query rows only (used to sample large problems)."""
+    rows = np.asarray(rows)
+    s = scale * (np.asarray(Q, np.float64)[rows] @ np.asarray(K, np.float64).T)
+    s = np.where(visible(rows, np.arange(K.shape[0]), causal, group), s, -np.inf)
+    m = s.max(axis=1)
+    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    O = np.exp(s - lse[:, None]) @ np.asarray(V, np.float64)
+    return lse, O
+
+
+def key_score(stats, mode: str, n: int) -> np.ndarray:
+    """Selection statistic per key: RMS (default), MEAN or MAX of p over the n queries."""
+    colsum, colsq, colmax = stats
+    if mode == "rms":
+        return np.sqrt(colsq / n)
+    if mode == "mean":
+        return colsum / n
+    if mode == "max":
+        return colmax.copy()
+    raise ValueError(mode)
+
+
+# --------------------------------------------------------------------------------------
+# S3: top-t selection
+# --------------------------------------------------------------------------------------
+def select_top(score: np.ndarray, t: int) -> np.ndarray:
+    """Indices of the t largest scores (ties -> lower index), returned ascending."""
+    score = np.asarray(score)
+    order = np.lexsort((np.arange(score.size), -score))
+    return np.sort(order[:t]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------------------
+# S4: the mass design
+# --------------------------------------------------------------------------------------
+def mass_design(Q, Ck, idx, lse, scale, causal=False, group=1, mode="relative"):
+    """Design matrix M [n, t] and target b [n] of the mass equations.
+
+    Mass equation for query i: sum_j exp(s_i,c_j + beta_j) ~= Z_i (blog, §Choosing beta).
+    relative: divide by Z_i  -> M_ij = exp(s_i,c_j - lse_i), b_i = 1.
+    absolute: divide by exp(c), c = max_i lse_i -> M_ij = exp(s_i,c_j - c), b_i = exp(lse_i - c).
+    Compacted keys keep their positions, so the causal mask uses idx.
+    """
+    Q = np.asarray(Q, np.float64)
+    s = scale * (Q @ np.asarray(Ck, np.float64).T)
+    vis = visible(np.arange(Q.shape[0]), np.asarray(idx), causal, group)
+    if mode == "relative":
+        M = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[:, None]), 0.0)
+        b = np.ones(Q.shape[0])
+    elif mode == "absolute":
+        c = lse.max()
+        M = np.where(vis, np.exp(np.where(vis, s, 0.0) - c), 0.0)
+        b = np.exp(lse - c)
+    else:
+        raise ValueError(mode)
+    return M, b
+
+
+# --------------------------------------------------------------------------------------
+# S5: non-negative least squares
+# --------------------------------------------------------------------------------------
+def nnls_gram(G: np.ndarray, h: np.ndarray, tol: float | None = None):
+    """Lawson-Hanson active-set NNLS on the normal equations.
+
+    Minimises f(w) = 1/2 w^T G w - h^T w over w >= 0, where G = M^T M and h = M^T b, which
+    is 1/2 ||M w - b||^2 up to a constant. The passive set P holds the free variables;
+    each outer step frees the variable with the largest dual u_j = (h - G w)_j, and the
+    inner loop steps toward the unconstrained minimiser on P, dropping variables that
+    reach zero, until that minimiser is strictly positive.
+    """
+    G = np.asarray(G, np.float64)
+    h = np.asarray(h, np.float64)
+    t = h.size
+    if tol is None:
+        tol = 1e-12 * max(1.0, float(np.abs(h).max())) * max(1.0, float(np.abs(np.diag(G)).max()))
+    w = np.zeros(t)
+    P = np.zeros(t, dtype=bool)
+    barred = np.zeros(t, dtype=bool)
+    u = h - G @ w
+    for _ in range(4 * t + 10):
+        cand = (~P) & (~barred) & (u > tol)
+        if not cand.any():
+            break
+        j = int(np.argmax(np.where(cand, u, -np.inf)))
+        P[j] = True
+        for _inner in range(4 * t + 10):
+            ip = np.flatnonzero(P)
+            z = np.zeros(t)
+            z[ip] = _spd_solve(G[np.ix_(ip, ip)], h[ip])
+            if np.all(z[ip] > 0):
+                w = z
+                break
+            neg = ip[z[ip] <= 0]
+            alpha = np.min(w[neg] / (w[neg] - z[neg]))
+            w = w + alpha * (z - w)
+            drop = P & (w <= 1e-300)
+            drop[neg[np.argmin(w[neg] / (w[neg] - z[neg]))]] = True
+            P &= ~drop
+            w[~P] = 0.0
+            if not P.any():
+                break
+        u = h - G @ w
+        # a freed variable that could not stay positive is numerically dependent
+        if not P[j]:
+            barred[j] = True
+        else:
+            barred[:] = False
+    return w
+
+
+def _spd_solve(A, b):
+    try:
+        c = scipy.linalg.cho_factor(A, lower=True, check_finite=False)
+        x = scipy.linalg.cho_solve(c, b, check_finite=False)
+        if np.all(np.isfinite(x)):
+            return x
+    except np.linalg.LinAlgError:
+        pass
+    return np.linalg.lstsq(A, b, rcond=None)[0]
+
+
+def nnls_box(M, b, lo: float, hi: float):
+    """Bounded least squares min ||M w - b|| over lo <= w <= hi (textbook BVLS)."""
+    r = scipy.optimize.lsq_linear(M, b, bounds=(lo, hi), method="bvls", tol=1e-14,
+                                  max_iter=10 * M.shape[1] + 100)
+    return r.x
+
+
+def fit_beta(M, b, lo: float = 0.0, hi: float = np.inf):
+    """w = argmin_{lo<=w<=hi} ||M w - b||^2 and beta = log w (w = 0 -> -inf)."""
+    if lo == 0.0 and np.isinf(hi):
+        G = M.T @ M
+        h = M.T @ b
+        w = nnls_gram(G, h)
+    else:
+        w = nnls_box(M, b, lo, hi)
+    with np.errstate(divide="ignore"):
+        beta = np.log(w)
+    return w, beta
+
+
+def nnls_kkt_residual(G, h, w, lo: float = 0.0, hi: float = np.inf) -> float:
+    """Largest violation of the box-NNLS optimality conditions, g = G w - h.
+
+    Free variables need g_j = 0; variables at the lower bound need g_j >= 0; variables at
+    the upper bound need g_j <= 0; and lo <= w <= hi.
+    """
+    g = G @ w - h
+    atlo = w <= lo + 1e-300 if lo == 0 else np.isclose(w, lo, rtol=1e-12, atol=0)
+    athi = np.isfinite(hi) & np.isclose(w, hi, rtol=1e-12, atol=0)
+    free = ~atlo & ~athi
+    v = 0.0
+    if free.any():
+        v = max(v, float(np.abs(g[free]).max()))
+    if atlo.any():
+        v = max(v, float(np.maximum(-g[atlo], 0).max()))
+    if np.any(athi):
+        v = max(v, float(np.maximum(g[athi], 0).max()))
+    v = max(v, float(np.maximum(lo - w, 0).max()), float(np.maximum(w - hi, 0).max()))
+    return v
+
+
+# --------------------------------------------------------------------------------------
+# S6 + S7: the value fit
+# --------------------------------------------------------------------------------------
+def value_design(M, w):
+    """A_i = (w * M_i) / (M_i . w): the compacted softmax weights with beta = log w.
+
+    Rows with no visible selected key of positive weight are zero.
+    """
+    Dm = M @ w
+    num = M * w[None, :]
+    A = np.zeros_like(M)
+    ok = Dm > 0
+    A[ok] = num[ok] / Dm[ok, None]
+    return A
+
+
+def fit_values(A, Y, lam: float):
+    """C_v = (A^T A + lam I)^{-1} A^T Y by Cholesky and two triangular solves."""
+    t = A.shape[1]
+    G = A.T @ A + lam * np.eye(t)
+    R = A.T @ Y
+    c = scipy.linalg.cho_factor(G, lower=True)
+    return scipy.linalg.cho_solve(c, R)
+
+
+# --------------------------------------------------------------------------------------
+# E: compacted attention and residuals
+# --------------------------------------------------------------------------------------
+def compacted_attention(Q, Ck, idx, beta, Cv, scale, causal=False, group=1):
+    """log Z_cmp [n] and A_cmp [n, d] of the biased compacted cache (Eq. 2-4)."""
+    Q = np.asarray(Q, np.float64)
+    l = scale * (Q @ np.asarray(Ck, np.float64).T) + np.asarray(beta, np.float64)[None, :]
+    vis = visible(np.arange(Q.shape[0]), np.asarray(idx), causal, group)
+    l = np.where(vis, l, -np.inf)
+    m = l.max(axis=1)
+    fin = np.isfinite(m)
+    logz = np.full(Q.shape[0], -np.inf)
+    A = np.zeros((Q.shape[0], np.asarray(Cv).shape[1]))
+    if fin.any():
+        lf = l[fin] - m[fin, None]
+        e = np.exp(lf)
+        z = e.sum(axis=1)
+        logz[fin] = m[fin] + np.log(z)
+        A[fin] = (e / z[:, None]) @ np.asarray(Cv, np.float64)
+    return logz, A
+
+
+def residuals(lse, O, logz_cmp, A_cmp):
+    """R_mass = mean_i (Z_cmp,i / Z_i - 1)^2 and R_out = sum ||A_cmp - O||^2 / sum ||O||^2."""
+    ratio = np.exp(logz_cmp - lse)
+    r_mass = float(np.mean((ratio - 1.0) ** 2))
+    r_out = float(((A_cmp - O) ** 2).sum() / (O ** 2).sum())
+    return r_mass, r_out
+
+
+def mass_residual(M, b, w) -> float:
+    """||M w - b||^2 / n for the relative design (b = 1) or the absolute one."""
+    r = M @ w - b
+    return float(r @ r / M.shape[0])
+
+
+def output_residual(A, Y, Cv) -> float:
+    R = A @ Cv - Y
+    return float((R * R).sum() / (Y * Y).sum())
+
+
+# --------------------------------------------------------------------------------------
+# the whole per-head pipeline
+# --------------------------------------------------------------------------------------
+def compact_head(Q, K, V, t, scale, causal=False, group=1, score="rms", mass="relative",
+                 w_lo=0.0, w_hi=np.inf, ridge_lambda=1e-3, idx=None):
+    """S1..S7 for one head. Returns a dict with every intermediate the parity tests use.
+
+    If idx is given, selection is skipped and the fits run on that key set.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    n = Q.shape[0]
+    lse, O, stats = full_cache_stats(Q, K, V, scale, causal, group)
+    sc = key_score(stats, score, n)
+    if idx is None:
+        idx = select_top(sc, t)
+    idx = np.asarray(idx, np.int64)
+    Ck = K[idx]
+    M, b = mass_design(Q, Ck, idx, lse, scale, causal, group, mass)
+    w, beta = fit_beta(M, b, w_lo, w_hi)
+    A = value_design(M, w)
+    Cv = fit_values(A, O, ridge_lambda)
+    return dict(lse=lse, O=O, stats=stats, score=sc, idx=idx, Ck=Ck, M=M, b=b, w=w,
+                beta=beta, A=A, Cv=Cv,
+                r_mass=mass_residual(M, b, w), r_out=output_residual(A, O, Cv))

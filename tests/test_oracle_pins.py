@@ -1,0 +1,330 @@
+"""Pins of the float64 oracle against facts the pages and the mathematics fix.
+
+Each test names the plausible mistake it would catch. None of these re-types the
+oracle's own formula: they compare against textbook routines (scipy), brute force over
+tiny inputs, closed forms and invariants.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import scipy.optimize
+import scipy.special
+
+from oracle import am_oracle as O
+
+RNG = np.random.default_rng(1234)
+
+
+def _qkv(n, T, d, rng=RNG, qscale=1.0):
+    Q = rng.standard_normal((n, d)) * qscale
+    K = rng.standard_normal((T, d)) * rng.lognormal(0, 0.5, d)
+    V = rng.standard_normal((T, d))
+    return Q, K, V
+
+
+def _loop_stats(Q, K, V, scale, causal, group):
+    """Per-query brute force with scipy's textbook softmax/logsumexp."""
+    n, T = Q.shape[0], K.shape[0]
+    lse = np.empty(n)
+    Oo = np.empty((n, V.shape[1]))
+    P = np.zeros((n, T))
+    for i in range(n):
+        nv = (i // group + 1) if causal else T
+        s = np.array([scale * float(np.dot(Q[i], K[j])) for j in range(nv)])
+        lse[i] = scipy.special.logsumexp(s)
+        p = scipy.special.softmax(s)
+        Oo[i] = p @ V[:nv]
+        P[i, :nv] = p
+    return lse, Oo, P
+
+
+# ---------------------------------------------------------------------------- S1 / S2
+@pytest.mark.parametrize("causal,group", [(False, 1), (True, 1), (True, 4), (False, 4)])
+def test_stats_match_textbook_softmax(causal, group):
+    # catches: missing scale, transposed operand, causal off-by-one, wrong lse base
+    T, d = 13, 8
+    n = T * group
+    Q, K, V = _qkv(n, T, d)
+    scale = 1 / np.sqrt(d)
+    lse, Oo, stats = O.full_cache_stats(Q, K, V, scale, causal, group)
+    lse2, O2, P = _loop_stats(Q, K, V, scale, causal, group)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Oo, O2, rtol=1e-12, atol=1e-12)
+    # per-key statistics by brute force over the full probability matrix
+    np.testing.assert_allclose(stats[0], P.sum(0), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(stats[1], (P ** 2).sum(0), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(stats[2], P.max(0), rtol=1e-12, atol=1e-15)
+    # MAX mode is Eq. 6: max over queries of softmax(s K q)_i (non-causal case)
+    if not causal:
+        sm = scipy.special.softmax(scale * Q @ K.T, axis=1)
+        np.testing.assert_allclose(O.key_score(stats, "max", n), sm.max(0), rtol=1e-12)
+    np.testing.assert_allclose(O.key_score(stats, "rms", n), np.sqrt((P ** 2).mean(0)), rtol=1e-12)
+    np.testing.assert_allclose(O.key_score(stats, "mean", n), P.mean(0), rtol=1e-12)
+
+
+def test_stats_chunked_equals_single_block():
+    # catches: chunk-boundary bugs in the query loop (budget forces many chunks)
+    Q, K, V = _qkv(300, 50, 8)
+    a = O.full_cache_stats(Q, K, V, 0.3, True, 3)
+    import oracle.am_oracle as mod
+    saved = mod._chunks
+    try:
+        mod._chunks = lambda n, T, budget=0: [(0, n)]
+        b = O.full_cache_stats(Q, K, V, 0.3, True, 3)
+    finally:
+        mod._chunks = saved
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13)
+    for x, y in zip(a[2], b[2]):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-16)
+
+
+def test_shift_invariance_and_value_linearity():
+    # adding c to every score of a row: O unchanged, lse shifted by c (catches max-shift bugs)
+    Q, K, V = _qkv(20, 30, 6)
+    scale = 0.37
+    c = 5.0
+    Q2 = np.hstack([Q, np.full((20, 1), c / scale)])
+    K2 = np.hstack([K, np.ones((30, 1))])
+    l1, O1, _ = O.full_cache_stats(Q, K, V, scale)
+    l2, O2, _ = O.full_cache_stats(Q2, K2, V, scale)
+    np.testing.assert_allclose(l2, l1 + c, atol=1e-12)
+    np.testing.assert_allclose(O2, O1, atol=1e-12)
+    _, O3, _ = O.full_cache_stats(Q, K, 2.5 * V, scale)
+    np.testing.assert_allclose(O3, 2.5 * O1, atol=1e-12)
+
+
+def test_large_scores_do_not_overflow():
+    # scores near 700 would overflow exp without the max shift
+    Q, K, V = _qkv(5, 7, 4)
+    l, Oo, _ = O.full_cache_stats(Q * 400, K, V, 1.0)
+    l2, O2, _ = _loop_stats(Q * 400, K, V, 1.0, False, 1)
+    np.testing.assert_allclose(l, l2, rtol=1e-14)
+    np.testing.assert_allclose(Oo, O2, atol=1e-12)
+
+
+def test_attention_rows_matches_full():
+    Q, K, V = _qkv(40, 10, 4)
+    lse, Oo, _ = O.full_cache_stats(Q, K, V, 0.5, True, 4)
+    rows = np.array([0, 3, 17, 39])
+    l2, O2 = O.attention_rows(Q, K, V, 0.5, rows, True, 4)
+    np.testing.assert_allclose(l2, lse[rows], atol=1e-13)
+    np.testing.assert_allclose(O2, Oo[rows], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------- S3
+def test_select_top_bruteforce_and_ties():
+    # I4(a): idx = lexicographically smallest argmax over all t-subsets of the score sum
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        T = int(rng.integers(2, 11))
+        t = int(rng.integers(1, min(4, T) + 1))
+        sc = rng.integers(0, 4, T).astype(float) / 3.0  # many exact ties
+        best, best_set = -1.0, None
+        for S in itertools.combinations(range(T), t):  # lexicographic order
+            v = sc[list(S)].sum()
+            if v > best + 1e-15:
+                best, best_set = v, S
+        got = O.select_top(sc, t)
+        assert list(got) == sorted(best_set), (sc, t, got, best_set)
+        assert np.all(np.diff(got) > 0)
+
+
+def test_select_top_tie_goes_to_lower_index():
+    sc = np.array([0.5, 0.9, 0.5, 0.5, 0.1])
+    assert list(O.select_top(sc, 2)) == [0, 1]
+    assert list(O.select_top(sc, 3)) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------------------- S5 NNLS
+def _bruteforce_nnls(M, b):
+    """Enumerate every support, solve unconstrained LS on it, keep feasible minimum."""
+    t = M.shape[1]
+    best, bw = np.inf, None
+    for mask in itertools.product([0, 1], repeat=t):
+        S = np.flatnonzero(mask)
+        w = np.zeros(t)
+        if S.size:
+            w[S] = np.linalg.lstsq(M[:, S], b, rcond=None)[0]
+        if np.any(w < -1e-12):
+            continue
+        w = np.maximum(w, 0)
+        f = np.sum((M @ w - b) ** 2)
+        if f < best - 1e-14:
+            best, bw = f, w
+    return bw, best
+
+
+def test_nnls_bruteforce_tiny():
+    # I4(b): the active-set NNLS equals enumeration of all 2^t supports
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        n = int(rng.integers(3, 25))
+        t = int(rng.integers(1, 5))
+        M = rng.standard_normal((n, t))
+        if trial % 2:
+            M = np.abs(M)
+        b = rng.standard_normal(n) + (trial % 3 == 0) * 2
+        w, _ = O.fit_beta(M, b)
+        wb, fb = _bruteforce_nnls(M, b)
+        f = np.sum((M @ w - b) ** 2)
+        assert f <= fb * (1 + 1e-10) + 1e-12
+        np.testing.assert_allclose(M @ w, M @ wb, atol=1e-8)
+        assert np.all(w >= 0)
+
+
+def test_nnls_matches_scipy_and_kkt():
+    # textbook routine (scipy's Lawson-Hanson) on medium problems; I3 KKT holds
+    rng = np.random.default_rng(5)
+    for n, t in [(200, 30), (500, 64), (100, 80)]:
+        M = np.abs(rng.standard_normal((n, t))) ** 2
+        b = np.ones(n) + 0.3 * rng.standard_normal(n)
+        w, beta = O.fit_beta(M, b)
+        ws, _ = scipy.optimize.nnls(M, b)
+        np.testing.assert_allclose(M @ w, M @ ws, atol=1e-8)
+        G, h = M.T @ M, M.T @ b
+        assert O.nnls_kkt_residual(G, h, w) <= 1e-9 * np.abs(h).max()
+        assert np.all(np.isneginf(beta[w == 0]))
+        np.testing.assert_allclose(np.exp(beta[w > 0]), w[w > 0], rtol=1e-14)
+
+
+def test_nnls_rank_deficient_unique_mass():
+    # duplicated columns: w is not unique, but M w is (I6 / reading A7)
+    rng = np.random.default_rng(9)
+    M = np.abs(rng.standard_normal((60, 5)))
+    M = np.hstack([M, M[:, :2]])
+    b = np.ones(60)
+    w, _ = O.fit_beta(M, b)
+    ws, _ = scipy.optimize.nnls(M, b)
+    np.testing.assert_allclose(M @ w, M @ ws, atol=1e-9)
+    assert O.nnls_kkt_residual(M.T @ M, M.T @ b, w) <= 1e-9
+
+
+def test_nnls_box_bounds_and_kkt():
+    rng = np.random.default_rng(3)
+    M = np.abs(rng.standard_normal((80, 10)))
+    b = 1 + rng.standard_normal(80)
+    lo, hi = np.exp(-3), np.exp(3)
+    w, _ = O.fit_beta(M, b, lo, hi)
+    assert np.all(w >= lo - 1e-12) and np.all(w <= hi + 1e-12)
+    assert O.nnls_kkt_residual(M.T @ M, M.T @ b, w, lo, hi) <= 1e-8
+
+
+# ---------------------------------------------------------------------------- S7 ridge
+def test_ridge_equals_stacked_lstsq_for_every_subset():
+    # I4(c): (A^T A + lam I)^-1 A^T Y equals QR least squares on [A; sqrt(lam) I]
+    rng = np.random.default_rng(21)
+    A_full = np.abs(rng.standard_normal((20, 6)))
+    Y = rng.standard_normal((20, 3))
+    for lam in (0.0, 1e-3, 0.5):
+        for t in range(1, 4):
+            for S in itertools.combinations(range(6), t):
+                A = A_full[:, S]
+                C = O.fit_values(A, Y, lam)
+                stacked = np.vstack([A, np.sqrt(lam) * np.eye(t)])
+                rhs = np.vstack([Y, np.zeros((t, 3))])
+                C2 = np.linalg.lstsq(stacked, rhs, rcond=None)[0]
+                np.testing.assert_allclose(C, C2, rtol=1e-9, atol=1e-10)
+
+
+def test_t1_closed_forms():
+    # I5: t = 1 -> w = m.1 / m.m and C_v = a^T Y / (a^T a + lam), a = 0/1 visibility
+    rng = np.random.default_rng(4)
+    T, d, group = 9, 4, 2
+    Q, K, V = _qkv(T * group, T, d, rng)
+    r = O.compact_head(Q, K, V, 1, 0.5, True, group, ridge_lambda=0.01)
+    m = r["M"][:, 0]
+    assert r["w"][0] == pytest.approx(m.sum() / (m @ m), rel=1e-12)
+    a = (m > 0).astype(float)
+    np.testing.assert_allclose(r["A"][:, 0], a, atol=0)
+    np.testing.assert_allclose(r["Cv"][0], a @ r["O"] / (a @ a + 0.01), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------- invariants
+@pytest.mark.parametrize("causal,group", [(False, 1), (True, 2)])
+def test_I1_full_budget_reproduces_cache(causal, group):
+    # with t = T, C_k = K, beta = 0, C_v = V the evaluator gives back O and lse exactly,
+    # and the fits recover w = 1 and (lambda = 0) C_v = V
+    rng = np.random.default_rng(31)
+    T, d = 12, 6
+    n = max(T * group, 3 * T)
+    n -= n % group
+    Q, K, V = _qkv(n, T, d, rng)
+    sc = 1 / np.sqrt(d)
+    lse, Oo, _ = O.full_cache_stats(Q, K, V, sc, causal, group)
+    logz, A = O.compacted_attention(Q, K, np.arange(T), np.zeros(T), V, sc, causal, group)
+    np.testing.assert_allclose(logz, lse, atol=1e-12)
+    np.testing.assert_allclose(A, Oo, atol=1e-12)
+    r = O.compact_head(Q, K, V, T, sc, causal, group, ridge_lambda=0.0)
+    assert list(r["idx"]) == list(range(T))
+    np.testing.assert_allclose(r["w"], 1.0, atol=1e-9)
+    np.testing.assert_allclose(r["Cv"], V, atol=1e-7)
+    assert r["r_mass"] < 1e-18 and r["r_out"] < 1e-14
+
+
+def test_I2_zero_query_mass():
+    # q = 0: every score is 0, so Z = number of visible keys (log T non-causal) and the
+    # compacted mass is sum_j exp(beta_j) over the visible compacted keys
+    rng = np.random.default_rng(8)
+    T, d = 10, 4
+    Q = np.zeros((T * 2, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    lse, _, _ = O.full_cache_stats(Q, K, V, 0.5)
+    np.testing.assert_allclose(lse, np.log(T), atol=1e-14)
+    lse_c, _, _ = O.full_cache_stats(Q, K, V, 0.5, True, 2)
+    np.testing.assert_allclose(lse_c, np.log(np.arange(2 * T) // 2 + 1), atol=1e-14)
+    beta = rng.standard_normal(4)
+    idx = np.array([0, 3, 5, 9])
+    logz, _ = O.compacted_attention(Q, K[idx], idx, beta, V[idx], 0.5)
+    np.testing.assert_allclose(logz, np.log(np.exp(beta).sum()), atol=1e-14)
+    # and the fit: constant rows, so NNLS reaches zero residual with sum(w) = T
+    r = O.compact_head(Q, K, V, 4, 0.5)
+    assert r["r_mass"] < 1e-20
+    assert r["w"].sum() == pytest.approx(T, rel=1e-10)
+
+
+def test_I6_permutation_equivariance():
+    rng = np.random.default_rng(12)
+    Q, K, V = _qkv(30, 15, 5, rng)
+    perm = rng.permutation(15)
+    a = O.compact_head(Q, K, V, 4, 0.4)
+    b = O.compact_head(Q, K[perm], V[perm], 4, 0.4)
+    inv = np.argsort(perm)
+    np.testing.assert_allclose(b["score"][inv], a["score"], rtol=1e-12)
+    assert sorted(perm[b["idx"]]) == list(a["idx"])
+    assert b["r_mass"] == pytest.approx(a["r_mass"], rel=1e-8)
+    assert b["r_out"] == pytest.approx(a["r_out"], rel=1e-8)
+
+
+def test_residuals_agree_with_evaluator():
+    # the fitted design residuals equal the evaluator's (Eq. 2-4) residuals
+    rng = np.random.default_rng(2)
+    Q, K, V = _qkv(64, 20, 6, rng)
+    for causal, group in [(False, 1), (True, 4)]:
+        Qg = Q if not causal else Q[:80] if Q.shape[0] >= 80 else np.vstack([Q, Q[:16]])
+        r = O.compact_head(Qg, K, V, 5, 0.4, causal, group)
+        logz, A = O.compacted_attention(Qg, r["Ck"], r["idx"], r["beta"], r["Cv"], 0.4, causal, group)
+        rm, ro = O.residuals(r["lse"], r["O"], logz, A)
+        assert rm == pytest.approx(r["r_mass"], rel=1e-9)
+        assert ro == pytest.approx(r["r_out"], rel=1e-9)
+
+
+def test_absolute_mass_mode_is_row_weighting():
+    # the absolute form weights equation i by Z_i: with an exact fit available (t = T)
+    # both forms give w = 1; otherwise the absolute optimum is the weighted LS optimum
+    rng = np.random.default_rng(17)
+    T, d = 8, 4
+    Q, K, V = _qkv(40, T, d, rng)
+    ra = O.compact_head(Q, K, V, T, 0.5, mass="absolute", ridge_lambda=0.0)
+    np.testing.assert_allclose(ra["w"], 1.0, atol=1e-8)
+    lse, _, _ = O.full_cache_stats(Q, K, V, 0.5)
+    idx = np.array([1, 4, 6])
+    Mr, _ = O.mass_design(Q, K[idx], idx, lse, 0.5, mode="relative")
+    Ma, ba = O.mass_design(Q, K[idx], idx, lse, 0.5, mode="absolute")
+    z = np.exp(lse - lse.max())
+    np.testing.assert_allclose(Ma, Mr * z[:, None], rtol=1e-12)
+    wa, _ = O.fit_beta(Ma, ba)
+    ws, _ = scipy.optimize.nnls(Mr * z[:, None], z)
+    np.testing.assert_allclose(Ma @ wa, Ma @ ws, atol=1e-10)
