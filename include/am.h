@@ -1,0 +1,184 @@
+/*
+ * am.h - C ABI of the MI355X (gfx950) attention-matching KV compaction library.
+ *
+ * Per KV head and a set of n reference queries, the library computes the full-cache
+ * statistics (row log-normalizer, attention output, per-key attention score), selects
+ * t of the T keys, fits per-key biases beta so that the compacted attention mass matches
+ * the full cache, and fits compacted values C_v so that the compacted attention output
+ * matches it. The problem statement followed is the one in the "Compaction" blog post,
+ * §Fast KV Compaction via Attention Matching: K, V in R^{T x d} become C_k, C_v in
+ * R^{t x d} with C_k a subset of K, plus beta in R^t; the three steps are highest-attention
+ * key selection, NNLS on the mass equations for w = exp(beta), and least squares on the
+ * output equations for C_v. Attention follows "Latent Compaction with Test-Time Training",
+ * §3 Preliminaries (Eq. 1) and §3.1 (Eq. 2-4, biased compacted attention).
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is a DEVICE pointer owned by the caller, 16-byte aligned.
+ *     The library keeps no pointer after a call returns and allocates no device memory:
+ *     scratch comes from the caller's workspace (size from am_workspace_bytes).
+ *   - Tensors are dense row-major, batched over h independent head problems:
+ *     Q [h, n, d], K and V [h, T, d] in the problem dtype; lse [h, n] f32; O [h, n, d] f32;
+ *     key_score [h, T] f32; idx [h, t] int32; C_k [h, t, d] problem dtype; beta [h, t] f32;
+ *     C_v [h, t, d] f32.
+ *   - Causal problems put query i at position i / group and let it see keys
+ *     0 .. i / group; compacted keys keep their original positions (Latent Compaction,
+ *     §3.1 "Handling Subsequent Tokens": no renumbering), so the same rule masks them.
+ *   - Calls only ENQUEUE work on `stream` (NULL = the default stream) and never
+ *     synchronize. Inputs, outputs and workspace must stay alive until the stream has
+ *     passed the work. Calls on different streams with disjoint buffers are independent.
+ *   - Arguments are validated on the host before any launch. A failed validation returns
+ *     an error and launches nothing. Conditions found on the device (NNLS not converged,
+ *     non-positive Cholesky pivot, non-finite values) are reported per head through the
+ *     optional head_status array (AM_HEAD_* bits), never by a return code.
+ *   - Results are deterministic: fixed reduction orders and no floating-point atomics.
+ */
+#ifndef AM_H
+#define AM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* am_stream_t;
+
+typedef enum {
+  AM_OK = 0,
+  AM_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, t outside [1, T], ... */
+  AM_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d not 64/128) */
+  AM_ERR_WORKSPACE = -3,   /* ws_bytes smaller than am_workspace_bytes() */
+  AM_ERR_DEVICE = -4       /* a HIP launch or device query failed */
+} am_status;
+
+typedef enum { AM_F32 = 0, AM_BF16 = 1 } am_dtype;
+
+/* Per-key selection statistic of p_ij = exp(s_ij - lse_i) over the n queries.
+ * RMS sqrt(sum_i p^2 / n) is the one the Attention Matching baseline uses (Latent
+ * Compaction, App. A.3); MEAN is sum_i p / n; MAX is max_i p (Latent Compaction Eq. 6). */
+typedef enum { AM_SCORE_RMS = 0, AM_SCORE_MEAN = 1, AM_SCORE_MAX = 2 } am_score_mode;
+
+/* Weighting of the mass equations (blog, §Choosing beta). RELATIVE divides equation i by
+ * its full-cache mass Z_i (design M_ij = exp(s_i,c_j - lse_i), target 1). ABSOLUTE keeps
+ * the literal equations, shifted by the largest lse so that they fit fp32. */
+typedef enum { AM_MASS_RELATIVE = 0, AM_MASS_ABSOLUTE = 1 } am_mass_mode;
+
+/* Per-head device status bits (head_status arrays). */
+enum {
+  AM_HEAD_OK = 0,
+  AM_HEAD_NNLS_NOT_CONVERGED = 1, /* KKT tolerance not reached within nnls_max_iter */
+  AM_HEAD_CHOL_PIVOT = 2,         /* non-positive pivot in the ridge Cholesky */
+  AM_HEAD_NONFINITE = 4           /* a non-finite value reached a fit */
+};
+
+typedef struct {
+  int64_t heads;   /* h >= 1 independent head problems */
+  int64_t n;       /* reference queries per head, >= 1 */
+  int64_t T;       /* full-cache keys per head, >= 1 */
+  int64_t d;       /* head dimension: 64 or 128 */
+  int32_t causal;  /* 0 or 1 */
+  int32_t group;   /* queries per position (>= 1); causal problems need n == group * T */
+  float scale;     /* score scale, normally 1 / sqrt(d) */
+  am_dtype dtype;  /* dtype of Q, K, V and C_k */
+} am_problem;
+
+typedef struct {
+  am_score_mode score;   /* key selection statistic (default RMS) */
+  am_mass_mode mass;     /* mass-equation weighting (default RELATIVE) */
+  float w_lo, w_hi;      /* box for w = exp(beta); defaults 0 and +inf */
+  int32_t nnls_max_iter; /* projected-gradient iterations cap (default 500) */
+  float nnls_tol;        /* relative KKT tolerance (default 1e-6) */
+  float ridge_lambda;    /* absolute ridge on A^T A (default 1e-3) */
+} am_options;
+
+/* Fills *opt with the defaults listed above. */
+void am_default_options(am_options* opt);
+
+/*
+ * am_targets - full-cache statistics (Latent Compaction §3 Preliminaries, Eq. 1; the
+ * first step of the blog's §Fast KV Compaction, "keys with the highest attention").
+ *   lse[h, n]       = log sum_{j visible} exp(scale * q_i . k_j)      (natural log)
+ *   O[h, n, d]      = sum_j exp(scale * q_i . k_j - lse_i) v_j        (optional, NULL skips)
+ *   key_score[h, T] = per-key statistic of the mode above over all n queries
+ *                     (optional, NULL skips the second pass)
+ * A fused flash pass produces lse and O; a second pass recomputes the scores with lse
+ * known and reduces them per key.
+ */
+am_status am_targets(const am_problem* p, const void* Q, const void* K, const void* V,
+                     float* lse, float* O, float* key_score, am_score_mode mode,
+                     void* ws, size_t ws_bytes, am_stream_t stream);
+
+/*
+ * am_select_keys - the t keys of largest key_score per head (blog §Fast KV Compaction,
+ * step 1; C_k is a subset of K). Ties go to the lower key index; idx[h, t] is returned in
+ * ascending order. C_k[h, t, d] = K[idx] and, if V_sel is not NULL, V_sel = V[idx]
+ * (bit-exact copies in the problem dtype). Requires 1 <= t <= T.
+ */
+am_status am_select_keys(const am_problem* p, const float* key_score, int64_t t,
+                         const void* K, const void* V, int32_t* idx, void* Ck, void* V_sel,
+                         void* ws, size_t ws_bytes, am_stream_t stream);
+
+/*
+ * am_fit_beta_nnls - beta from the mass equations by non-negative least squares on
+ * w = exp(beta) (blog, §Choosing beta). With M the mass design of the selected keys
+ * (see am_mass_mode), w = argmin_{w_lo <= w <= w_hi} ||M w - b||^2, solved on the device
+ * from the Gram form G = M^T M, M^T b by accelerated projected gradient. beta = log w
+ * (w = 0 gives -inf). lse[h, n] is the natural-log normalizer from am_targets.
+ * Optional outputs: w[h, t]; mass_resid[h] = ||M w - b||^2 / n; head_status[h].
+ */
+am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,
+                           const int32_t* idx, const float* lse, int64_t t,
+                           const am_options* opt, float* beta, float* w, float* mass_resid,
+                           int32_t* head_status, void* ws, size_t ws_bytes, am_stream_t stream);
+
+/*
+ * am_fit_values_ols - C_v from the output equations (blog, §Choosing C_v) by ridge least
+ * squares: A_i = softmax over the visible selected keys of (scale * q_i . C_k + beta)
+ * (Latent Compaction Eq. 2-3), Y = O (targets from am_targets), and
+ * C_v = (A^T A + lambda I)^{-1} A^T Y by Cholesky and two triangular solves.
+ * lambda = 0 is ordinary least squares and needs A of rank t.
+ * Optional outputs: out_resid[h] = ||A C_v - Y||_F^2 / ||Y||_F^2; head_status[h] (OR-ed).
+ */
+am_status am_fit_values_ols(const am_problem* p, const void* Q, const void* Ck,
+                            const int32_t* idx, const float* beta, const float* O, int64_t t,
+                            float ridge_lambda, float* Cv, float* out_resid,
+                            int32_t* head_status, void* ws, size_t ws_bytes,
+                            am_stream_t stream);
+
+/*
+ * am_compact_head - the whole path per head (the per-layer map over H heads of "The
+ * Optimization Landscape of Learning Compacted Context Models", §2 Eq. 1): targets ->
+ * selection -> beta -> C_v. Outputs idx, C_k, beta, C_v; optional lse_out, O_out,
+ * score_out (full-cache statistics), resid_out[2, h] (row 0: mass residuals, row 1: output
+ * residuals, as defined for the two fit calls) and head_status[h].
+ */
+am_status am_compact_head(const am_problem* p, const void* Q, const void* K, const void* V,
+                          int64_t t, const am_options* opt, int32_t* idx, void* Ck,
+                          float* beta, float* Cv, float* lse_out, float* O_out,
+                          float* score_out, float* resid_out, int32_t* head_status,
+                          void* ws, size_t ws_bytes, am_stream_t stream);
+
+/* Which call a workspace size is for. */
+typedef enum {
+  AM_CALL_TARGETS = 0,
+  AM_CALL_SELECT = 1,
+  AM_CALL_FIT_BETA = 2,
+  AM_CALL_FIT_VALUES = 3,
+  AM_CALL_COMPACT = 4
+} am_call;
+
+/* Workspace bytes a call needs for problem p and budget t (0 if the problem is invalid). */
+size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which);
+
+/* Static string for a status code. */
+const char* am_status_str(am_status s);
+
+/* ABI version (incremented on any incompatible change). */
+int am_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AM_H */

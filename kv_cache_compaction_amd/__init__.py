@@ -1,0 +1,282 @@
+"""Attention-matching KV compaction on MI355X: Python binding of the C ABI (libamc.so).
+
+The functions mirror include/am.h one to one. They only marshal arguments: every step of
+the path runs in the library's gfx950 kernels. PyTorch supplies device memory (outputs and
+workspace are torch tensors) and the stream (torch's current stream). If the library is
+missing, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libamc.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "am.h")
+
+AM_OK, AM_ERR_INVALID_ARG, AM_ERR_UNSUPPORTED, AM_ERR_WORKSPACE, AM_ERR_DEVICE = 0, -1, -2, -3, -4
+AM_F32, AM_BF16 = 0, 1
+SCORE_MODES = {"rms": 0, "mean": 1, "max": 2}
+MASS_MODES = {"relative": 0, "absolute": 1}
+CALL_TARGETS, CALL_SELECT, CALL_FIT_BETA, CALL_FIT_VALUES, CALL_COMPACT = range(5)
+HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE = 1, 2, 4
+
+
+class AmProblem(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int64), ("n", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("causal", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+class AmOptions(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_int), ("mass", ctypes.c_int), ("w_lo", ctypes.c_float),
+                ("w_hi", ctypes.c_float), ("nnls_max_iter", ctypes.c_int32),
+                ("nnls_tol", ctypes.c_float), ("ridge_lambda", ctypes.c_float)]
+
+
+class AmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_PROTOS = {
+    "am_abi_version": (ctypes.c_int, []),
+    "am_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "am_default_options": (None, [ctypes.POINTER(AmOptions)]),
+    "am_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AmProblem), ctypes.c_int64, ctypes.c_int]),
+    "am_targets": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P, ctypes.c_int,
+                                  _P, ctypes.c_size_t, _P]),
+    "am_select_keys": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, ctypes.c_int64, _P, _P, _P, _P,
+                                      _P, _P, ctypes.c_size_t, _P]),
+    "am_fit_beta_nnls": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, ctypes.c_int64,
+                                        ctypes.POINTER(AmOptions), _P, _P, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
+    "am_fit_values_ols": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P,
+                                         ctypes.c_int64, ctypes.c_float, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "am_compact_head": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, ctypes.c_int64,
+                                       ctypes.POINTER(AmOptions), _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, ctypes.c_size_t, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/am.h declares."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[a-z_]+\s*\*?\s+)+\*?(am_[a-z_]+)\s*\(", txt, re.M)))
+
+
+def status_str(s: int) -> str:
+    return lib().am_status_str(s).decode()
+
+
+def _check(s: int, what: str):
+    if s != AM_OK:
+        raise AmError(s, what)
+
+
+# ------------------------------------------------------------------------------------------
+# marshalling helpers
+# ------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return AM_BF16
+    if t.dtype == torch.float32:
+        return AM_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _need(t, name, *, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def make_problem(Q, K, *, causal=False, group=1, scale=None) -> AmProblem:
+    h, n, d = Q.shape
+    h2, T, d2 = K.shape
+    if h2 != h or d2 != d:
+        raise ValueError("Q [h, n, d] and K [h, T, d] disagree")
+    if Q.dtype != K.dtype:
+        raise TypeError("Q and K must share a dtype")
+    return AmProblem(h, n, T, d, int(bool(causal)), int(group),
+                     float(1.0 / math.sqrt(d) if scale is None else scale), _dtype_code(Q))
+
+
+def make_options(score="rms", mass="relative", w_lo=0.0, w_hi=math.inf, nnls_max_iter=500,
+                 nnls_tol=1e-6, ridge_lambda=1e-3) -> AmOptions:
+    return AmOptions(SCORE_MODES[score], MASS_MODES[mass], w_lo, w_hi, nnls_max_iter, nnls_tol,
+                     ridge_lambda)
+
+
+def workspace_bytes(p: AmProblem, t: int, which: int) -> int:
+    return int(lib().am_workspace_bytes(ctypes.byref(p), t, which))
+
+
+def _workspace(p, t, which, device):
+    torch = _torch()
+    nb = max(workspace_bytes(p, t, which), 256)
+    return torch.empty(nb, dtype=torch.uint8, device=device), nb
+
+
+# ------------------------------------------------------------------------------------------
+# the five calls
+# ------------------------------------------------------------------------------------------
+def targets(Q, K, V=None, *, causal=False, group=1, scale=None, score="rms", want_O=True,
+            want_score=True):
+    """lse [h, n], O [h, n, d] (or None) and key_score [h, T] (or None)."""
+    torch = _torch()
+    _need(Q, "Q"); _need(K, "K")
+    p = make_problem(Q, K, causal=causal, group=group, scale=scale)
+    if want_O:
+        _need(V, "V", dtype=Q.dtype, shape=K.shape)
+    dev = Q.device
+    lse = torch.empty((p.heads, p.n), dtype=torch.float32, device=dev)
+    O = torch.empty((p.heads, p.n, p.d), dtype=torch.float32, device=dev) if want_O else None
+    sc = torch.empty((p.heads, p.T), dtype=torch.float32, device=dev) if want_score else None
+    ws, nb = _workspace(p, 0, CALL_TARGETS, dev)
+    _check(lib().am_targets(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V) if want_O else None,
+                            _ptr(lse), _ptr(O), _ptr(sc), SCORE_MODES[score], _ptr(ws), nb,
+                            _stream()), "am_targets")
+    return lse, O, sc
+
+
+def select_keys(key_score, K, t, V=None, *, want_vsel=False):
+    """idx [h, t] int32 ascending, C_k [h, t, d] and (optionally) V[idx]."""
+    torch = _torch()
+    _need(K, "K")
+    h, T, d = K.shape
+    _need(key_score, "key_score", dtype=torch.float32, shape=(h, T))
+    p = AmProblem(h, 1, T, d, 0, 1, 1.0 / math.sqrt(d), _dtype_code(K))
+    idx = torch.empty((h, t), dtype=torch.int32, device=K.device)
+    Ck = torch.empty((h, t, d), dtype=K.dtype, device=K.device)
+    Vs = None
+    if want_vsel:
+        _need(V, "V", dtype=K.dtype, shape=K.shape)
+        Vs = torch.empty_like(Ck)
+    _check(lib().am_select_keys(ctypes.byref(p), _ptr(key_score), t, _ptr(K), _ptr(V), _ptr(idx),
+                                _ptr(Ck), _ptr(Vs), None, 0, _stream()), "am_select_keys")
+    return idx, Ck, Vs
+
+
+def fit_beta_nnls(Q, Ck, idx, lse, *, causal=False, group=1, scale=None, options=None,
+                  T=None):
+    """beta [h, t], w [h, t], mass residual [h], head status [h]."""
+    torch = _torch()
+    _need(Q, "Q"); _need(Ck, "Ck", dtype=Q.dtype)
+    h, n, d = Q.shape
+    t = Ck.shape[1]
+    _need(idx, "idx", dtype=torch.int32, shape=(h, t))
+    _need(lse, "lse", dtype=torch.float32, shape=(h, n))
+    Tk = T if T is not None else (n // group if causal else max(t, 1))
+    p = AmProblem(h, n, Tk, d, int(bool(causal)), int(group),
+                  float(1.0 / math.sqrt(d) if scale is None else scale), _dtype_code(Q))
+    o = options or make_options()
+    dev = Q.device
+    beta = torch.empty((h, t), dtype=torch.float32, device=dev)
+    w = torch.empty((h, t), dtype=torch.float32, device=dev)
+    res = torch.empty((h,), dtype=torch.float32, device=dev)
+    st = torch.empty((h,), dtype=torch.int32, device=dev)
+    ws, nb = _workspace(p, t, CALL_FIT_BETA, dev)
+    _check(lib().am_fit_beta_nnls(ctypes.byref(p), _ptr(Q), _ptr(Ck), _ptr(idx), _ptr(lse), t,
+                                  ctypes.byref(o), _ptr(beta), _ptr(w), _ptr(res), _ptr(st),
+                                  _ptr(ws), nb, _stream()), "am_fit_beta_nnls")
+    return beta, w, res, st
+
+
+def fit_values_ols(Q, Ck, idx, beta, O, *, causal=False, group=1, scale=None, ridge_lambda=1e-3,
+                   T=None):
+    """C_v [h, t, d] f32, output residual [h], head status [h]."""
+    torch = _torch()
+    _need(Q, "Q"); _need(Ck, "Ck", dtype=Q.dtype)
+    h, n, d = Q.shape
+    t = Ck.shape[1]
+    _need(idx, "idx", dtype=torch.int32, shape=(h, t))
+    _need(beta, "beta", dtype=torch.float32, shape=(h, t))
+    _need(O, "O", dtype=torch.float32, shape=(h, n, d))
+    Tk = T if T is not None else (n // group if causal else max(t, 1))
+    p = AmProblem(h, n, Tk, d, int(bool(causal)), int(group),
+                  float(1.0 / math.sqrt(d) if scale is None else scale), _dtype_code(Q))
+    dev = Q.device
+    Cv = torch.empty((h, t, d), dtype=torch.float32, device=dev)
+    res = torch.empty((h,), dtype=torch.float32, device=dev)
+    st = torch.empty((h,), dtype=torch.int32, device=dev)
+    ws, nb = _workspace(p, t, CALL_FIT_VALUES, dev)
+    _check(lib().am_fit_values_ols(ctypes.byref(p), _ptr(Q), _ptr(Ck), _ptr(idx), _ptr(beta),
+                                   _ptr(O), t, float(ridge_lambda), _ptr(Cv), _ptr(res), _ptr(st),
+                                   _ptr(ws), nb, _stream()), "am_fit_values_ols")
+    return Cv, res, st
+
+
+def compact_head(Q, K, V, t, *, causal=False, group=1, scale=None, options=None,
+                 want_stats=True):
+    """The whole path. Returns a dict of idx, Ck, beta, Cv, resid [2, h], status [h] and,
+    with want_stats, lse, O and score."""
+    torch = _torch()
+    _need(Q, "Q"); _need(K, "K"); _need(V, "V", dtype=K.dtype, shape=K.shape)
+    p = make_problem(Q, K, causal=causal, group=group, scale=scale)
+    o = options or make_options()
+    dev = Q.device
+    h, n, T, d = p.heads, p.n, p.T, p.d
+    out = dict(
+        idx=torch.empty((h, t), dtype=torch.int32, device=dev),
+        Ck=torch.empty((h, t, d), dtype=Q.dtype, device=dev),
+        beta=torch.empty((h, t), dtype=torch.float32, device=dev),
+        Cv=torch.empty((h, t, d), dtype=torch.float32, device=dev),
+        resid=torch.empty((2, h), dtype=torch.float32, device=dev),
+        status=torch.empty((h,), dtype=torch.int32, device=dev),
+    )
+    if want_stats:
+        out["lse"] = torch.empty((h, n), dtype=torch.float32, device=dev)
+        out["O"] = torch.empty((h, n, d), dtype=torch.float32, device=dev)
+        out["score"] = torch.empty((h, T), dtype=torch.float32, device=dev)
+    ws, nb = _workspace(p, t, CALL_COMPACT, dev)
+    g = out.get
+    _check(lib().am_compact_head(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), t, ctypes.byref(o),
+                                 _ptr(out["idx"]), _ptr(out["Ck"]), _ptr(out["beta"]),
+                                 _ptr(out["Cv"]), _ptr(g("lse")), _ptr(g("O")), _ptr(g("score")),
+                                 _ptr(out["resid"]), _ptr(out["status"]), _ptr(ws), nb, _stream()),
+           "am_compact_head")
+    return out

@@ -1,0 +1,266 @@
+// C ABI of the compaction library: argument validation, workspace carving and launch
+// sequencing on the caller's stream. Every check runs on the host before any launch; no
+// call synchronizes, allocates device memory or keeps a pointer after it returns.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/am.h"
+#include "am_internal.hpp"
+
+using namespace amc;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(const am_problem* p) { return p->dtype == AM_BF16 ? 2 : 4; }
+
+am_status check_problem(const am_problem* p) {
+  if (!p) return AM_ERR_INVALID_ARG;
+  if (p->heads < 1 || p->n < 1 || p->T < 1 || p->d < 1) return AM_ERR_INVALID_ARG;
+  if (p->group < 1 || (p->causal != 0 && p->causal != 1)) return AM_ERR_INVALID_ARG;
+  if (p->dtype != AM_F32 && p->dtype != AM_BF16) return AM_ERR_INVALID_ARG;
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return AM_ERR_INVALID_ARG;
+  if (p->causal && p->n != (int64_t)p->group * p->T) return AM_ERR_INVALID_ARG;
+  if (p->d != 64 && p->d != 128) return AM_ERR_UNSUPPORTED;
+  // row indices are 32-bit inside the kernels; element offsets are 64-bit
+  if (p->n > (int64_t)1 << 30 || p->T > (int64_t)1 << 30 || p->heads > (int64_t)1 << 24)
+    return AM_ERR_UNSUPPORTED;
+  if ((p->heads * p->n) > ((int64_t)1 << 40) || (p->heads * p->T) > ((int64_t)1 << 40))
+    return AM_ERR_UNSUPPORTED;
+  return AM_OK;
+}
+
+am_status check_t(const am_problem* p, int64_t t) {
+  if (t < 1 || t > p->T) return AM_ERR_INVALID_ARG;
+  return AM_OK;
+}
+
+am_status check_opts(const am_options* o) {
+  if (!o) return AM_ERR_INVALID_ARG;
+  if (o->score < AM_SCORE_RMS || o->score > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (o->mass != AM_MASS_RELATIVE && o->mass != AM_MASS_ABSOLUTE) return AM_ERR_INVALID_ARG;
+  if (!(o->w_lo >= 0.f) || isnan(o->w_hi) || !(o->w_hi > o->w_lo) || isinf(o->w_lo))
+    return AM_ERR_INVALID_ARG;
+  if (o->nnls_max_iter < 1 || !(o->nnls_tol >= 0.f) || !(o->ridge_lambda >= 0.f) ||
+      !isfinite(o->ridge_lambda))
+    return AM_ERR_INVALID_ARG;
+  return AM_OK;
+}
+
+am_status from_hip(hipError_t e) { return e == hipSuccess ? AM_OK : AM_ERR_DEVICE; }
+
+size_t ws_targets(const am_problem* p) {
+  return targets_ws_bytes(p->heads, p->n, p->T, p->d, esize(p));
+}
+size_t ws_fit_beta(const am_problem* p, int64_t t) {
+  return fit_beta_ws_bytes(p->heads, p->n, t, p->d);
+}
+size_t ws_fit_values(const am_problem* p, int64_t t) {
+  return fit_values_ws_bytes(p->heads, p->n, t, p->d);
+}
+size_t ws_compact(const am_problem* p, int64_t t) {
+  // lse, O and score live in the workspace when the caller does not want them
+  const size_t own = align_up((size_t)p->heads * p->n * 4) +
+                     align_up((size_t)p->heads * p->n * p->d * 4) +
+                     align_up((size_t)p->heads * p->T * 4);
+  size_t fit = ws_fit_beta(p, t);
+  const size_t fv = ws_fit_values(p, t);
+  if (fv > fit) fit = fv;
+  size_t stage = ws_targets(p);
+  if (fit > stage) stage = fit;
+  return own + stage;
+}
+
+TargetsArgs targets_args(const am_problem* p, const void* Q, const void* K, const void* V,
+                         float* lse, float* O, float* score, int mode, void* ws,
+                         hipStream_t s) {
+  TargetsArgs a;
+  a.Q = Q; a.K = K; a.V = V;
+  a.Vt = ws;
+  a.rowstat = (char*)ws + targets_vt_bytes(p->heads, p->T, p->d, esize(p));
+  a.lse = lse; a.O = O; a.score = score; a.mode = mode;
+  a.heads = (int)p->heads; a.n = (int)p->n; a.T = (int)p->T; a.d = (int)p->d;
+  a.group = p->group; a.causal = p->causal != 0; a.bf16 = p->dtype == AM_BF16;
+  a.scale = p->scale; a.stream = s;
+  return a;
+}
+
+FitArgs fit_args(const am_problem* p, const void* Q, const void* Ck, const int32_t* idx,
+                 int64_t t, void* ws, size_t ws_bytes, hipStream_t s) {
+  FitArgs a;
+  memset(&a, 0, sizeof a);
+  a.Q = Q; a.Ck = Ck; a.idx = idx;
+  a.heads = (int)p->heads; a.n = (int)p->n; a.t = (int)t; a.d = (int)p->d;
+  a.group = p->group; a.causal = p->causal != 0; a.bf16 = p->dtype == AM_BF16;
+  a.scale = p->scale; a.ws = ws; a.ws_bytes = ws_bytes; a.stream = s;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int am_abi_version(void) { return kAbiVersion; }
+
+const char* am_status_str(am_status s) {
+  switch (s) {
+    case AM_OK: return "ok";
+    case AM_ERR_INVALID_ARG: return "invalid argument";
+    case AM_ERR_UNSUPPORTED: return "unsupported problem";
+    case AM_ERR_WORKSPACE: return "workspace too small";
+    case AM_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+void am_default_options(am_options* o) {
+  if (!o) return;
+  o->score = AM_SCORE_RMS;
+  o->mass = AM_MASS_RELATIVE;
+  o->w_lo = 0.f;
+  o->w_hi = INFINITY;
+  o->nnls_max_iter = 500;
+  o->nnls_tol = 1e-6f;
+  o->ridge_lambda = 1e-3f;
+}
+
+size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
+  if (check_problem(p) != AM_OK) return 0;
+  if (which != AM_CALL_TARGETS && check_t(p, t) != AM_OK) return 0;
+  switch (which) {
+    case AM_CALL_TARGETS: return ws_targets(p);
+    case AM_CALL_SELECT: return 0;
+    case AM_CALL_FIT_BETA: return ws_fit_beta(p, t);
+    case AM_CALL_FIT_VALUES: return ws_fit_values(p, t);
+    case AM_CALL_COMPACT: return ws_compact(p, t);
+  }
+  return 0;
+}
+
+am_status am_targets(const am_problem* p, const void* Q, const void* K, const void* V,
+                     float* lse, float* O, float* key_score, am_score_mode mode, void* ws,
+                     size_t ws_bytes, am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if (!Q || !K || !lse || (O && !V)) return AM_ERR_INVALID_ARG;
+  if (mode < AM_SCORE_RMS || mode > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(K) || (V && !al16(V)) || !al16(lse) || (O && !al16(O)) ||
+      (key_score && !al16(key_score)) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_targets(p)) return AM_ERR_WORKSPACE;
+  return from_hip(launch_targets(
+      targets_args(p, Q, K, V, lse, O, key_score, (int)mode, ws, (hipStream_t)stream)));
+}
+
+am_status am_select_keys(const am_problem* p, const float* key_score, int64_t t, const void* K,
+                         const void* V, int32_t* idx, void* Ck, void* V_sel, void* ws,
+                         size_t ws_bytes, am_stream_t stream) {
+  (void)ws; (void)ws_bytes;
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if (!key_score || !K || !idx || !Ck || (V_sel && !V)) return AM_ERR_INVALID_ARG;
+  if (!al16(key_score) || !al16(K) || !al16(idx) || !al16(Ck) || (V && !al16(V)) ||
+      (V_sel && !al16(V_sel)))
+    return AM_ERR_INVALID_ARG;
+  SelectArgs a;
+  a.score = key_score; a.K = K; a.V = V; a.idx = idx; a.Ck = Ck; a.Vsel = V_sel;
+  a.heads = (int)p->heads; a.T = (int)p->T; a.t = (int)t; a.d = (int)p->d;
+  a.bf16 = p->dtype == AM_BF16; a.stream = (hipStream_t)stream;
+  return from_hip(launch_select(a));
+}
+
+am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,
+                           const int32_t* idx, const float* lse, int64_t t,
+                           const am_options* opt, float* beta, float* w, float* mass_resid,
+                           int32_t* head_status, void* ws, size_t ws_bytes,
+                           am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if ((st = check_opts(opt)) != AM_OK) return st;
+  if (!Q || !Ck || !idx || !lse || !beta) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(Ck) || !al16(idx) || !al16(lse) || !al16(beta) || (w && !al16(w)) ||
+      (mass_resid && !al16(mass_resid)) || (head_status && !al16(head_status)) ||
+      (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_fit_beta(p, t)) return AM_ERR_WORKSPACE;
+  FitArgs a = fit_args(p, Q, Ck, idx, t, ws, ws_bytes, (hipStream_t)stream);
+  a.lse = lse; a.beta = beta; a.w = w; a.mass_resid = mass_resid; a.head_status = head_status;
+  a.absolute = opt->mass == AM_MASS_ABSOLUTE;
+  a.w_lo = opt->w_lo; a.w_hi = opt->w_hi; a.tol = opt->nnls_tol; a.max_iter = opt->nnls_max_iter;
+  return from_hip(launch_fit_beta(a));
+}
+
+am_status am_fit_values_ols(const am_problem* p, const void* Q, const void* Ck,
+                            const int32_t* idx, const float* beta, const float* O, int64_t t,
+                            float ridge_lambda, float* Cv, float* out_resid,
+                            int32_t* head_status, void* ws, size_t ws_bytes,
+                            am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if (!Q || !Ck || !idx || !beta || !O || !Cv) return AM_ERR_INVALID_ARG;
+  if (!(ridge_lambda >= 0.f) || !isfinite(ridge_lambda)) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(Ck) || !al16(idx) || !al16(beta) || !al16(O) || !al16(Cv) ||
+      (out_resid && !al16(out_resid)) || (head_status && !al16(head_status)) ||
+      (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_fit_values(p, t)) return AM_ERR_WORKSPACE;
+  FitArgs a = fit_args(p, Q, Ck, idx, t, ws, ws_bytes, (hipStream_t)stream);
+  a.beta_in = beta; a.O = O; a.Cv = Cv; a.out_resid = out_resid; a.head_status = head_status;
+  a.lambda = ridge_lambda;
+  return from_hip(launch_fit_values(a));
+}
+
+am_status am_compact_head(const am_problem* p, const void* Q, const void* K, const void* V,
+                          int64_t t, const am_options* opt, int32_t* idx, void* Ck,
+                          float* beta, float* Cv, float* lse_out, float* O_out,
+                          float* score_out, float* resid_out, int32_t* head_status, void* ws,
+                          size_t ws_bytes, am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if ((st = check_opts(opt)) != AM_OK) return st;
+  if (!Q || !K || !V || !idx || !Ck || !beta || !Cv) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(K) || !al16(V) || !al16(idx) || !al16(Ck) || !al16(beta) ||
+      !al16(Cv) || (lse_out && !al16(lse_out)) || (O_out && !al16(O_out)) ||
+      (score_out && !al16(score_out)) || (resid_out && !al16(resid_out)) ||
+      (head_status && !al16(head_status)) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_compact(p, t)) return AM_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* lse = (float*)w;  w += align_up((size_t)p->heads * p->n * 4);
+  float* O = (float*)w;    w += align_up((size_t)p->heads * p->n * p->d * 4);
+  float* sc = (float*)w;   w += align_up((size_t)p->heads * p->T * 4);
+  const size_t stage_bytes = ws_bytes - (size_t)(w - (char*)ws);
+  if (lse_out) lse = lse_out;
+  if (O_out) O = O_out;
+  if (score_out) sc = score_out;
+  hipError_t e = launch_targets(targets_args(p, Q, K, V, lse, O, sc, (int)opt->score, w, s));
+  if (e != hipSuccess) return AM_ERR_DEVICE;
+  SelectArgs sa;
+  sa.score = sc; sa.K = K; sa.V = V; sa.idx = idx; sa.Ck = Ck; sa.Vsel = nullptr;
+  sa.heads = (int)p->heads; sa.T = (int)p->T; sa.t = (int)t; sa.d = (int)p->d;
+  sa.bf16 = p->dtype == AM_BF16; sa.stream = s;
+  if ((e = launch_select(sa)) != hipSuccess) return AM_ERR_DEVICE;
+  FitArgs fa = fit_args(p, Q, Ck, idx, t, w, stage_bytes, s);
+  fa.lse = lse; fa.beta = beta; fa.w = nullptr; fa.head_status = head_status;
+  fa.mass_resid = resid_out ? resid_out : nullptr;
+  fa.absolute = opt->mass == AM_MASS_ABSOLUTE;
+  fa.w_lo = opt->w_lo; fa.w_hi = opt->w_hi; fa.tol = opt->nnls_tol;
+  fa.max_iter = opt->nnls_max_iter;
+  fa.lambda = opt->ridge_lambda;
+  if ((e = launch_fit_beta(fa)) != hipSuccess) return AM_ERR_DEVICE;
+  fa.beta_in = beta; fa.O = O; fa.Cv = Cv;
+  fa.mass_resid = nullptr;
+  fa.out_resid = resid_out ? resid_out + p->heads : nullptr;
+  if ((e = launch_fit_values(fa)) != hipSuccess) return AM_ERR_DEVICE;
+  return AM_OK;
+}
+
+}  // extern "C"

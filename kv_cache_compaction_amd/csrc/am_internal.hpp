@@ -1,0 +1,54 @@
+// Host-side interface between the C ABI and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace amc {
+
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct TargetsArgs {
+  const void* Q; const void* K; const void* V;
+  void* Vt;          // workspace: transposed values [h, d, Tpad]
+  void* rowstat;     // workspace: per-query (max, log2 sum) [h, n] float2
+  float* lse; float* O; float* score;
+  int mode;
+  int heads, n, T, d, group;
+  bool causal, bf16;
+  float scale;
+  hipStream_t stream;
+};
+hipError_t launch_targets(const TargetsArgs& a);
+size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize);
+size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize);
+
+struct SelectArgs {
+  const float* score; const void* K; const void* V;
+  int32_t* idx; void* Ck; void* Vsel;
+  int heads, T, t, d;
+  bool bf16;
+  hipStream_t stream;
+};
+hipError_t launch_select(const SelectArgs& a);
+
+struct FitArgs {
+  const void* Q; const void* Ck; const int32_t* idx; const float* lse;
+  const float* beta_in;  // value fit: beta of the selected keys
+  const float* O;        // value fit: targets Y [h, n, d]
+  float* beta; float* w; float* mass_resid; float* Cv; float* out_resid;
+  int32_t* head_status;
+  int heads, n, t, d, group;
+  bool causal, bf16, absolute;
+  float scale, w_lo, w_hi, tol, lambda;
+  int max_iter;
+  void* ws; size_t ws_bytes;
+  hipStream_t stream;
+};
+hipError_t launch_fit_beta(const FitArgs& a);
+hipError_t launch_fit_values(const FitArgs& a);
+size_t fit_beta_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d);
+size_t fit_values_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d);
+
+}  // namespace amc

@@ -1,0 +1,437 @@
+// Full-cache statistics on gfx950: the fused flash pass (lse and outputs) and the
+// per-key column-score pass.
+//
+// What is computed follows "Latent Compaction with Test-Time Training", §3 Preliminaries,
+// Eq. 1 (A(q) and Z(q) over the causally visible entries, scale 1/sqrt(d)), and the
+// "Compaction" blog, §Fast KV Compaction via Attention Matching, step 1 (per-key attention
+// of the reference queries, from which the highest-attention keys are chosen).
+//
+// Layout: Q [h, n, D], K [h, T, D] in the input dtype; V is first transposed once into the
+// workspace as Vt [h, D, Tpad] (Tpad = T rounded up to the key tile, zero padded) so the
+// P.V product can read key-contiguous 16-byte fragments from LDS.
+//
+// Flash pass (one workgroup = WAVES waves x 32 queries): each lane owns one query. The
+// score tile is computed transposed, S^T = K Q^T, with Q held in registers as the MFMA B
+// operand and 64-key K tiles staged in LDS (double buffered through registers). K rows are
+// loaded in the kperm order, so the lane's 32 probabilities of a tile are already the B
+// operand of O^T += V^T P^T: no shuffle or LDS round trip between the two products. The
+// row max needs one swap between the lane halves; the running sum stays per lane until
+// the end. Scores are kept in the log2 domain (x = s * scale * log2 e).
+//
+// Column-score pass (one workgroup = WAVES waves x 32 keys): K fragments stay in
+// registers, query tiles stream through LDS with their (m, log2 l) row statistics, and
+// p = 2^((x - m) - log2 l) reproduces the flash pass's normalisation bit for bit (same
+// MFMA operands and order, same row statistics). Each lane accumulates 16 queries of its
+// key in fp32 and folds the partial into fp64 once per 32-query block; the two lane
+// halves are combined at the end. No atomics: every key is owned by one lane.
+#include "am_common.hpp"
+#include "am_internal.hpp"
+
+namespace amc {
+
+constexpr int kBN = 64;  // keys per flash-pass tile
+constexpr int kBQ = 64;  // queries per column-score tile
+
+template <typename T> constexpr int epc() { return 16 / (int)sizeof(T); }  // elements per 16 B
+
+// ------------------------------------------------------------------------------------
+// V [h, T, D] -> Vt [h, D, Tpad], zero padded beyond T.
+// ------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V,
+                                                          T* __restrict__ Vt, int Tk, int Tpad) {
+  constexpr int E = epc<T>();
+  __shared__ T tile[kBN][D + 1];
+  const int head = blockIdx.y;
+  const int k0 = blockIdx.x * kBN;
+  const T* Vh = V + (size_t)head * Tk * D;
+  for (int c = threadIdx.x; c < kBN * D / E; c += 256) {
+    const int row = c / (D / E), col = (c % (D / E)) * E;
+    const int key = k0 + row;
+    if (key < Tk) {
+      const uint4 v = *(const uint4*)(Vh + (size_t)key * D + col);
+      const T* e = (const T*)&v;
+#pragma unroll
+      for (int i = 0; i < E; ++i) tile[row][col + i] = e[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) tile[row][col + i] = (T)0.0f;
+    }
+  }
+  __syncthreads();
+  T* Vth = Vt + (size_t)head * D * Tpad;
+  for (int c = threadIdx.x; c < D * kBN / E; c += 256) {
+    const int d = c / (kBN / E), kk = (c % (kBN / E)) * E;
+    uint4 v;
+    T* e = (T*)&v;
+#pragma unroll
+    for (int i = 0; i < E; ++i) e[i] = tile[kk + i][d];
+    *(uint4*)(Vth + (size_t)d * Tpad + k0 + kk) = v;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Flash pass.
+// ------------------------------------------------------------------------------------
+template <typename T, int D>
+struct FlashLds {
+  static constexpr int KP = D + epc<T>();    // K tile row pitch (+16 B against bank conflicts)
+  static constexpr int VP = kBN + epc<T>();  // Vt tile row pitch
+  static constexpr int K_ELEMS = kBN * KP;
+  static constexpr int BUF = K_ELEMS + D * VP;
+};
+
+template <typename T, int D, int WAVES, bool CAUSAL, bool WITH_O>
+__global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ Vt,
+    float* __restrict__ lse, float2* __restrict__ rowstat, float* __restrict__ O, int n, int Tk,
+    int Tpad, int group, float c2, int heads, int n_qtiles) {
+  using L = FlashLds<T, D>;
+  typedef typename V8<T>::type v8;
+  constexpr int NT = WAVES * 64;
+  constexpr int BM = WAVES * 32;
+  constexpr int E = epc<T>();
+  constexpr int KCPR = D / E;                 // 16-byte chunks per K row
+  constexpr int VCPR = kBN / E;               // 16-byte chunks per Vt row
+  constexpr int KPT = kBN * KCPR / NT;        // K chunks per thread
+  constexpr int VPT = WITH_O ? D * VCPR / NT : 0;
+  constexpr int KC = D / 16;                  // 16-deep k-steps over the head dim
+  static_assert(kBN * KCPR % NT == 0 && D * VCPR % NT == 0, "tile/thread mismatch");
+
+  __shared__ __align__(16) T lds[2 * L::BUF];
+
+  const int b = blockIdx.x;
+  const int head = b % heads;
+  const int tile = n_qtiles - 1 - b / heads;  // late (longest under the causal mask) first
+  const int q0 = tile * BM;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+
+  const T* Qh = Q + (size_t)head * n * D;
+  const T* Kh = K + (size_t)head * Tk * D;
+  const T* Vh = Vt + (size_t)head * D * Tpad;
+
+  const int qi = q0 + wave * 32 + r;
+  const int qrow = min(qi, n - 1);
+  v8 bq[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) bq[kc] = *(const v8*)(Qh + (size_t)qrow * D + kc * 16 + hh * 8);
+
+  int kend = Tk;
+  if (CAUSAL) kend = min(Tk, (min(q0 + BM, n) - 1) / group + 1);
+  const int ntiles = (kend + kBN - 1) / kBN;
+  const int qpos = qi / group;
+  const int wave_first_pos = (q0 + wave * 32) / group;
+
+  uint4 kreg[KPT];
+  uint4 vreg[VPT > 0 ? VPT : 1];
+  auto gload = [&](int kt) {
+    const int k0 = kt * kBN;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / KCPR, col = (c % KCPR) * E;
+      const int kr = min(k0 + row, Tk - 1);
+      kreg[i] = *(const uint4*)(Kh + (size_t)kr * D + col);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / VCPR, col = (c % VCPR) * E;
+      vreg[i] = *(const uint4*)(Vh + (size_t)row * Tpad + k0 + col);
+    }
+  };
+  auto sstore = [&](int buf) {
+    T* Ks = lds + buf * L::BUF;
+    T* Vs = Ks + L::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NT;
+      *(uint4*)(Ks + (c / KCPR) * L::KP + (c % KCPR) * E) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      *(uint4*)(Vs + (c / VCPR) * L::VP + (c % VCPR) * E) = vreg[i];
+    }
+  };
+
+  f32x16 oacc[WITH_O ? D / 32 : 1];
+#pragma unroll
+  for (int db = 0; db < (WITH_O ? D / 32 : 1); ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);
+    const T* Ks = lds + buf * L::BUF;
+    const T* Vs = Ks + L::K_ELEMS;
+    const int k0 = kt * kBN;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+      const T* arow = Ks + (kb * 32 + kperm(r)) * L::KP + hh * 8;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) mma16(s[kb], *(const v8*)(arow + kc * 16), bq[kc]);
+    }
+
+    const bool need_mask = (k0 + kBN > Tk) || (CAUSAL && k0 + kBN - 1 > wave_first_pos);
+    float x[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float v = s[kb][j] * c2;
+        if (need_mask) {
+          const int key = k0 + kb * 32 + (j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8));
+          const bool vis = key < Tk && (!CAUSAL || key <= qpos);
+          v = vis ? v : -INFINITY;
+        }
+        x[kb * 16 + j] = v;
+      }
+    float tmax = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = fmaxf(tmax, shfl_xor32(tmax));
+    const float mnew = fmaxf(m, tmax);
+    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = ex2(m - msafe);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      x[i] = ex2(x[i] - msafe);
+      psum += x[i];
+    }
+    l = l * alpha + psum;
+    m = mnew;
+
+    if constexpr (WITH_O) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const v8 pb = cvt8<T>(&x[kb * 16 + kk * 8]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            mma16(oacc[db], *(const v8*)(Vs + (db * 32 + r) * L::VP + kb * 32 + kk * 16 + hh * 8),
+                  pb);
+        }
+    }
+    if (kt + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float ltot = l + shfl_xor32(l);
+  if (qi < n) {
+    if constexpr (WITH_O) {
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      float* Orow = O + ((size_t)head * n + qi) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          float4 v;
+          v.x = oacc[db][jq * 4 + 0] * inv;
+          v.y = oacc[db][jq * 4 + 1] * inv;
+          v.z = oacc[db][jq * 4 + 2] * inv;
+          v.w = oacc[db][jq * 4 + 3] * inv;
+          *(float4*)(Orow + db * 32 + jq * 8 + hh * 4) = v;
+        }
+    }
+    if (hh == 0) {
+      const float lgl = lg2(ltot);
+      lse[(size_t)head * n + qi] = (m + lgl) * kLn2;
+      rowstat[(size_t)head * n + qi] = make_float2(m, lgl);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Column-score pass.
+// ------------------------------------------------------------------------------------
+template <typename T, int D, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const float2* __restrict__ rowstat,
+    float* __restrict__ score, int mode, int n, int Tk, int group, float c2, int heads) {
+  typedef typename V8<T>::type v8;
+  constexpr int NT = WAVES * 64;
+  constexpr int BK = WAVES * 32;
+  constexpr int E = epc<T>();
+  constexpr int QP = D + E;
+  constexpr int QCPR = D / E;
+  constexpr int QPT = kBQ * QCPR / NT;
+  constexpr int KC = D / 16;
+  static_assert(kBQ * QCPR % NT == 0, "tile/thread mismatch");
+  static_assert(kBQ <= NT, "row statistics load");
+
+  __shared__ __align__(16) T qs[2][kBQ * QP];
+  __shared__ float2 rs[2][kBQ];
+
+  const int b = blockIdx.x;
+  const int head = b % heads;
+  const int k0 = (b / heads) * BK;  // key block 0 (most queries under the causal mask) first
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const T* Qh = Q + (size_t)head * n * D;
+  const T* Kh = K + (size_t)head * Tk * D;
+  const float2* RSh = rowstat + (size_t)head * n;
+
+  const int key = k0 + wave * 32 + r;
+  const int krow = min(key, Tk - 1);
+  v8 bk[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) bk[kc] = *(const v8*)(Kh + (size_t)krow * D + kc * 16 + hh * 8);
+
+  int qbeg = 0;
+  if (CAUSAL) qbeg = (min(n, k0 * group) / kBQ) * kBQ;
+  const int ntiles = (n - qbeg + kBQ - 1) / kBQ;
+  const int wave_k0 = k0 + wave * 32;
+
+  uint4 qreg[QPT];
+  float2 rreg = make_float2(0.f, 0.f);
+  auto gload = [&](int it) {
+    const int qt0 = qbeg + it * kBQ;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / QCPR, col = (c % QCPR) * E;
+      qreg[i] = *(const uint4*)(Qh + (size_t)min(qt0 + row, n - 1) * D + col);
+    }
+    if (tid < kBQ) rreg = RSh[min(qt0 + tid, n - 1)];
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int c = tid + i * NT;
+      *(uint4*)(&qs[buf][(c / QCPR) * QP + (c % QCPR) * E]) = qreg[i];
+    }
+    if (tid < kBQ) rs[buf][tid] = rreg;
+  };
+
+  double asum = 0.0, asq = 0.0;
+  float amax = 0.f;
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(it + 1);
+    const int qt0 = qbeg + it * kBQ;
+    const bool need_mask =
+        (qt0 + kBQ > n) || (CAUSAL && qt0 / group < wave_k0 + 31);
+#pragma unroll
+    for (int qb = 0; qb < kBQ / 32; ++qb) {
+      f32x16 s;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = 0.f;
+      const T* arow = &qs[buf][(qb * 32 + r) * QP + hh * 8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) mma16(s, *(const v8*)(arow + kc * 16), bk[kc]);
+      float ps = 0.f, pq = 0.f, pm = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int ql = qb * 32 + crow(j, hh);
+        const float2 st = rs[buf][ql];
+        float v = ex2((s[j] * c2 - st.x) - st.y);
+        if (need_mask) {
+          const int q = qt0 + ql;
+          const bool vis = q < n && (!CAUSAL || key <= q / group);
+          v = vis ? v : 0.f;
+        }
+        ps += v;
+        pq += v * v;
+        pm = fmaxf(pm, v);
+      }
+      asum += (double)ps;
+      asq += (double)pq;
+      amax = fmaxf(amax, pm);
+    }
+    if (it + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  asum += __shfl_xor(asum, 32, 64);
+  asq += __shfl_xor(asq, 32, 64);
+  amax = fmaxf(amax, shfl_xor32(amax));
+  if (hh == 0 && key < Tk) {
+    float out;
+    if (mode == 0) out = (float)sqrt(asq / (double)n);
+    else if (mode == 1) out = (float)(asum / (double)n);
+    else out = amax;
+    score[(size_t)head * Tk + key] = out;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------
+constexpr int kFlashWaves = 4;
+constexpr int kScoreWaves = 4;
+
+template <typename T, int D>
+static hipError_t launch_targets_t(const TargetsArgs& a) {
+  const int Tpad = round_up(a.T, kBN);
+  const float c2 = a.scale * kLog2e;
+  if (a.O) {
+    dim3 g(Tpad / kBN, a.heads);
+    hipLaunchKernelGGL((transpose_v_kernel<T, D>), g, dim3(256), 0, a.stream, (const T*)a.V,
+                       (T*)a.Vt, a.T, Tpad);
+  }
+  const int BM = kFlashWaves * 32;
+  const int nq = (a.n + BM - 1) / BM;
+  const dim3 gf(nq * a.heads), bf(kFlashWaves * 64);
+#define AM_FLASH(C, W)                                                                        \
+  hipLaunchKernelGGL((flash_fwd_kernel<T, D, kFlashWaves, C, W>), gf, bf, 0, a.stream,       \
+                     (const T*)a.Q, (const T*)a.K, (const T*)a.Vt, a.lse, (float2*)a.rowstat, \
+                     a.O, a.n, a.T, Tpad, a.group, c2, a.heads, nq)
+  if (a.causal) {
+    if (a.O) AM_FLASH(true, true); else AM_FLASH(true, false);
+  } else {
+    if (a.O) AM_FLASH(false, true); else AM_FLASH(false, false);
+  }
+#undef AM_FLASH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.score) return e;
+  const int BK = kScoreWaves * 32;
+  const dim3 gs(((a.T + BK - 1) / BK) * a.heads), bs(kScoreWaves * 64);
+  if (a.causal)
+    hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, true>), gs, bs, 0, a.stream,
+                       (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.mode,
+                       a.n, a.T, a.group, c2, a.heads);
+  else
+    hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, false>), gs, bs, 0, a.stream,
+                       (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.mode,
+                       a.n, a.T, a.group, c2, a.heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_targets(const TargetsArgs& a) {
+  if (a.bf16) return a.d == 128 ? launch_targets_t<bf16, 128>(a) : launch_targets_t<bf16, 64>(a);
+  return a.d == 128 ? launch_targets_t<float, 128>(a) : launch_targets_t<float, 64>(a);
+}
+
+size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize) {
+  const size_t vt = align_up((size_t)heads * d * round_up((int)T, kBN) * esize);
+  const size_t rs = align_up((size_t)heads * n * sizeof(float2));
+  return vt + rs;
+}
+
+size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize) {
+  return align_up((size_t)heads * d * round_up((int)T, kBN) * esize);
+}
+
+}  // namespace amc

@@ -1,0 +1,42 @@
+"""Shared helpers of the GPU parity tests: device upload of generated inputs and the
+tolerance checks (normwise output rows, selection near-tie rule)."""
+import numpy as np
+
+from kv_cache_compaction_amd import synth
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    return synth.as_f64(x, dtype)
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """||got_i - ref_i|| / ||ref_i|| per row (reading of 'relative' for outputs)."""
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return num / np.maximum(den, 1e-300)
+
+
+def check_selection(idx_gpu: np.ndarray, score_ref: np.ndarray, t: int, rel: float = 1e-5):
+    """idx must hold every key clearly above the t-th score and none clearly below it;
+    keys within rel of the threshold may differ. Returns the overlap with the oracle."""
+    idx_gpu = np.asarray(idx_gpu, dtype=np.int64)
+    assert idx_gpu.shape == (t,)
+    assert np.all(np.diff(idx_gpu) > 0), "indices must be strictly ascending"
+    assert idx_gpu.min() >= 0 and idx_gpu.max() < score_ref.size
+    order = np.lexsort((np.arange(score_ref.size), -score_ref))
+    sig_t = score_ref[order[t - 1]]
+    S = set(idx_gpu.tolist())
+    must = np.flatnonzero(score_ref > sig_t * (1 + rel))
+    never = np.flatnonzero(score_ref < sig_t * (1 - rel))
+    missing = [j for j in must if j not in S]
+    extra = [j for j in idx_gpu if j in set(never.tolist())]
+    assert not missing, f"keys clearly above threshold not selected: {missing[:10]}"
+    assert not extra, f"keys clearly below threshold selected: {extra[:10]}"
+    return len(S & set(order[:t].tolist())) / t
