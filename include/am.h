@@ -48,7 +48,8 @@ typedef struct ihipStream_t* am_stream_t;
 typedef enum {
   AM_OK = 0,
   AM_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, t outside [1, T], ... */
-  AM_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d not 64/128) */
+  AM_ERR_UNSUPPORTED = -2, /* valid request this build does not implement: d not 64/128,
+                              n or T above 2^30, or t above 8192 in the fit calls */
   AM_ERR_WORKSPACE = -3,   /* ws_bytes smaller than am_workspace_bytes() */
   AM_ERR_DEVICE = -4       /* a HIP launch or device query failed */
 } am_status;
@@ -74,7 +75,7 @@ enum {
 };
 
 typedef struct {
-  int64_t heads;   /* h >= 1 independent head problems */
+  int64_t heads;   /* 1 <= h <= 65535 independent head problems */
   int64_t n;       /* reference queries per head, >= 1 */
   int64_t T;       /* full-cache keys per head, >= 1 */
   int64_t d;       /* head dimension: 64 or 128 */
@@ -125,7 +126,8 @@ am_status am_select_keys(const am_problem* p, const float* key_score, int64_t t,
  * w = exp(beta) (blog, §Choosing beta). With M the mass design of the selected keys
  * (see am_mass_mode), w = argmin_{w_lo <= w <= w_hi} ||M w - b||^2, solved on the device
  * from the Gram form G = M^T M, M^T b by accelerated projected gradient. beta = log w
- * (w = 0 gives -inf). lse[h, n] is the natural-log normalizer from am_targets.
+ * (w = 0 gives -inf). lse[h, n] is the natural-log normalizer from am_targets. idx must
+ * be ascending (as am_select_keys returns it); it gives the compacted keys' positions.
  * Optional outputs: w[h, t]; mass_resid[h] = ||M w - b||^2 / n; head_status[h].
  */
 am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,

@@ -25,8 +25,8 @@ am_status check_problem(const am_problem* p) {
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return AM_ERR_INVALID_ARG;
   if (p->causal && p->n != (int64_t)p->group * p->T) return AM_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return AM_ERR_UNSUPPORTED;
-  // row indices are 32-bit inside the kernels; element offsets are 64-bit
-  if (p->n > (int64_t)1 << 30 || p->T > (int64_t)1 << 30 || p->heads > (int64_t)1 << 24)
+  // row indices are 32-bit inside the kernels; heads index a grid dimension of <= 65535
+  if (p->n > (int64_t)1 << 30 || p->T > (int64_t)1 << 30 || p->heads > 65535)
     return AM_ERR_UNSUPPORTED;
   if ((p->heads * p->n) > ((int64_t)1 << 40) || (p->heads * p->T) > ((int64_t)1 << 40))
     return AM_ERR_UNSUPPORTED;
@@ -37,6 +37,8 @@ am_status check_t(const am_problem* p, int64_t t) {
   if (t < 1 || t > p->T) return AM_ERR_INVALID_ARG;
   return AM_OK;
 }
+
+am_status check_fit_t(int64_t t) { return t > kMaxFitT ? AM_ERR_UNSUPPORTED : AM_OK; }
 
 am_status check_opts(const am_options* o) {
   if (!o) return AM_ERR_INVALID_ARG;
@@ -133,9 +135,9 @@ size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
   switch (which) {
     case AM_CALL_TARGETS: return ws_targets(p);
     case AM_CALL_SELECT: return 0;
-    case AM_CALL_FIT_BETA: return ws_fit_beta(p, t);
-    case AM_CALL_FIT_VALUES: return ws_fit_values(p, t);
-    case AM_CALL_COMPACT: return ws_compact(p, t);
+    case AM_CALL_FIT_BETA: return t > kMaxFitT ? 0 : ws_fit_beta(p, t);
+    case AM_CALL_FIT_VALUES: return t > kMaxFitT ? 0 : ws_fit_values(p, t);
+    case AM_CALL_COMPACT: return t > kMaxFitT ? 0 : ws_compact(p, t);
   }
   return 0;
 }
@@ -182,6 +184,7 @@ am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,
   if (st != AM_OK) return st;
   if ((st = check_t(p, t)) != AM_OK) return st;
   if ((st = check_opts(opt)) != AM_OK) return st;
+  if ((st = check_fit_t(t)) != AM_OK) return st;
   if (!Q || !Ck || !idx || !lse || !beta) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(Ck) || !al16(idx) || !al16(lse) || !al16(beta) || (w && !al16(w)) ||
       (mass_resid && !al16(mass_resid)) || (head_status && !al16(head_status)) ||
@@ -203,6 +206,7 @@ am_status am_fit_values_ols(const am_problem* p, const void* Q, const void* Ck,
   am_status st = check_problem(p);
   if (st != AM_OK) return st;
   if ((st = check_t(p, t)) != AM_OK) return st;
+  if ((st = check_fit_t(t)) != AM_OK) return st;
   if (!Q || !Ck || !idx || !beta || !O || !Cv) return AM_ERR_INVALID_ARG;
   if (!(ridge_lambda >= 0.f) || !isfinite(ridge_lambda)) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(Ck) || !al16(idx) || !al16(beta) || !al16(O) || !al16(Cv) ||
@@ -225,6 +229,7 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
   if (st != AM_OK) return st;
   if ((st = check_t(p, t)) != AM_OK) return st;
   if ((st = check_opts(opt)) != AM_OK) return st;
+  if ((st = check_fit_t(t)) != AM_OK) return st;
   if (!Q || !K || !V || !idx || !Ck || !beta || !Cv) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(K) || !al16(V) || !al16(idx) || !al16(Ck) || !al16(beta) ||
       !al16(Cv) || (lse_out && !al16(lse_out)) || (O_out && !al16(O_out)) ||
@@ -258,6 +263,7 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
   if ((e = launch_fit_beta(fa)) != hipSuccess) return AM_ERR_DEVICE;
   fa.beta_in = beta; fa.O = O; fa.Cv = Cv;
   fa.mass_resid = nullptr;
+  fa.keep_status = true;
   fa.out_resid = resid_out ? resid_out + p->heads : nullptr;
   if ((e = launch_fit_values(fa)) != hipSuccess) return AM_ERR_DEVICE;
   return AM_OK;

@@ -7,6 +7,13 @@
 namespace amc {
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// per-head device status bits (same values as the AM_HEAD_* constants of am.h)
+constexpr int AM_HEAD_NNLS_BIT = 1;
+constexpr int AM_HEAD_CHOL_BIT = 2;
+constexpr int AM_HEAD_NONFINITE_BIT = 4;
+// largest compacted size the fits support (the NNLS keeps a t-vector in LDS)
+constexpr int kMaxFitT = 8192;
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct TargetsArgs {
@@ -23,6 +30,21 @@ struct TargetsArgs {
 hipError_t launch_targets(const TargetsArgs& a);
 size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize);
 size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize);
+
+// Biased compacted attention (the flash pass over C_k with per-key bias and original
+// positions). Cv null: statistics only. Y set: per-query residuals instead of O.
+struct CmpAttnArgs {
+  const void* Q; const void* Ck; const float* Cv; const float* bias; const int32_t* keypos;
+  const float* Y;
+  void* Vt;             // workspace [h, d, round_up(t, 64)] when Cv is set
+  float* lse; float2* rowstat; float* O; float2* rowres;
+  int heads, n, t, d, group;
+  bool causal, bf16;
+  float scale;
+  hipStream_t stream;
+};
+hipError_t launch_cmp_attention(const CmpAttnArgs& a);
+size_t cmp_vt_bytes(int64_t heads, int64_t t, int64_t d, int esize);
 
 struct SelectArgs {
   const float* score; const void* K; const void* V;
@@ -43,6 +65,7 @@ struct FitArgs {
   bool causal, bf16, absolute;
   float scale, w_lo, w_hi, tol, lambda;
   int max_iter;
+  bool keep_status;  // value fit after the beta fit: OR into head_status instead of clearing
   void* ws; size_t ws_bytes;
   hipStream_t stream;
 };

@@ -1,8 +1,956 @@
-// placeholder until the fit kernels land
+// The two fits on gfx950: beta from the mass equations by NNLS on w = exp(beta)
+// ("Compaction" blog, §Choosing beta) and C_v from the output equations by ridge least
+// squares (§Choosing C_v), with A_i the biased compacted softmax of "Latent Compaction with
+// Test-Time Training", §3.1 Eq. 2-3.
+//
+// Gram builds. Neither the n x t design M nor A is ever stored. A workgroup owns one
+// 128 x 128 tile (ta >= tb) of the t x t Gram and one chunk of queries. For every 32
+// queries, its four waves recompute the needed 32 x 32 score blocks Q C_k^T on bf16 MFMA
+// (query rows loaded in the kperm order), turn them into design entries
+// 2^(s * scale * log2 e + bias_j - shift_i) under the causal mask of the original key
+// positions, and park them in LDS as bf16 MFMA fragments. Because of the kperm order, a
+// lane's fragment of a score block is at once the A operand (as M^T) and the B operand
+// (as M) of the Gram product over those queries, so M^T M accumulates with no transpose.
+// Diagonal tiles also accumulate M^T b (mass) or A^T Y (values, Y staged as bf16 Y^T).
+// Partial tiles per query chunk are summed in a fixed order by a reduce kernel: no
+// floating-point atomics, bit-reproducible.
+//
+// NNLS. Accelerated projected gradient with Jacobi scaling (v = sqrt(diag G) * w),
+// step 1/L with L from power iteration, momentum restarted when the step turns back
+// (gradient-mapping test), stopped on the scaled gradient-mapping norm. One launch per
+// iteration; each workgroup owns 16 rows, redundantly reduces the previous launch's
+// per-block partial sums (fixed order) for the momentum scalars, and builds the full
+// extrapolated point in LDS. No grid-wide barrier is needed.
+//
+// Ridge solve. (G_A + lambda I) C = A^T Y in fp64: right-looking blocked Cholesky with
+// 64 x 64 blocks (diagonal factor and its explicit inverse in one workgroup, panel as a
+// product with that inverse, trailing update per block pair), then blocked forward and
+// backward substitution with the stored diagonal inverses.
+#include "am_common.hpp"
 #include "am_internal.hpp"
+
 namespace amc {
-hipError_t launch_fit_beta(const FitArgs&) { return hipErrorNotSupported; }
-hipError_t launch_fit_values(const FitArgs&) { return hipErrorNotSupported; }
-size_t fit_beta_ws_bytes(int64_t, int64_t, int64_t, int64_t) { return 256; }
-size_t fit_values_ws_bytes(int64_t, int64_t, int64_t, int64_t) { return 256; }
+
+constexpr int kGT = 128;  // Gram tile (keys per side)
+constexpr int kGQ = 32;   // queries per Gram step
+constexpr int kRB = 16;   // NNLS rows per workgroup
+constexpr int kNB = 64;   // Cholesky block
+constexpr int kPow = 24;  // power iterations for the NNLS step size
+
+template <typename T> constexpr int epcf() { return 16 / (int)sizeof(T); }
+
+__device__ __forceinline__ void tri_index(int k, int& ta, int& tb) {
+  int a = (int)((sqrtf(8.f * (float)k + 1.f) - 1.f) * 0.5f);
+  while ((a + 1) * (a + 2) / 2 <= k) ++a;
+  while (a * (a + 1) / 2 > k) --a;
+  ta = a;
+  tb = k - a * (a + 1) / 2;
 }
+
+// ------------------------------------------------------------------------------------
+// Gram builds
+// ------------------------------------------------------------------------------------
+struct GramParams {
+  const void* Q; const void* Ck; const int32_t* keypos; const float* bias;
+  const float* shift2;  // per query, log2 domain
+  const float* target;  // mass: per-query right-hand side (null = 1)
+  const float* Y;       // values: targets [h, n, D]
+  float* Gpart;         // [h, nch, ntri, 128, 128]
+  float* Vpart;         // mass: [h, nch, tpad]; values: [h, nch, tpad, D]
+  int n, t, tpad, group, ntri, nch, chunk;
+  int causal;
+  float c2;
+};
+
+template <typename T, int D, bool VALUE>
+__global__ __launch_bounds__(256, 1) void gram_kernel(const GramParams p) {
+  typedef typename V8<T>::type v8;
+  constexpr int E = epcf<T>(), QP = D + E, KC = D / 16, YP = kGQ + 8;
+  __shared__ __align__(16) T qs[kGQ * QP];
+  __shared__ float shs[kGQ], tgs[kGQ];
+  __shared__ __align__(16) bf16x8 mb[8][2][64];
+  __shared__ __align__(16) bf16 yts[VALUE ? D * YP : 8];
+
+  const int tri = blockIdx.x, chunk = blockIdx.y, head = blockIdx.z;
+  int ta, tb;
+  tri_index(tri, ta, tb);
+  const bool diag = ta == tb;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int n = p.n, t = p.t;
+  const T* Qh = (const T*)p.Q + (size_t)head * n * D;
+  const T* Ch = (const T*)p.Ck + (size_t)head * t * D;
+  const float* Sh = p.shift2 + (size_t)head * n;
+
+  const int nblk = diag ? 1 : 2;
+  const int bid[2] = {diag ? wave : 2 * wave, 2 * wave + 1};
+  v8 bck[2][KC];
+  int kpos[2] = {0, 0};
+  float kb2[2] = {0.f, 0.f};
+  bool kval[2] = {false, false};
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    if (bi < nblk) {
+      const int s = bid[bi];
+      const int key = (s < 4) ? ta * kGT + 32 * s + r : tb * kGT + 32 * (s - 4) + r;
+      kval[bi] = key < t;
+      const int kr = min(key, t - 1);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) bck[bi][kc] = *(const v8*)(Ch + (size_t)kr * D + kc * 16 + hh * 8);
+      kpos[bi] = p.keypos[(size_t)head * t + kr];
+      if (VALUE) kb2[bi] = p.bias[(size_t)head * t + kr] * kLog2e;
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) bck[bi][kc] = bck[0][kc];
+    }
+  }
+
+  const int qa = chunk * p.chunk;
+  const int qb = min(n, qa + p.chunk);
+  int qstart = qa;
+  if (p.causal) {
+    // queries before the later of the two blocks' first positions see nothing in one block
+    const int f = max(p.keypos[(size_t)head * t + min(ta * kGT, t - 1)],
+                      p.keypos[(size_t)head * t + min(tb * kGT, t - 1)]);
+    qstart = max(qa, (int)min((long long)f * p.group, (long long)qb) / kGQ * kGQ);
+  }
+
+  f32x16 gacc[2][2];
+  f32x16 racc[VALUE ? D / 32 : 1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) gacc[i][jj][j] = 0.f;
+#pragma unroll
+  for (int db = 0; db < (VALUE ? D / 32 : 1); ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) racc[db][j] = 0.f;
+  float hacc = 0.f;
+  const int wa = wave >> 1, wb = wave & 1;
+
+  for (int q0 = qstart; q0 < qb; q0 += kGQ) {
+    for (int c = tid; c < kGQ * D / E; c += 256) {
+      const int row = c / (D / E), col = (c % (D / E)) * E;
+      *(uint4*)&qs[row * QP + col] = *(const uint4*)(Qh + (size_t)min(q0 + row, n - 1) * D + col);
+    }
+    if (tid < kGQ) {
+      const int q = min(q0 + tid, n - 1);
+      shs[tid] = Sh[q];
+      tgs[tid] = p.target ? p.target[(size_t)head * n + q] : 1.f;
+    }
+    if (VALUE && diag) {
+      const float* Yh = p.Y + (size_t)head * n * D;
+      for (int c = tid; c < kGQ * D / 4; c += 256) {
+        const int row = c / (D / 4), col = (c % (D / 4)) * 4;
+        const float4 y = *(const float4*)(Yh + (size_t)min(q0 + row, n - 1) * D + col);
+        yts[(col + 0) * YP + row] = (bf16)y.x;
+        yts[(col + 1) * YP + row] = (bf16)y.y;
+        yts[(col + 2) * YP + row] = (bf16)y.z;
+        yts[(col + 3) * YP + row] = (bf16)y.w;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      if (bi < nblk) {
+        f32x16 s;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[j] = 0.f;
+        const T* arow = qs + kperm(r) * QP + hh * 8;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma16(s, *(const v8*)(arow + kc * 16), bck[bi][kc]);
+        float mv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ql = j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8);
+          const int q = q0 + ql;
+          const float sh = shs[ql];
+          const float v = ex2(s[j] * p.c2 + kb2[bi] - sh);
+          const bool vis = kval[bi] && q < qb && sh > -INFINITY &&
+                           (!p.causal || kpos[bi] <= q / p.group);
+          mv[j] = vis ? v : 0.f;
+          if (!VALUE && diag) hacc += mv[j] * tgs[ql];
+        }
+        mb[bid[bi]][0][lane] = cvt8<bf16>(mv);
+        mb[bid[bi]][1][lane] = cvt8<bf16>(mv + 8);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int ai = 2 * wa + i;
+        const int bj = diag ? 2 * wb + jj : 4 + 2 * wb + jj;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) mma16(gacc[i][jj], mb[ai][ks][lane], mb[bj][ks][lane]);
+      }
+    if (VALUE && diag) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          mma16(racc[db], mb[wave][ks][lane],
+                *(const bf16x8*)&yts[(db * 32 + r) * YP + ks * 16 + hh * 8]);
+    }
+    __syncthreads();
+  }
+
+  float* Gp = p.Gpart + (((size_t)head * p.nch + chunk) * p.ntri + tri) * kGT * kGT;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        Gp[((2 * wa + i) * 32 + crow(j, hh)) * kGT + (2 * wb + jj) * 32 + r] = gacc[i][jj][j];
+  if (diag) {
+    if (!VALUE) {
+      hacc += shfl_xor32(hacc);
+      if (hh == 0) p.Vpart[((size_t)head * p.nch + chunk) * p.tpad + ta * kGT + 32 * wave + r] = hacc;
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int row = ta * kGT + 32 * wave + crow(j, hh);
+          p.Vpart[(((size_t)head * p.nch + chunk) * p.tpad + row) * D + db * 32 + r] = racc[db][j];
+        }
+    }
+  }
+}
+
+// Full symmetric Gram from the chunk partials, into an ld x ld matrix per head:
+// fp32 (NNLS, ld = t) or fp64 + lambda I with identity padding (Cholesky, ld >= t).
+template <typename OT>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ Gpart,
+                                                          OT* __restrict__ G, int t, int ld,
+                                                          int ntri, int nch, float lambda) {
+  const int head = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)ld * ld) return;
+  const int i = (int)(e / ld), j = (int)(e % ld);
+  double v;
+  if (i < t && j < t) {
+    int ta = i / kGT, tb = j / kGT, ii = i % kGT, jj = j % kGT;
+    if (ta < tb) {
+      const int x = ta; ta = tb; tb = x;
+      const int y = ii; ii = jj; jj = y;
+    }
+    const int tri = ta * (ta + 1) / 2 + tb;
+    float acc = 0.f;
+    for (int c = 0; c < nch; ++c)
+      acc += Gpart[(((size_t)head * nch + c) * ntri + tri) * kGT * kGT + ii * kGT + jj];
+    v = (double)acc + (i == j ? (double)lambda : 0.0);
+  } else {
+    v = (i == j) ? 1.0 : 0.0;
+  }
+  G[(size_t)head * ld * ld + (size_t)i * ld + j] = (OT)v;
+}
+
+// Vector part: rows < t summed over chunks, rows in [t, ld) zero. width = 1 (M^T b) or D.
+template <typename OT>
+__global__ __launch_bounds__(256) void vec_reduce_kernel(const float* __restrict__ Vpart,
+                                                         OT* __restrict__ out, int t, int tpad,
+                                                         int ld, int width, int nch) {
+  const int head = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)ld * width) return;
+  const int i = (int)(e / width), c0 = (int)(e % width);
+  float acc = 0.f;
+  if (i < t)
+    for (int c = 0; c < nch; ++c)
+      acc += Vpart[(((size_t)head * nch + c) * tpad + i) * width + c0];
+  out[(size_t)head * ld * width + e] = (OT)acc;
+}
+
+// Per-query shift (log2 domain) and mass right-hand side.
+//   mode 0: shift = lse * log2 e (relative mass design)
+//   mode 1: shift = max_i lse_i * log2 e, target = 2^(lse_i log2 e - shift) (absolute)
+//   mode 2: shift = m + log2 l of the biased compacted pass (value design)
+__global__ __launch_bounds__(256) void shift_kernel(const float* __restrict__ lse,
+                                                    const float2* __restrict__ rowstat,
+                                                    float* __restrict__ shift2,
+                                                    float* __restrict__ target, int n, int mode) {
+  const int head = blockIdx.x;
+  __shared__ float red[256];
+  float c = -INFINITY;
+  if (mode == 1) {
+    for (int i = threadIdx.x; i < n; i += 256) c = fmaxf(c, lse[(size_t)head * n + i]);
+    red[threadIdx.x] = c;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+      __syncthreads();
+    }
+    c = red[0] * kLog2e;
+  }
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const size_t o = (size_t)head * n + i;
+    if (mode == 0) {
+      shift2[o] = lse[o] * kLog2e;
+    } else if (mode == 1) {
+      shift2[o] = c;
+      target[o] = ex2(lse[o] * kLog2e - c);
+    } else {
+      const float2 st = rowstat[o];
+      shift2[o] = st.x + st.y;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// NNLS by accelerated projected gradient (one launch per iteration)
+// ------------------------------------------------------------------------------------
+struct NnlsState {
+  const float* G;   // [h, t, t]
+  const float* hv;  // [h, t]
+  float* dinv;      // [h, t]   1 / sqrt(G_jj) (0 for empty columns)
+  float* hs;        // [h, t]   scaled right-hand side
+  float* V;         // [h, 3, t] iterates (ring of three)
+  float* X;         // [h, 2, t] power-iteration vectors
+  float* PN;        // [h, 2, nblk] power-iteration partial squared norms
+  float2* P;        // [h, 2, nblk] (restart dot, gradient-mapping max) partials
+  float* TK;        // [h, 2] momentum scalars
+  float* hsmax;     // [h]
+  int* iters;       // [h]
+  int t, nblk;
+  float lo, hi, tol;
+};
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  return s;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+__global__ __launch_bounds__(256) void nnls_prep_kernel(NnlsState s, int32_t* status) {
+  __shared__ float red[4];
+  const int head = blockIdx.x, t = s.t;
+  const float* G = s.G + (size_t)head * t * t;
+  bool bad = false;
+  float hm = 0.f;
+  for (int j = threadIdx.x; j < t; j += 256) {
+    const float g = G[(size_t)j * t + j];
+    const float h = s.hv[(size_t)head * t + j];
+    bad |= !isfinite(g) || !isfinite(h);
+    const float di = g > 0.f ? rsqrtf(g) : 0.f;
+    s.dinv[(size_t)head * t + j] = di;
+    const float hsj = h * di;
+    s.hs[(size_t)head * t + j] = hsj;
+    hm = fmaxf(hm, fabsf(hsj));
+    const float v0 = di > 0.f ? s.lo / di : 0.f;
+    s.V[((size_t)head * 3 + 0) * t + j] = v0;
+    s.V[((size_t)head * 3 + 2) * t + j] = v0;
+    s.X[((size_t)head * 2 + 0) * t + j] = 1.f;
+  }
+  hm = block_max(hm, red);
+  const float nb = block_max(bad ? 1.f : 0.f, red);
+  for (int b = threadIdx.x; b < s.nblk; b += 256) {
+    s.PN[((size_t)head * 2 + 0) * s.nblk + b] = b == 0 ? (float)t : 0.f;
+    s.P[((size_t)head * 2 + 0) * s.nblk + b] = make_float2(0.f, INFINITY);
+  }
+  if (threadIdx.x == 0) {
+    s.hsmax[head] = hm;
+    s.TK[head * 2 + 0] = 1.f;
+    s.iters[head] = 0;
+    if (status) status[head] = nb > 0.f ? AM_HEAD_NONFINITE_BIT : 0;
+  }
+}
+
+// rows of this block: y_i = (D^-1 G D^-1 x)_i  with x read from X[k % 2] normalised
+__global__ __launch_bounds__(256) void nnls_power_kernel(NnlsState s, int k) {
+  __shared__ float xs[kMaxFitT];
+  __shared__ float red[4];
+  const int head = blockIdx.y, blk = blockIdx.x, t = s.t;
+  const float* xin = s.X + ((size_t)head * 2 + (k & 1)) * t;
+  float* xout = s.X + ((size_t)head * 2 + ((k + 1) & 1)) * t;
+  const float* pn = s.PN + ((size_t)head * 2 + (k & 1)) * s.nblk;
+  float nrm = 0.f;
+  for (int b = 0; b < s.nblk; ++b) nrm += pn[b];
+  const float sc = nrm > 0.f ? rsqrtf(nrm) : 0.f;
+  const float* di = s.dinv + (size_t)head * t;
+  for (int j = threadIdx.x; j < t; j += 256) xs[j] = xin[j] * sc * di[j];
+  __syncthreads();
+  const float* G = s.G + (size_t)head * t * t;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float part = 0.f;
+  for (int rr = wave; rr < kRB; rr += 4) {
+    const int i = blk * kRB + rr;
+    if (i >= t) break;
+    float acc = 0.f;
+    for (int j = lane; j < t; j += 64) acc += G[(size_t)i * t + j] * xs[j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    const float y = acc * di[i];
+    if (lane == 0) xout[i] = y;
+    part += (lane == 0) ? y * y : 0.f;
+  }
+  part = block_sum(part, red);
+  if (threadIdx.x == 0) s.PN[((size_t)head * 2 + ((k + 1) & 1)) * s.nblk + blk] = part;
+}
+
+__device__ __forceinline__ float nnls_L(const NnlsState& s, int head) {
+  // ||D^-1 G D^-1 x|| for the last normalised power vector, with a safety margin
+  const float* pn = s.PN + ((size_t)head * 2 + (kPow & 1)) * s.nblk;
+  float nrm = 0.f;
+  for (int b = 0; b < s.nblk; ++b) nrm += pn[b];
+  return 1.1f * sqrtf(nrm) + 1e-30f;
+}
+
+__global__ __launch_bounds__(256) void nnls_step_kernel(NnlsState s, int k) {
+  __shared__ float ys[kMaxFitT];
+  __shared__ float red[4];
+  const int head = blockIdx.y, blk = blockIdx.x, t = s.t;
+  const float L = nnls_L(s, head);
+  const float2* P = s.P + ((size_t)head * 2 + (k & 1)) * s.nblk;
+  float dot = 0.f, gm = 0.f;
+  for (int b = 0; b < s.nblk; ++b) {
+    const float2 v = P[b];
+    dot += v.x;
+    gm = fmaxf(gm, v.y);
+  }
+  const float thr = s.tol * fmaxf(s.hsmax[head], 1e-30f);
+  const bool done = k > 0 && gm <= thr;
+  const float tk = s.TK[head * 2 + (k & 1)];
+  const bool restart = dot > 0.f;
+  const float tn = restart ? 1.f : 0.5f * (1.f + sqrtf(1.f + 4.f * tk * tk));
+  const float mom = restart ? 0.f : (tk - 1.f) / tn;
+  const float* vprev = s.V + ((size_t)head * 3 + (k + 2) % 3) * t;
+  const float* vcur = s.V + ((size_t)head * 3 + k % 3) * t;
+  float* vnext = s.V + ((size_t)head * 3 + (k + 1) % 3) * t;
+  const float* di = s.dinv + (size_t)head * t;
+  for (int j = threadIdx.x; j < t; j += 256) {
+    const float y = vcur[j] + mom * (vcur[j] - vprev[j]);
+    ys[j] = y;
+  }
+  __syncthreads();
+  const float* G = s.G + (size_t)head * t * t;
+  const float* hs = s.hs + (size_t)head * t;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float pdot = 0.f, pgm = 0.f;
+  for (int rr = wave; rr < kRB; rr += 4) {
+    const int i = blk * kRB + rr;
+    if (i >= t) break;
+    float vn;
+    if (done) {
+      vn = vcur[i];
+    } else {
+      float acc = 0.f;
+      for (int j = lane; j < t; j += 64) acc += G[(size_t)i * t + j] * (ys[j] * di[j]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const float g = acc * di[i] - hs[i];
+      const float y = ys[i];
+      if (di[i] > 0.f) {
+        const float lo = s.lo / di[i];
+        const float hi = isinf(s.hi) ? INFINITY : s.hi / di[i];
+        vn = fminf(fmaxf(y - g / L, lo), hi);
+      } else {
+        vn = 0.f;
+      }
+      if (lane == 0) {
+        pdot += (vn - vcur[i]) * (y - vn);
+        pgm = fmaxf(pgm, fabsf(y - vn) * L);
+      }
+    }
+    if (lane == 0) vnext[i] = vn;
+  }
+  pdot = block_sum(pdot, red);
+  pgm = block_max(pgm, red);
+  if (threadIdx.x == 0) {
+    s.P[((size_t)head * 2 + ((k + 1) & 1)) * s.nblk + blk] =
+        done ? make_float2(0.f, gm) : make_float2(pdot, pgm);
+    if (blk == 0) {
+      s.TK[head * 2 + ((k + 1) & 1)] = tn;
+      if (!done) s.iters[head] = k + 1;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void nnls_finish_kernel(NnlsState s, int K, float* w_out,
+                                                          float* beta, int32_t* status) {
+  __shared__ float red[4];
+  const int head = blockIdx.x, t = s.t;
+  const float* v = s.V + ((size_t)head * 3 + K % 3) * t;
+  const float2* P = s.P + ((size_t)head * 2 + (K & 1)) * s.nblk;
+  float gm = 0.f;
+  for (int b = 0; b < s.nblk; ++b) gm = fmaxf(gm, P[b].y);
+  const float thr = s.tol * fmaxf(s.hsmax[head], 1e-30f);
+  bool bad = false;
+  for (int j = threadIdx.x; j < t; j += 256) {
+    const float di = s.dinv[(size_t)head * t + j];
+    float w = di > 0.f ? v[j] * di : s.lo;
+    w = fminf(fmaxf(w, s.lo), s.hi);
+    bad |= !isfinite(w);
+    if (w_out) w_out[(size_t)head * t + j] = w;
+    beta[(size_t)head * t + j] = w > 0.f ? logf(w) : -INFINITY;
+  }
+  const float nb = block_max(bad ? 1.f : 0.f, red);
+  if (threadIdx.x == 0 && status)
+    status[head] |= (gm > thr ? AM_HEAD_NNLS_BIT : 0) | (nb > 0.f ? AM_HEAD_NONFINITE_BIT : 0);
+}
+
+// ------------------------------------------------------------------------------------
+// Blocked fp64 Cholesky and triangular solves on A [h, ld, ld], R [h, ld, D]
+// ------------------------------------------------------------------------------------
+// Factor the diagonal block kb in place (lower) and store its inverse in Linv[h, nb, 64, 64].
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
+                                                        int nb, int32_t* status) {
+  __shared__ double a[kNB][kNB + 1];
+  __shared__ double li[kNB][kNB + 1];
+  __shared__ int flag;
+  const int head = blockIdx.x, tid = threadIdx.x;
+  double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
+  for (int e = tid; e < kNB * kNB; e += 256) a[e / kNB][e % kNB] = Ah[(size_t)(e / kNB) * ld + e % kNB];
+  if (tid == 0) flag = 0;
+  __syncthreads();
+  for (int c = 0; c < kNB; ++c) {
+    if (tid == 0) {
+      double pv = a[c][c];
+      if (!(pv > 0.0)) {
+        flag = 1;
+        pv = 1e-300;
+      }
+      a[c][c] = sqrt(pv);
+    }
+    __syncthreads();
+    const double dc = a[c][c];
+    for (int i = c + 1 + tid; i < kNB; i += 256) a[i][c] /= dc;
+    __syncthreads();
+    const int m = kNB - c - 1;
+    for (int e = tid; e < m * m; e += 256) {
+      const int i = c + 1 + e / m, j = c + 1 + e % m;
+      if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+    }
+    __syncthreads();
+  }
+  // inverse of the lower factor, one column per thread (forward substitution)
+  if (tid < kNB) {
+    const int j = tid;
+    for (int i = 0; i < kNB; ++i) {
+      double v = (i == j) ? 1.0 : 0.0;
+      for (int k2 = j; k2 < i; ++k2) v -= a[i][k2] * li[k2][j];
+      li[i][j] = (i < j) ? 0.0 : v / a[i][i];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int i = e / kNB, j = e % kNB;
+    Ah[(size_t)i * ld + j] = j <= i ? a[i][j] : 0.0;
+    Linv[(((size_t)head * nb + kb) * kNB + i) * kNB + j] = li[i][j];
+  }
+  if (tid == 0 && flag && status) status[head] |= AM_HEAD_CHOL_BIT;
+}
+
+// L_ik = A_ik Linv_kk^T for block rows i > kb.
+__global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double* Linv, int ld,
+                                                         int kb, int nb) {
+  __shared__ double x[kNB][kNB + 1];
+  __shared__ double li[kNB][kNB + 1];
+  const int head = blockIdx.y, ib = kb + 1 + blockIdx.x, tid = threadIdx.x;
+  double* Ai = A + (size_t)head * ld * ld + (size_t)ib * kNB * ld + kb * kNB;
+  const double* Lh = Linv + ((size_t)head * nb + kb) * kNB * kNB;
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    x[e / kNB][e % kNB] = Ai[(size_t)(e / kNB) * ld + e % kNB];
+    li[e / kNB][e % kNB] = Lh[e];
+  }
+  __syncthreads();
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int i = e / kNB, j = e % kNB;
+    double v = 0.0;
+    for (int k2 = 0; k2 <= j; ++k2) v += x[i][k2] * li[j][k2];
+    Ai[(size_t)i * ld + j] = v;
+  }
+}
+
+// A_ij -= L_ik L_jk^T for kb < j <= i (lower block pairs enumerated by blockIdx.x).
+__global__ __launch_bounds__(256) void chol_update_kernel(double* A, int ld, int kb, int nb) {
+  __shared__ double li[kNB][kNB + 1];
+  __shared__ double lj[kNB][kNB + 1];
+  const int head = blockIdx.y, tid = threadIdx.x;
+  int a, b;
+  tri_index(blockIdx.x, a, b);
+  const int ib = kb + 1 + a, jb = kb + 1 + b;
+  double* Ah = A + (size_t)head * ld * ld;
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    li[e / kNB][e % kNB] = Ah[(size_t)(ib * kNB + e / kNB) * ld + kb * kNB + e % kNB];
+    lj[e / kNB][e % kNB] = Ah[(size_t)(jb * kNB + e / kNB) * ld + kb * kNB + e % kNB];
+  }
+  __syncthreads();
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int i = e / kNB, j = e % kNB;
+    double v = 0.0;
+#pragma unroll 8
+    for (int k2 = 0; k2 < kNB; ++k2) v += li[i][k2] * lj[j][k2];
+    Ah[(size_t)(ib * kNB + i) * ld + jb * kNB + j] -= v;
+  }
+}
+
+// R_kb <- Linv_kk R_kb (forward) or Linv_kk^T R_kb (backward); one workgroup per
+// (head, 32-column slice of R).
+__global__ __launch_bounds__(256) void trsm_diag_kernel(double* R, const double* Linv, int ld,
+                                                        int D, int kb, int nb, int trans) {
+  __shared__ double li[kNB][kNB + 1];
+  __shared__ double x[kNB][33];
+  const int head = blockIdx.y, c0 = blockIdx.x * 32, tid = threadIdx.x;
+  const double* Lh = Linv + ((size_t)head * nb + kb) * kNB * kNB;
+  double* Rh = R + ((size_t)head * ld + (size_t)kb * kNB) * D + c0;
+  for (int e = tid; e < kNB * kNB; e += 256) li[e / kNB][e % kNB] = Lh[e];
+  for (int e = tid; e < kNB * 32; e += 256) x[e / 32][e % 32] = Rh[(size_t)(e / 32) * D + e % 32];
+  __syncthreads();
+  for (int e = tid; e < kNB * 32; e += 256) {
+    const int i = e / 32, c = e % 32;
+    double v = 0.0;
+    if (!trans)
+      for (int k2 = 0; k2 <= i; ++k2) v += li[i][k2] * x[k2][c];
+    else
+      for (int k2 = i; k2 < kNB; ++k2) v += li[k2][i] * x[k2][c];
+    Rh[(size_t)i * D + c] = v;
+  }
+}
+
+// forward: R_i -= L_{i,kb} R_kb for i > kb;  backward: R_i -= L_{kb,i}^T R_kb for i < kb.
+__global__ __launch_bounds__(256) void trsm_update_kernel(double* R, const double* A, int ld,
+                                                          int D, int kb, int trans) {
+  __shared__ double l[kNB][kNB + 1];
+  __shared__ double x[kNB][33];
+  const int head = blockIdx.z, c0 = blockIdx.y * 32, tid = threadIdx.x;
+  const int ib = trans ? blockIdx.x : kb + 1 + blockIdx.x;
+  const double* Ah = A + (size_t)head * ld * ld;
+  double* Rh = R + (size_t)head * ld * D;
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int i = e / kNB, j = e % kNB;
+    l[i][j] = trans ? Ah[(size_t)(kb * kNB + i) * ld + ib * kNB + j]
+                    : Ah[(size_t)(ib * kNB + i) * ld + kb * kNB + j];
+  }
+  for (int e = tid; e < kNB * 32; e += 256)
+    x[e / 32][e % 32] = Rh[(size_t)(kb * kNB + e / 32) * D + c0 + e % 32];
+  __syncthreads();
+  for (int e = tid; e < kNB * 32; e += 256) {
+    const int i = e / 32, c = e % 32;
+    double v = 0.0;
+    if (!trans)
+      for (int k2 = 0; k2 < kNB; ++k2) v += l[i][k2] * x[k2][c];
+    else
+      for (int k2 = 0; k2 < kNB; ++k2) v += l[k2][i] * x[k2][c];
+    Rh[(size_t)(ib * kNB + i) * D + c0 + c] -= v;
+  }
+}
+
+__global__ __launch_bounds__(256) void store_cv_kernel(const double* R, float* Cv, int t, int ld,
+                                                       int D, int32_t* status) {
+  const int head = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)t * D) return;
+  const double v = R[(size_t)head * ld * D + e];
+  Cv[(size_t)head * t * D + e] = (float)v;
+  if (!isfinite(v) && status) atomicOr(&status[head], AM_HEAD_NONFINITE_BIT);
+}
+
+// ------------------------------------------------------------------------------------
+// residual reductions (one workgroup per head, fixed order)
+// ------------------------------------------------------------------------------------
+// mass: mean_i (2^(lc_i - sh_i) - b_i)^2 with lc from the biased compacted pass.
+__global__ __launch_bounds__(256) void mass_resid_kernel(const float2* __restrict__ rowstat_cmp,
+                                                         const float* __restrict__ shift2,
+                                                         const float* __restrict__ target,
+                                                         float* __restrict__ out, int n) {
+  __shared__ double red[256];
+  const int head = blockIdx.x;
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const size_t o = (size_t)head * n + i;
+    const float2 st = rowstat_cmp[o];
+    const float b = target ? target[o] : 1.f;
+    const double z = (st.y == -INFINITY) ? 0.0 : exp2((double)st.x + (double)st.y - (double)shift2[o]);
+    acc += (z - b) * (z - b);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[head] = (float)(red[0] / n);
+}
+
+__global__ __launch_bounds__(256) void out_resid_kernel(const float2* __restrict__ rowres,
+                                                        float* __restrict__ out, int n) {
+  __shared__ double re[256], ry[256];
+  const int head = blockIdx.x;
+  double e = 0.0, y = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float2 v = rowres[(size_t)head * n + i];
+    e += v.x;
+    y += v.y;
+  }
+  re[threadIdx.x] = e;
+  ry[threadIdx.x] = y;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      re[threadIdx.x] += re[threadIdx.x + s];
+      ry[threadIdx.x] += ry[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[head] = (float)(ry[0] > 0.0 ? re[0] / ry[0] : 0.0);
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// ------------------------------------------------------------------------------------
+// host side: workspace plans and launch sequences
+// ------------------------------------------------------------------------------------
+static int gram_ntile(int t) { return (t + kGT - 1) / kGT; }
+static int gram_ntri(int t) { const int a = gram_ntile(t); return a * (a + 1) / 2; }
+static int gram_nch(int heads, int n, int t) {
+  const int ntri = gram_ntri(t);
+  int want = (2048 + heads * ntri - 1) / (heads * ntri);
+  int maxc = n / 2048;
+  if (maxc < 1) maxc = 1;
+  if (want > maxc) want = maxc;
+  if (want < 1) want = 1;
+  return want;
+}
+static int gram_chunk(int n, int nch) { return round_up((n + nch - 1) / nch, kGQ); }
+
+struct Carve {
+  char* base; size_t off;
+  template <typename X> X* take(size_t count) {
+    X* p = (X*)(base + off);
+    off = align_up(off + count * sizeof(X));
+    return p;
+  }
+};
+
+struct BetaPlan {
+  float* shift2; float* target; float* Gpart; float* hpart; float* G; float* hv;
+  float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float* TK; float* hsmax;
+  int* iters; float2* rowstat_cmp; int32_t* status;
+  size_t bytes;
+};
+
+static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64_t d) {
+  (void)d;
+  Carve c{base, 0};
+  const int tpad = gram_ntile((int)t) * kGT;
+  const int nch = gram_nch((int)heads, (int)n, (int)t);
+  const int ntri = gram_ntri((int)t);
+  const int nblk = ((int)t + kRB - 1) / kRB;
+  BetaPlan p;
+  p.shift2 = c.take<float>(heads * n);
+  p.target = c.take<float>(heads * n);
+  p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
+  p.hpart = c.take<float>((size_t)heads * nch * tpad);
+  p.G = c.take<float>((size_t)heads * t * t);
+  p.hv = c.take<float>(heads * t);
+  p.dinv = c.take<float>(heads * t);
+  p.hs = c.take<float>(heads * t);
+  p.V = c.take<float>(heads * 3 * t);
+  p.X = c.take<float>(heads * 2 * t);
+  p.PN = c.take<float>(heads * 2 * nblk);
+  p.P = c.take<float2>(heads * 2 * nblk);
+  p.TK = c.take<float>(heads * 2);
+  p.hsmax = c.take<float>(heads);
+  p.iters = c.take<int>(heads);
+  p.rowstat_cmp = c.take<float2>(heads * n);
+  p.status = c.take<int32_t>(heads);
+  p.bytes = c.off;
+  return p;
+}
+
+struct ValuePlan {
+  float2* rowstat_cmp; float* shift2; float* Gpart; float* Rpart; double* A; double* R;
+  double* Linv; void* Vt; float2* rowres; int32_t* status;
+  size_t bytes;
+};
+
+static int chol_ld(int t) { return round_up(t, kNB); }
+
+static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, int64_t d, int esize) {
+  Carve c{base, 0};
+  const int tpad = gram_ntile((int)t) * kGT;
+  const int nch = gram_nch((int)heads, (int)n, (int)t);
+  const int ntri = gram_ntri((int)t);
+  const int ld = chol_ld((int)t);
+  ValuePlan p;
+  p.rowstat_cmp = c.take<float2>(heads * n);
+  p.shift2 = c.take<float>(heads * n);
+  p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
+  p.Rpart = c.take<float>((size_t)heads * nch * tpad * d);
+  p.A = c.take<double>((size_t)heads * ld * ld);
+  p.R = c.take<double>((size_t)heads * ld * d);
+  p.Linv = c.take<double>((size_t)heads * (ld / kNB) * kNB * kNB);
+  p.Vt = c.take<char>(cmp_vt_bytes(heads, t, d, esize));
+  p.rowres = c.take<float2>(heads * n);
+  p.status = c.take<int32_t>(heads);
+  p.bytes = c.off;
+  return p;
+}
+
+size_t fit_beta_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d) {
+  return plan_beta(nullptr, heads, n, t, d).bytes;
+}
+size_t fit_values_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d) {
+  return plan_values(nullptr, heads, n, t, d, 4).bytes;
+}
+
+template <typename T, int D, bool VALUE>
+static void launch_gram(const GramParams& gp, int heads, hipStream_t st) {
+  hipLaunchKernelGGL((gram_kernel<T, D, VALUE>), dim3(gp.ntri, gp.nch, heads), dim3(256), 0, st, gp);
+}
+
+static void launch_gram_any(const GramParams& gp, int heads, int d, bool bf, bool value,
+                            hipStream_t st) {
+  if (bf) {
+    if (d == 128) { if (value) launch_gram<bf16, 128, true>(gp, heads, st); else launch_gram<bf16, 128, false>(gp, heads, st); }
+    else { if (value) launch_gram<bf16, 64, true>(gp, heads, st); else launch_gram<bf16, 64, false>(gp, heads, st); }
+  } else {
+    if (d == 128) { if (value) launch_gram<float, 128, true>(gp, heads, st); else launch_gram<float, 128, false>(gp, heads, st); }
+    else { if (value) launch_gram<float, 64, true>(gp, heads, st); else launch_gram<float, 64, false>(gp, heads, st); }
+  }
+}
+
+static unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+
+hipError_t launch_fit_beta(const FitArgs& a) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads, n = a.n, t = a.t, d = a.d;
+  BetaPlan pl = plan_beta((char*)a.ws, H, n, t, d);
+  int32_t* status = a.head_status ? a.head_status : pl.status;
+  const int tpad = gram_ntile(t) * kGT, nch = gram_nch(H, n, t), ntri = gram_ntri(t);
+  // row shifts and right-hand side
+  hipLaunchKernelGGL(shift_kernel, dim3(H), dim3(256), 0, st, a.lse, (const float2*)nullptr,
+                     pl.shift2, pl.target, n, a.absolute ? 1 : 0);
+  GramParams gp;
+  gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = nullptr;
+  gp.shift2 = pl.shift2; gp.target = a.absolute ? pl.target : nullptr; gp.Y = nullptr;
+  gp.Gpart = pl.Gpart; gp.Vpart = pl.hpart;
+  gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
+  gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
+  launch_gram_any(gp, H, d, a.bf16, false, st);
+  hipLaunchKernelGGL((gram_reduce_kernel<float>), dim3(cdiv((long long)t * t, 256), H), dim3(256),
+                     0, st, pl.Gpart, pl.G, t, t, ntri, nch, 0.f);
+  hipLaunchKernelGGL((vec_reduce_kernel<float>), dim3(cdiv(t, 256), H), dim3(256), 0, st,
+                     pl.hpart, pl.hv, t, tpad, t, 1, nch);
+  // NNLS
+  NnlsState s;
+  s.G = pl.G; s.hv = pl.hv; s.dinv = pl.dinv; s.hs = pl.hs; s.V = pl.V; s.X = pl.X;
+  s.PN = pl.PN; s.P = pl.P; s.TK = pl.TK; s.hsmax = pl.hsmax; s.iters = pl.iters;
+  s.t = t; s.nblk = (t + kRB - 1) / kRB;
+  s.lo = a.w_lo; s.hi = a.w_hi; s.tol = a.tol;
+  hipLaunchKernelGGL(nnls_prep_kernel, dim3(H), dim3(256), 0, st, s, status);
+  for (int k = 0; k < kPow; ++k)
+    hipLaunchKernelGGL(nnls_power_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
+  for (int k = 0; k < a.max_iter; ++k)
+    hipLaunchKernelGGL(nnls_step_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
+  hipLaunchKernelGGL(nnls_finish_kernel, dim3(H), dim3(256), 0, st, s, a.max_iter, a.w, a.beta,
+                     status);
+  // mass residual from the biased compacted pass: Z_cmp / Z = 2^(lc - lse2)
+  if (a.mass_resid) {
+    CmpAttnArgs ca;
+    ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = a.beta; ca.keypos = a.idx; ca.Y = nullptr;
+    ca.Vt = nullptr; ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
+    ca.heads = H; ca.n = n; ca.t = t; ca.d = d; ca.group = a.group; ca.causal = a.causal;
+    ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
+    hipError_t e = launch_cmp_attention(ca);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mass_resid_kernel, dim3(H), dim3(256), 0, st, pl.rowstat_cmp, pl.shift2,
+                       a.absolute ? pl.target : nullptr, a.mass_resid, n);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fit_values(const FitArgs& a) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads, n = a.n, t = a.t, d = a.d;
+  ValuePlan pl = plan_values((char*)a.ws, H, n, t, d, a.bf16 ? 2 : 4);
+  int32_t* status = a.head_status ? a.head_status : pl.status;
+  if (!a.head_status || !a.keep_status)
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(H, 256)), dim3(256), 0, st, status, H);
+  const int tpad = gram_ntile(t) * kGT, nch = gram_nch(H, n, t), ntri = gram_ntri(t);
+  const int ld = chol_ld(t), nb = ld / kNB;
+  // compacted log-normalizer per query (biased pass, statistics only)
+  CmpAttnArgs ca;
+  ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = a.beta_in; ca.keypos = a.idx; ca.Y = nullptr;
+  ca.Vt = pl.Vt; ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
+  ca.heads = H; ca.n = n; ca.t = t; ca.d = d; ca.group = a.group; ca.causal = a.causal;
+  ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
+  hipError_t e = launch_cmp_attention(ca);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(shift_kernel, dim3(H), dim3(256), 0, st, (const float*)nullptr,
+                     (const float2*)pl.rowstat_cmp, pl.shift2, (float*)nullptr, n, 2);
+  GramParams gp;
+  gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = a.beta_in;
+  gp.shift2 = pl.shift2; gp.target = nullptr; gp.Y = a.O;
+  gp.Gpart = pl.Gpart; gp.Vpart = pl.Rpart;
+  gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
+  gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
+  launch_gram_any(gp, H, d, a.bf16, true, st);
+  hipLaunchKernelGGL((gram_reduce_kernel<double>), dim3(cdiv((long long)ld * ld, 256), H),
+                     dim3(256), 0, st, pl.Gpart, pl.A, t, ld, ntri, nch, a.lambda);
+  hipLaunchKernelGGL((vec_reduce_kernel<double>), dim3(cdiv((long long)ld * d, 256), H),
+                     dim3(256), 0, st, pl.Rpart, pl.R, t, tpad, ld, d, nch);
+  // Cholesky
+  for (int kb = 0; kb < nb; ++kb) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv, ld, kb, nb,
+                       status);
+    const int m = nb - kb - 1;
+    if (m > 0) {
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(m, H), dim3(256), 0, st, pl.A,
+                         (const double*)pl.Linv, ld, kb, nb);
+      hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2, H), dim3(256), 0, st, pl.A,
+                         ld, kb, nb);
+    }
+  }
+  // L Z = R, then L^T C = Z
+  for (int kb = 0; kb < nb; ++kb) {
+    hipLaunchKernelGGL(trsm_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
+                       (const double*)pl.Linv, ld, d, kb, nb, 0);
+    if (nb - kb - 1 > 0)
+      hipLaunchKernelGGL(trsm_update_kernel, dim3(nb - kb - 1, d / 32, H), dim3(256), 0, st,
+                         pl.R, (const double*)pl.A, ld, d, kb, 0);
+  }
+  for (int kb = nb - 1; kb >= 0; --kb) {
+    hipLaunchKernelGGL(trsm_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
+                       (const double*)pl.Linv, ld, d, kb, nb, 1);
+    if (kb > 0)
+      hipLaunchKernelGGL(trsm_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
+                         (const double*)pl.A, ld, d, kb, 1);
+  }
+  hipLaunchKernelGGL(store_cv_kernel, dim3(cdiv((long long)t * d, 256), H), dim3(256), 0, st,
+                     (const double*)pl.R, a.Cv, t, ld, d, status);
+  if (a.out_resid) {
+    CmpAttnArgs cr = ca;
+    cr.Cv = a.Cv; cr.Y = a.O; cr.rowstat = nullptr; cr.rowres = pl.rowres;
+    e = launch_cmp_attention(cr);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(out_resid_kernel, dim3(H), dim3(256), 0, st, pl.rowres, a.out_resid, n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace amc

@@ -35,27 +35,29 @@ constexpr int kBQ = 64;  // queries per column-score tile
 template <typename T> constexpr int epc() { return 16 / (int)sizeof(T); }  // elements per 16 B
 
 // ------------------------------------------------------------------------------------
-// V [h, T, D] -> Vt [h, D, Tpad], zero padded beyond T.
+// V [h, T, D] -> Vt [h, D, Tpad], zero padded beyond T (Ti -> T converts, e.g. fitted
+// fp32 values to the problem dtype for the compacted-attention pass).
 // ------------------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V,
+template <typename Ti, typename T, int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const Ti* __restrict__ V,
                                                           T* __restrict__ Vt, int Tk, int Tpad) {
   constexpr int E = epc<T>();
+  constexpr int Ei = epc<Ti>();
   __shared__ T tile[kBN][D + 1];
   const int head = blockIdx.y;
   const int k0 = blockIdx.x * kBN;
-  const T* Vh = V + (size_t)head * Tk * D;
-  for (int c = threadIdx.x; c < kBN * D / E; c += 256) {
-    const int row = c / (D / E), col = (c % (D / E)) * E;
+  const Ti* Vh = V + (size_t)head * Tk * D;
+  for (int c = threadIdx.x; c < kBN * D / Ei; c += 256) {
+    const int row = c / (D / Ei), col = (c % (D / Ei)) * Ei;
     const int key = k0 + row;
     if (key < Tk) {
       const uint4 v = *(const uint4*)(Vh + (size_t)key * D + col);
-      const T* e = (const T*)&v;
+      const Ti* e = (const Ti*)&v;
 #pragma unroll
-      for (int i = 0; i < E; ++i) tile[row][col + i] = e[i];
+      for (int i = 0; i < Ei; ++i) tile[row][col + i] = (T)(float)e[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < E; ++i) tile[row][col + i] = (T)0.0f;
+      for (int i = 0; i < Ei; ++i) tile[row][col + i] = (T)0.0f;
     }
   }
   __syncthreads();
@@ -81,11 +83,21 @@ struct FlashLds {
   static constexpr int BUF = K_ELEMS + D * VP;
 };
 
-template <typename T, int D, int WAVES, bool CAUSAL, bool WITH_O>
-__global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ Vt,
-    float* __restrict__ lse, float2* __restrict__ rowstat, float* __restrict__ O, int n, int Tk,
-    int Tpad, int group, float c2, int heads, int n_qtiles) {
+// One kernel serves the full cache and the biased compacted cache. With BIASED, key j
+// carries a bias b_j (natural log, may be -inf) added to its score and an original
+// position keypos[j] that the causal mask compares against (Latent Compaction §3.1,
+// Eq. 2-4: l(q) = s K_cmp q + b and Z_cmp = 1^T exp(l)). With Y set, the epilogue writes
+// (||O_i - Y_i||^2, ||Y_i||^2) per query instead of O.
+struct FlashParams {
+  const void* Q; const void* K; const void* Vt;
+  const float* bias; const int32_t* keypos; const float* Y;
+  float* lse; float2* rowstat; float* O; float2* rowres;
+  int n, Tk, Tpad, group, heads, n_qtiles;
+  float c2;
+};
+
+template <typename T, int D, int WAVES, bool CAUSAL, bool WITH_O, bool BIASED>
+__global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashParams p) {
   using L = FlashLds<T, D>;
   typedef typename V8<T>::type v8;
   constexpr int NT = WAVES * 64;
@@ -99,16 +111,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
   static_assert(kBN * KCPR % NT == 0 && D * VCPR % NT == 0, "tile/thread mismatch");
 
   __shared__ __align__(16) T lds[2 * L::BUF];
+  __shared__ float kbias[BIASED ? 2 : 1][BIASED ? kBN : 1];
+  __shared__ int kposs[BIASED ? 2 : 1][BIASED ? kBN : 1];
 
+  const int n = p.n, Tk = p.Tk, group = p.group;
   const int b = blockIdx.x;
-  const int head = b % heads;
-  const int tile = n_qtiles - 1 - b / heads;  // late (longest under the causal mask) first
+  const int head = b % p.heads;
+  const int tile = p.n_qtiles - 1 - b / p.heads;  // late (longest under the causal mask) first
   const int q0 = tile * BM;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
 
-  const T* Qh = Q + (size_t)head * n * D;
-  const T* Kh = K + (size_t)head * Tk * D;
-  const T* Vh = Vt + (size_t)head * D * Tpad;
+  const T* Qh = (const T*)p.Q + (size_t)head * n * D;
+  const T* Kh = (const T*)p.K + (size_t)head * Tk * D;
+  const T* Vh = (const T*)p.Vt + (size_t)head * D * p.Tpad;
 
   const int qi = q0 + wave * 32 + r;
   const int qrow = min(qi, n - 1);
@@ -117,13 +132,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
   for (int kc = 0; kc < KC; ++kc) bq[kc] = *(const v8*)(Qh + (size_t)qrow * D + kc * 16 + hh * 8);
 
   int kend = Tk;
-  if (CAUSAL) kend = min(Tk, (min(q0 + BM, n) - 1) / group + 1);
+  if (CAUSAL && !BIASED) kend = min(Tk, (min(q0 + BM, n) - 1) / group + 1);
   const int ntiles = (kend + kBN - 1) / kBN;
   const int qpos = qi / group;
   const int wave_first_pos = (q0 + wave * 32) / group;
 
   uint4 kreg[KPT];
   uint4 vreg[VPT > 0 ? VPT : 1];
+  float breg = 0.f;
+  int preg = 0;
   auto gload = [&](int kt) {
     const int k0 = kt * kBN;
 #pragma unroll
@@ -137,7 +154,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + i * NT;
       const int row = c / VCPR, col = (c % VCPR) * E;
-      vreg[i] = *(const uint4*)(Vh + (size_t)row * Tpad + k0 + col);
+      vreg[i] = *(const uint4*)(Vh + (size_t)row * p.Tpad + k0 + col);
+    }
+    if (BIASED && tid < kBN) {
+      const int kr = min(k0 + tid, Tk - 1);
+      breg = p.bias[(size_t)head * Tk + kr] * kLog2e;
+      preg = p.keypos[(size_t)head * Tk + kr];
     }
   };
   auto sstore = [&](int buf) {
@@ -152,6 +174,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + i * NT;
       *(uint4*)(Vs + (c / VCPR) * L::VP + (c % VCPR) * E) = vreg[i];
+    }
+    if (BIASED && tid < kBN) {
+      kbias[buf][tid] = breg;
+      kposs[buf][tid] = preg;
     }
   };
 
@@ -185,16 +211,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
       for (int kc = 0; kc < KC; ++kc) mma16(s[kb], *(const v8*)(arow + kc * 16), bq[kc]);
     }
 
-    const bool need_mask = (k0 + kBN > Tk) || (CAUSAL && k0 + kBN - 1 > wave_first_pos);
+    const bool need_mask = (k0 + kBN > Tk) || (CAUSAL && (BIASED || k0 + kBN - 1 > wave_first_pos));
     float x[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float v = s[kb][j] * c2;
+        const int kl = kb * 32 + (j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8));
+        float v = s[kb][j] * p.c2;
+        if (BIASED) v += kbias[buf][kl];
         if (need_mask) {
-          const int key = k0 + kb * 32 + (j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8));
-          const bool vis = key < Tk && (!CAUSAL || key <= qpos);
+          const int key = k0 + kl;
+          const int pos = BIASED ? kposs[buf][kl] : key;
+          const bool vis = key < Tk && (!CAUSAL || pos <= qpos);
           v = vis ? v : -INFINITY;
         }
         x[kb * 16 + j] = v;
@@ -236,10 +265,27 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
   }
 
   const float ltot = l + shfl_xor32(l);
-  if (qi < n) {
-    if constexpr (WITH_O) {
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      float* Orow = O + ((size_t)head * n + qi) * D;
+  if constexpr (WITH_O) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (p.Y) {
+      // residual against the targets: sum over this lane's d values, then both halves
+      float e = 0.f, yy = 0.f;
+      const float* Yrow = p.Y + ((size_t)head * n + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const float4 y = *(const float4*)(Yrow + db * 32 + jq * 8 + hh * 4);
+          const float d0 = oacc[db][jq * 4 + 0] * inv - y.x, d1 = oacc[db][jq * 4 + 1] * inv - y.y;
+          const float d2 = oacc[db][jq * 4 + 2] * inv - y.z, d3 = oacc[db][jq * 4 + 3] * inv - y.w;
+          e += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+          yy += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+        }
+      e += shfl_xor32(e);
+      yy += shfl_xor32(yy);
+      if (qi < n && hh == 0) p.rowres[(size_t)head * n + qi] = make_float2(e, yy);
+    } else if (qi < n) {
+      float* Orow = p.O + ((size_t)head * n + qi) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -252,11 +298,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(
           *(float4*)(Orow + db * 32 + jq * 8 + hh * 4) = v;
         }
     }
-    if (hh == 0) {
-      const float lgl = lg2(ltot);
-      lse[(size_t)head * n + qi] = (m + lgl) * kLn2;
-      rowstat[(size_t)head * n + qi] = make_float2(m, lgl);
-    }
+  }
+  if (qi < n && hh == 0) {
+    const float lgl = lg2(ltot);
+    if (p.lse) p.lse[(size_t)head * n + qi] = (m + lgl) * kLn2;
+    if (p.rowstat) p.rowstat[(size_t)head * n + qi] = make_float2(m, lgl);
   }
 }
 
@@ -382,28 +428,37 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
 constexpr int kFlashWaves = 4;
 constexpr int kScoreWaves = 4;
 
+template <typename T, int D, bool BIASED>
+static void launch_flash(const FlashParams& fp, bool causal, bool with_o, hipStream_t st) {
+  const dim3 g(fp.n_qtiles * fp.heads), blk(kFlashWaves * 64);
+#define AM_FLASH(C, W) \
+  hipLaunchKernelGGL((flash_fwd_kernel<T, D, kFlashWaves, C, W, BIASED>), g, blk, 0, st, fp)
+  if (causal) {
+    if (with_o) AM_FLASH(true, true); else AM_FLASH(true, false);
+  } else {
+    if (with_o) AM_FLASH(false, true); else AM_FLASH(false, false);
+  }
+#undef AM_FLASH
+}
+
 template <typename T, int D>
 static hipError_t launch_targets_t(const TargetsArgs& a) {
   const int Tpad = round_up(a.T, kBN);
   const float c2 = a.scale * kLog2e;
   if (a.O) {
     dim3 g(Tpad / kBN, a.heads);
-    hipLaunchKernelGGL((transpose_v_kernel<T, D>), g, dim3(256), 0, a.stream, (const T*)a.V,
+    hipLaunchKernelGGL((transpose_v_kernel<T, T, D>), g, dim3(256), 0, a.stream, (const T*)a.V,
                        (T*)a.Vt, a.T, Tpad);
   }
   const int BM = kFlashWaves * 32;
-  const int nq = (a.n + BM - 1) / BM;
-  const dim3 gf(nq * a.heads), bf(kFlashWaves * 64);
-#define AM_FLASH(C, W)                                                                        \
-  hipLaunchKernelGGL((flash_fwd_kernel<T, D, kFlashWaves, C, W>), gf, bf, 0, a.stream,       \
-                     (const T*)a.Q, (const T*)a.K, (const T*)a.Vt, a.lse, (float2*)a.rowstat, \
-                     a.O, a.n, a.T, Tpad, a.group, c2, a.heads, nq)
-  if (a.causal) {
-    if (a.O) AM_FLASH(true, true); else AM_FLASH(true, false);
-  } else {
-    if (a.O) AM_FLASH(false, true); else AM_FLASH(false, false);
-  }
-#undef AM_FLASH
+  FlashParams fp;
+  fp.Q = a.Q; fp.K = a.K; fp.Vt = a.Vt;
+  fp.bias = nullptr; fp.keypos = nullptr; fp.Y = nullptr;
+  fp.lse = a.lse; fp.rowstat = (float2*)a.rowstat; fp.O = a.O; fp.rowres = nullptr;
+  fp.n = a.n; fp.Tk = a.T; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
+  fp.n_qtiles = (a.n + BM - 1) / BM;
+  fp.c2 = c2;
+  launch_flash<T, D, false>(fp, a.causal, a.O != nullptr, a.stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.score) return e;
   const int BK = kScoreWaves * 32;
@@ -424,6 +479,31 @@ hipError_t launch_targets(const TargetsArgs& a) {
   return a.d == 128 ? launch_targets_t<float, 128>(a) : launch_targets_t<float, 64>(a);
 }
 
+template <typename T, int D>
+static hipError_t launch_cmp_t(const CmpAttnArgs& a) {
+  const int Tpad = round_up(a.t, kBN);
+  if (a.Cv) {
+    dim3 g(Tpad / kBN, a.heads);
+    hipLaunchKernelGGL((transpose_v_kernel<float, T, D>), g, dim3(256), 0, a.stream, a.Cv,
+                       (T*)a.Vt, a.t, Tpad);
+  }
+  const int BM = kFlashWaves * 32;
+  FlashParams fp;
+  fp.Q = a.Q; fp.K = a.Ck; fp.Vt = a.Vt;
+  fp.bias = a.bias; fp.keypos = a.keypos; fp.Y = a.Y;
+  fp.lse = a.lse; fp.rowstat = a.rowstat; fp.O = a.O; fp.rowres = a.rowres;
+  fp.n = a.n; fp.Tk = a.t; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
+  fp.n_qtiles = (a.n + BM - 1) / BM;
+  fp.c2 = a.scale * kLog2e;
+  launch_flash<T, D, true>(fp, a.causal, a.Cv != nullptr, a.stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_cmp_attention(const CmpAttnArgs& a) {
+  if (a.bf16) return a.d == 128 ? launch_cmp_t<bf16, 128>(a) : launch_cmp_t<bf16, 64>(a);
+  return a.d == 128 ? launch_cmp_t<float, 128>(a) : launch_cmp_t<float, 64>(a);
+}
+
 size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize) {
   const size_t vt = align_up((size_t)heads * d * round_up((int)T, kBN) * esize);
   const size_t rs = align_up((size_t)heads * n * sizeof(float2));
@@ -434,4 +514,10 @@ size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize) {
   return align_up((size_t)heads * d * round_up((int)T, kBN) * esize);
 }
 
+}  // namespace amc
+
+namespace amc {
+size_t cmp_vt_bytes(int64_t heads, int64_t t, int64_t d, int esize) {
+  return align_up((size_t)heads * d * round_up((int)t, kBN) * esize);
+}
 }  // namespace amc

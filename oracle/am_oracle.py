@@ -78,11 +78,12 @@ def _chunks(n: int, T: int, budget: int = 1 << 24):
 # --------------------------------------------------------------------------------------
 # S1 + S2: full-cache statistics
 # --------------------------------------------------------------------------------------
-def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True):
+def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True, rows=None):
     """lse [n], O [n, d] (or None) and per-key (sum p, sum p^2, max p) over queries.
 
     Q [n, d], K and V [T, d], all float64. p_ij = exp(s_ij - lse_i) for visible pairs, 0
-    otherwise. Queries are processed in chunks only to bound memory.
+    otherwise. Queries are processed in chunks only to bound memory. `rows` gives the
+    query indices (positions) of the rows of Q when Q is a subset of a problem's queries.
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
@@ -93,9 +94,10 @@ def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True):
     colsq = np.zeros(T)
     colmax = np.zeros(T)
     keys = np.arange(T)
+    rows = np.arange(n) if rows is None else np.asarray(rows)
     for a, b in _chunks(n, T):
         s = scale * (Q[a:b] @ K.T)
-        vis = visible(np.arange(a, b), keys, causal, group)
+        vis = visible(rows[a:b], keys, causal, group)
         s = np.where(vis, s, -np.inf)
         m = s.max(axis=1)
         lse[a:b] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
