@@ -11,6 +11,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16-byte staging chunk (a native vector type, so arrays of it stay in registers)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Eight consecutive elements along the contraction dimension: the per-lane share of one
 // 16-deep k-step of a 32x32 MFMA tile (lane l holds k = 8 * (l / 32) .. + 7).
@@ -30,6 +32,20 @@ __device__ __forceinline__ void mma16(f32x16& c, const f32x8& a, const f32x8& b)
 #pragma unroll
   for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
 }
+
+// Eight floats to the operand type, by value (no address taken, so the temporaries stay
+// in registers).
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type pack8(float a0, float a1, float a2, float a3,
+                                                      float a4, float a5, float a6, float a7) {
+  typename V8<T>::type r;
+  r[0] = (T)a0; r[1] = (T)a1; r[2] = (T)a2; r[3] = (T)a3;
+  r[4] = (T)a4; r[5] = (T)a5; r[6] = (T)a6; r[7] = (T)a7;
+  return r;
+}
+#define AM_PACK8(T, x, o) \
+  pack8<T>((x)[(o) + 0], (x)[(o) + 1], (x)[(o) + 2], (x)[(o) + 3], (x)[(o) + 4], (x)[(o) + 5], \
+           (x)[(o) + 6], (x)[(o) + 7])
 
 template <typename T> __device__ __forceinline__ typename V8<T>::type cvt8(const float* x);
 template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(const float* x) {

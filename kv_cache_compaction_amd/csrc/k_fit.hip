@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(const GramParams p) {
   int ta, tb;
   tri_index(tri, ta, tb);
   const bool diag = ta == tb;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int n = p.n, t = p.t;
   const T* Qh = (const T*)p.Q + (size_t)head * n * D;
   const T* Ch = (const T*)p.Ck + (size_t)head * t * D;
@@ -172,8 +173,8 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(const GramParams p) {
           mv[j] = vis ? v : 0.f;
           if (!VALUE && diag) hacc += mv[j] * tgs[ql];
         }
-        mb[bid[bi]][0][lane] = cvt8<bf16>(mv);
-        mb[bid[bi]][1][lane] = cvt8<bf16>(mv + 8);
+        mb[bid[bi]][0][lane] = AM_PACK8(bf16, mv, 0);
+        mb[bid[bi]][1][lane] = AM_PACK8(bf16, mv, 8);
       }
     }
     __syncthreads();

@@ -27,6 +27,8 @@
 #include "am_common.hpp"
 #include "am_internal.hpp"
 
+#include <type_traits>
+
 namespace amc {
 
 constexpr int kBN = 64;  // keys per flash-pass tile
@@ -75,11 +77,11 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const Ti* __restrict__
 // ------------------------------------------------------------------------------------
 // Flash pass.
 // ------------------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int BN>
 struct FlashLds {
   static constexpr int KP = D + epc<T>();    // K tile row pitch (+16 B against bank conflicts)
-  static constexpr int VP = kBN + epc<T>();  // Vt tile row pitch
-  static constexpr int K_ELEMS = kBN * KP;
+  static constexpr int VP = BN + epc<T>();   // Vt tile row pitch
+  static constexpr int K_ELEMS = BN * KP;
   static constexpr int BUF = K_ELEMS + D * VP;
 };
 
@@ -96,67 +98,90 @@ struct FlashParams {
   float c2;
 };
 
+// Launch shape (measured on MI355X at the long causal workload): 8 waves of 32 queries
+// each, two waves per SIMD so one wave's softmax overlaps the other's MFMAs; 64-key tiles
+// (32 for fp32 operands at d = 128, for LDS) in a ring of three LDS buffers with one
+// barrier per tile; the running max is rescaled lazily.
+constexpr int kFlashWaves = 8;
+template <typename T, int D> constexpr int flash_bn() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
+constexpr float kLazyTau = 8.f;  // rescale only when the row max grows by more than 2^8
+
 template <typename T, int D, int WAVES, bool CAUSAL, bool WITH_O, bool BIASED>
 __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashParams p) {
-  using L = FlashLds<T, D>;
+  constexpr int BN = flash_bn<T, D>();
+  using L = FlashLds<T, D, BN>;
   typedef typename V8<T>::type v8;
+  constexpr int NKB = BN / 32;                // 32-key blocks per tile
   constexpr int NT = WAVES * 64;
   constexpr int BM = WAVES * 32;
+  constexpr int NBUF = 3;
   constexpr int E = epc<T>();
   constexpr int KCPR = D / E;                 // 16-byte chunks per K row
-  constexpr int VCPR = kBN / E;               // 16-byte chunks per Vt row
-  constexpr int KPT = kBN * KCPR / NT;        // K chunks per thread
-  constexpr int VPT = WITH_O ? D * VCPR / NT : 0;
+  constexpr int VCPR = BN / E;                // 16-byte chunks per Vt row
+  constexpr int KCH = BN * KCPR, VCH = D * VCPR;   // 16-byte chunks per K / Vt tile
+  constexpr int KPT = (KCH + NT - 1) / NT;         // K chunks per thread
+  constexpr int VPT = WITH_O ? (VCH + NT - 1) / NT : 0;
   constexpr int KC = D / 16;                  // 16-deep k-steps over the head dim
-  static_assert(kBN * KCPR % NT == 0 && D * VCPR % NT == 0, "tile/thread mismatch");
+  constexpr int DB = D / 32;
 
-  __shared__ __align__(16) T lds[2 * L::BUF];
-  __shared__ float kbias[BIASED ? 2 : 1][BIASED ? kBN : 1];
-  __shared__ int kposs[BIASED ? 2 : 1][BIASED ? kBN : 1];
+  __shared__ __align__(16) T lds[NBUF * L::BUF];
+  __shared__ float kbias[BIASED ? NBUF : 1][BIASED ? BN : 1];
+  __shared__ int kposs[BIASED ? NBUF : 1][BIASED ? BN : 1];
 
   const int n = p.n, Tk = p.Tk, group = p.group;
   const int b = blockIdx.x;
   const int head = b % p.heads;
   const int tile = p.n_qtiles - 1 - b / p.heads;  // late (longest under the causal mask) first
   const int q0 = tile * BM;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
 
   const T* Qh = (const T*)p.Q + (size_t)head * n * D;
   const T* Kh = (const T*)p.K + (size_t)head * Tk * D;
   const T* Vh = (const T*)p.Vt + (size_t)head * D * p.Tpad;
 
-  const int qi = q0 + wave * 32 + r;
-  const int qrow = min(qi, n - 1);
+  const int wq0 = q0 + wave * 32;            // first query of this wave
+  const int qi = wq0 + r;                    // this lane's query (column of S^T)
+  const int qpos = qi / group;
   v8 bq[KC];
+  {
+    const int qrow = min(qi, n - 1);
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) bq[kc] = *(const v8*)(Qh + (size_t)qrow * D + kc * 16 + hh * 8);
+    for (int kc = 0; kc < KC; ++kc) bq[kc] = *(const v8*)(Qh + (size_t)qrow * D + kc * 16 + hh * 8);
+  }
 
   int kend = Tk;
   if (CAUSAL && !BIASED) kend = min(Tk, (min(q0 + BM, n) - 1) / group + 1);
-  const int ntiles = (kend + kBN - 1) / kBN;
-  const int qpos = qi / group;
-  const int wave_first_pos = (q0 + wave * 32) / group;
+  const int ntiles = (kend + BN - 1) / BN;
+  // leading tiles this wave can take without any mask
+  int nfull = Tk / BN;
+  if (CAUSAL) nfull = BIASED ? 0 : min(nfull, (wq0 / group + 1) / BN);
+  nfull = min(nfull, ntiles);
 
-  uint4 kreg[KPT];
-  uint4 vreg[VPT > 0 ? VPT : 1];
+  u32x4 kreg[KPT];
+  u32x4 vreg[VPT > 0 ? VPT : 1];
   float breg = 0.f;
   int preg = 0;
   auto gload = [&](int kt) {
-    const int k0 = kt * kBN;
+    const int k0 = kt * BN;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NT;
-      const int row = c / KCPR, col = (c % KCPR) * E;
-      const int kr = min(k0 + row, Tk - 1);
-      kreg[i] = *(const uint4*)(Kh + (size_t)kr * D + col);
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / KCPR, col = (c % KCPR) * E;
+        const int kr = min(k0 + row, Tk - 1);
+        kreg[i] = *(const u32x4*)(Kh + (size_t)kr * D + col);
+      }
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + i * NT;
-      const int row = c / VCPR, col = (c % VCPR) * E;
-      vreg[i] = *(const uint4*)(Vh + (size_t)row * p.Tpad + k0 + col);
+      if (VCH % NT == 0 || c < VCH) {
+        const int row = c / VCPR, col = (c % VCPR) * E;
+        vreg[i] = *(const u32x4*)(Vh + (size_t)row * p.Tpad + k0 + col);
+      }
     }
-    if (BIASED && tid < kBN) {
+    if (BIASED && tid < BN) {
       const int kr = min(k0 + tid, Tk - 1);
       breg = p.bias[(size_t)head * Tk + kr] * kLog2e;
       preg = p.keypos[(size_t)head * Tk + kr];
@@ -168,116 +193,129 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NT;
-      *(uint4*)(Ks + (c / KCPR) * L::KP + (c % KCPR) * E) = kreg[i];
+      if (KCH % NT == 0 || c < KCH) *(u32x4*)(Ks + (c / KCPR) * L::KP + (c % KCPR) * E) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + i * NT;
-      *(uint4*)(Vs + (c / VCPR) * L::VP + (c % VCPR) * E) = vreg[i];
+      if (VCH % NT == 0 || c < VCH) *(u32x4*)(Vs + (c / VCPR) * L::VP + (c % VCPR) * E) = vreg[i];
     }
-    if (BIASED && tid < kBN) {
+    if (BIASED && tid < BN) {
       kbias[buf][tid] = breg;
       kposs[buf][tid] = preg;
     }
   };
 
-  f32x16 oacc[WITH_O ? D / 32 : 1];
+  f32x16 oacc[WITH_O ? DB : 1];
 #pragma unroll
-  for (int db = 0; db < (WITH_O ? D / 32 : 1); ++db)
+  for (int db = 0; db < (WITH_O ? DB : 1); ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  if (ntiles > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
-    const T* Ks = lds + buf * L::BUF;
-    const T* Vs = Ks + L::K_ELEMS;
-    const int k0 = kt * kBN;
-
-    f32x16 s[2];
+  // One tile: S^T = K Q^T, lazy online softmax, O^T += V^T P^T. MASK is a compile-time
+  // choice so unmasked tiles carry no per-element visibility code.
+  auto tile_step = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (kt + 2 < ntiles) gload(kt + 2);
+    const int buf = kt % NBUF;
+    const int k0 = kt * BN;
+    const T* Ks = lds + buf * L::BUF + kperm(r) * L::KP + hh * 8;
+    f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
-      const T* arow = Ks + (kb * 32 + kperm(r)) * L::KP + hh * 8;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) mma16(s[kb], *(const v8*)(arow + kc * 16), bq[kc]);
-    }
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        mma16(s[kb], *(const v8*)(Ks + kb * 32 * L::KP + kc * 16), bq[kc]);
 
-    const bool need_mask = (k0 + kBN > Tk) || (CAUSAL && (BIASED || k0 + kBN - 1 > wave_first_pos));
-    float x[32];
+    float x[NKB * 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int kl = kb * 32 + (j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8));
-        float v = s[kb][j] * p.c2;
-        if (BIASED) v += kbias[buf][kl];
-        if (need_mask) {
+        float v = BIASED ? s[kb][j] * p.c2 + kbias[buf][kl] : s[kb][j];
+        if (MASK) {
           const int key = k0 + kl;
           const int pos = BIASED ? kposs[buf][kl] : key;
-          const bool vis = key < Tk && (!CAUSAL || pos <= qpos);
-          v = vis ? v : -INFINITY;
+          v = (key < Tk && (!CAUSAL || pos <= qpos)) ? v : -INFINITY;
         }
         x[kb * 16 + j] = v;
       }
-    float tmax = x[0];
+    float tmax = fmaxf(x[0], x[1]);
 #pragma unroll
-    for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, x[i]);
+    for (int i = 2; i < NKB * 16; i += 2) tmax = fmaxf(tmax, fmaxf(x[i], x[i + 1]));
     tmax = fmaxf(tmax, shfl_xor32(tmax));
-    const float mnew = fmaxf(m, tmax);
-    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = ex2(m - msafe);
+    if (!BIASED) tmax *= p.c2;
+    const bool need = tmax > m + kLazyTau;
+    if (__ballot(need)) {
+      const float mnew = need ? tmax : m;
+      const float alpha = ex2(m - mnew);   // 0 when m was -inf, 1 when unchanged
+      l *= alpha;
+      if constexpr (WITH_O) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+      }
+      m = mnew;
+    }
+    const float msafe = m == -INFINITY ? 0.f : m;
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = ex2(x[i] - msafe);
+    for (int i = 0; i < NKB * 16; ++i) {
+      x[i] = BIASED ? ex2(x[i] - msafe) : ex2(__builtin_fmaf(x[i], p.c2, -msafe));
       psum += x[i];
     }
-    l = l * alpha + psum;
-    m = mnew;
-
+    l += psum;
     if constexpr (WITH_O) {
+      const T* Vs = lds + buf * L::BUF + L::K_ELEMS + r * L::VP + hh * 8;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const v8 pb = cvt8<T>(&x[kb * 16 + kk * 8]);
+          const v8 pb = AM_PACK8(T, x, kb * 16 + kk * 8);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            mma16(oacc[db], *(const v8*)(Vs + (db * 32 + r) * L::VP + kb * 32 + kk * 16 + hh * 8),
-                  pb);
+          for (int db = 0; db < DB; ++db)
+            mma16(oacc[db], *(const v8*)(Vs + db * 32 * L::VP + kb * 32 + kk * 16), pb);
         }
     }
-    if (kt + 1 < ntiles) sstore(buf ^ 1);
+    if (kt + 2 < ntiles) sstore((kt + 2) % NBUF);
     __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+    if (ntiles > 1) {
+      gload(1);
+      sstore(1);
+    }
   }
+  __syncthreads();
+  // every wave runs ntiles iterations with one barrier each; only the split differs
+  for (int kt = 0; kt < nfull; ++kt) tile_step(kt, std::false_type{});
+  for (int kt = nfull; kt < ntiles; ++kt) tile_step(kt, std::true_type{});
 
   const float ltot = l + shfl_xor32(l);
   if constexpr (WITH_O) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (p.Y) {
-      // residual against the targets: sum over this lane's d values, then both halves
       float e = 0.f, yy = 0.f;
-      const float* Yrow = p.Y + ((size_t)head * n + qrow) * D;
+      const float* Yrow = p.Y + ((size_t)head * n + min(qi, n - 1)) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           const float4 y = *(const float4*)(Yrow + db * 32 + jq * 8 + hh * 4);
-          const float d0 = oacc[db][jq * 4 + 0] * inv - y.x, d1 = oacc[db][jq * 4 + 1] * inv - y.y;
-          const float d2 = oacc[db][jq * 4 + 2] * inv - y.z, d3 = oacc[db][jq * 4 + 3] * inv - y.w;
+          const float d0 = oacc[db][jq * 4 + 0] * inv - y.x;
+          const float d1 = oacc[db][jq * 4 + 1] * inv - y.y;
+          const float d2 = oacc[db][jq * 4 + 2] * inv - y.z;
+          const float d3 = oacc[db][jq * 4 + 3] * inv - y.w;
           e += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
           yy += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
         }
@@ -287,7 +325,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
     } else if (qi < n) {
       float* Orow = p.O + ((size_t)head * n + qi) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           float4 v;
@@ -309,13 +347,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 // ------------------------------------------------------------------------------------
 // Column-score pass.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int WAVES, bool CAUSAL>
+// MODE: 0 = RMS (sum of p^2), 1 = MEAN (sum of p), 2 = MAX (max of p). Only the requested
+// statistic is computed: RMS exponentiates 2 ((x - m) - log2 l) directly (p^2, the doubling
+// is exact) and MAX keeps the max of the exponent and exponentiates once at the end.
+template <typename T, int D> constexpr int colscore_kb() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
+
+template <typename T, int D, int WAVES, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float2* __restrict__ rowstat,
-    float* __restrict__ score, int mode, int n, int Tk, int group, float c2, int heads) {
+    float* __restrict__ score, int n, int Tk, int group, float c2, int heads) {
   typedef typename V8<T>::type v8;
+  constexpr int KB = colscore_kb<T, D>();  // 32-key blocks per wave
   constexpr int NT = WAVES * 64;
-  constexpr int BK = WAVES * 32;
+  constexpr int BK = WAVES * 32 * KB;
   constexpr int E = epc<T>();
   constexpr int QP = D + E;
   constexpr int QCPR = D / E;
@@ -323,6 +367,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   constexpr int KC = D / 16;
   static_assert(kBQ * QCPR % NT == 0, "tile/thread mismatch");
   static_assert(kBQ <= NT, "row statistics load");
+  const float f = MODE == 0 ? 2.f : 1.f;   // exponent factor
 
   __shared__ __align__(16) T qs[2][kBQ * QP];
   __shared__ float2 rs[2][kBQ];
@@ -330,23 +375,29 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   const int b = blockIdx.x;
   const int head = b % heads;
   const int k0 = (b / heads) * BK;  // key block 0 (most queries under the causal mask) first
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const T* Qh = Q + (size_t)head * n * D;
   const T* Kh = K + (size_t)head * Tk * D;
   const float2* RSh = rowstat + (size_t)head * n;
 
-  const int key = k0 + wave * 32 + r;
-  const int krow = min(key, Tk - 1);
-  v8 bk[KC];
+  const int wk0 = k0 + wave * 32 * KB;
+  v8 bk[KB][KC];
+  int key[KB];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) bk[kc] = *(const v8*)(Kh + (size_t)krow * D + kc * 16 + hh * 8);
+  for (int kb = 0; kb < KB; ++kb) {
+    key[kb] = wk0 + kb * 32 + r;
+    const int krow = min(key[kb], Tk - 1);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      bk[kb][kc] = *(const v8*)(Kh + (size_t)krow * D + kc * 16 + hh * 8);
+  }
 
   int qbeg = 0;
   if (CAUSAL) qbeg = (min(n, k0 * group) / kBQ) * kBQ;
   const int ntiles = (n - qbeg + kBQ - 1) / kBQ;
-  const int wave_k0 = k0 + wave * 32;
 
-  uint4 qreg[QPT];
+  u32x4 qreg[QPT];
   float2 rreg = make_float2(0.f, 0.f);
   auto gload = [&](int it) {
     const int qt0 = qbeg + it * kBQ;
@@ -354,82 +405,115 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     for (int i = 0; i < QPT; ++i) {
       const int c = tid + i * NT;
       const int row = c / QCPR, col = (c % QCPR) * E;
-      qreg[i] = *(const uint4*)(Qh + (size_t)min(qt0 + row, n - 1) * D + col);
+      qreg[i] = *(const u32x4*)(Qh + (size_t)min(qt0 + row, n - 1) * D + col);
     }
-    if (tid < kBQ) rreg = RSh[min(qt0 + tid, n - 1)];
+    if (tid < kBQ) {
+      const float2 st = RSh[min(qt0 + tid, n - 1)];
+      rreg = make_float2(f * st.x, f * st.y);
+    }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
       const int c = tid + i * NT;
-      *(uint4*)(&qs[buf][(c / QCPR) * QP + (c % QCPR) * E]) = qreg[i];
+      *(u32x4*)(&qs[buf][(c / QCPR) * QP + (c % QCPR) * E]) = qreg[i];
     }
     if (tid < kBQ) rs[buf][tid] = rreg;
   };
 
-  double asum = 0.0, asq = 0.0;
-  float amax = 0.f;
+  double acc[KB];
+  float amx[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    acc[kb] = 0.0;
+    amx[kb] = -INFINITY;
+  }
+  const float fc2 = f * c2;
+
+  // One query tile; MASK is a compile-time choice (diagonal tiles and a ragged end only).
+  auto tile_step = [&](int it, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(it + 1);
+    const int qt0 = qbeg + it * kBQ;
+#pragma unroll
+    for (int qb = 0; qb < kBQ / 32; ++qb) {
+      f32x16 s[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+      const T* arow = &qs[buf][(qb * 32 + r) * QP + hh * 8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const v8 a = *(const v8*)(arow + kc * 16);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) mma16(s[kb], a, bk[kb][kc]);
+      }
+      float st_m[16], st_l[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float2 st = rs[buf][qb * 32 + crow(j, hh)];
+        st_m[j] = st.x;
+        st_l[j] = st.y;
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float part = MODE == 2 ? -INFINITY : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float e = __builtin_fmaf(s[kb][j], fc2, -st_m[j]) - st_l[j];
+          if (MASK) {
+            const int q = qt0 + qb * 32 + crow(j, hh);
+            e = (q < n && (!CAUSAL || key[kb] <= q / group)) ? e : -INFINITY;
+          }
+          if (MODE == 2) part = fmaxf(part, e);
+          else part += ex2(e);
+        }
+        if (MODE == 2) amx[kb] = fmaxf(amx[kb], part);
+        else acc[kb] += (double)part;
+      }
+    }
+    if (it + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  };
+
   if (ntiles > 0) {
     gload(0);
     sstore(0);
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(it + 1);
-    const int qt0 = qbeg + it * kBQ;
-    const bool need_mask =
-        (qt0 + kBQ > n) || (CAUSAL && qt0 / group < wave_k0 + 31);
+  // leading tiles on the causal diagonal and a ragged last tile need the mask
+  int nhead = 0;
+  if (CAUSAL) nhead = min(ntiles, max(0, (group * (wk0 + 32 * KB - 1) - qbeg + kBQ - 1) / kBQ));
+  int nbody = ntiles - ((qbeg + ntiles * kBQ > n) ? 1 : 0);
+  nbody = max(nbody, nhead);
+  for (int it = 0; it < nhead; ++it) tile_step(it, std::true_type{});
+  for (int it = nhead; it < nbody; ++it) tile_step(it, std::false_type{});
+  for (int it = nbody; it < ntiles; ++it) tile_step(it, std::true_type{});
 #pragma unroll
-    for (int qb = 0; qb < kBQ / 32; ++qb) {
-      f32x16 s;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[j] = 0.f;
-      const T* arow = &qs[buf][(qb * 32 + r) * QP + hh * 8];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) mma16(s, *(const v8*)(arow + kc * 16), bk[kc]);
-      float ps = 0.f, pq = 0.f, pm = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int ql = qb * 32 + crow(j, hh);
-        const float2 st = rs[buf][ql];
-        float v = ex2((s[j] * c2 - st.x) - st.y);
-        if (need_mask) {
-          const int q = qt0 + ql;
-          const bool vis = q < n && (!CAUSAL || key <= q / group);
-          v = vis ? v : 0.f;
-        }
-        ps += v;
-        pq += v * v;
-        pm = fmaxf(pm, v);
-      }
-      asum += (double)ps;
-      asq += (double)pq;
-      amax = fmaxf(amax, pm);
-    }
-    if (it + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
-  }
-  asum += __shfl_xor(asum, 32, 64);
-  asq += __shfl_xor(asq, 32, 64);
-  amax = fmaxf(amax, shfl_xor32(amax));
-  if (hh == 0 && key < Tk) {
+  for (int kb = 0; kb < KB; ++kb) {
     float out;
-    if (mode == 0) out = (float)sqrt(asq / (double)n);
-    else if (mode == 1) out = (float)(asum / (double)n);
-    else out = amax;
-    score[(size_t)head * Tk + key] = out;
+    if (MODE == 2) {
+      const float mx = fmaxf(amx[kb], shfl_xor32(amx[kb]));
+      out = ex2(mx);
+    } else {
+      const double tot = acc[kb] + __shfl_xor(acc[kb], 32, 64);
+      out = MODE == 0 ? (float)sqrt(tot / (double)n) : (float)(tot / (double)n);
+    }
+    if (hh == 0 && key[kb] < Tk) score[(size_t)head * Tk + key[kb]] = out;
   }
 }
 
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
-constexpr int kFlashWaves = 4;
 constexpr int kScoreWaves = 4;
 
 template <typename T, int D, bool BIASED>
-static void launch_flash(const FlashParams& fp, bool causal, bool with_o, hipStream_t st) {
+static void launch_flash(FlashParams fp, bool causal, bool with_o, hipStream_t st) {
+  constexpr int BM = kFlashWaves * 32;
+  fp.n_qtiles = (fp.n + BM - 1) / BM;
   const dim3 g(fp.n_qtiles * fp.heads), blk(kFlashWaves * 64);
 #define AM_FLASH(C, W) \
   hipLaunchKernelGGL((flash_fwd_kernel<T, D, kFlashWaves, C, W, BIASED>), g, blk, 0, st, fp)
@@ -450,27 +534,27 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
     hipLaunchKernelGGL((transpose_v_kernel<T, T, D>), g, dim3(256), 0, a.stream, (const T*)a.V,
                        (T*)a.Vt, a.T, Tpad);
   }
-  const int BM = kFlashWaves * 32;
   FlashParams fp;
   fp.Q = a.Q; fp.K = a.K; fp.Vt = a.Vt;
   fp.bias = nullptr; fp.keypos = nullptr; fp.Y = nullptr;
   fp.lse = a.lse; fp.rowstat = (float2*)a.rowstat; fp.O = a.O; fp.rowres = nullptr;
   fp.n = a.n; fp.Tk = a.T; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
-  fp.n_qtiles = (a.n + BM - 1) / BM;
   fp.c2 = c2;
   launch_flash<T, D, false>(fp, a.causal, a.O != nullptr, a.stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.score) return e;
-  const int BK = kScoreWaves * 32;
+  const int BK = kScoreWaves * 32 * colscore_kb<T, D>();
   const dim3 gs(((a.T + BK - 1) / BK) * a.heads), bs(kScoreWaves * 64);
-  if (a.causal)
-    hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, true>), gs, bs, 0, a.stream,
-                       (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.mode,
-                       a.n, a.T, a.group, c2, a.heads);
-  else
-    hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, false>), gs, bs, 0, a.stream,
-                       (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.mode,
-                       a.n, a.T, a.group, c2, a.heads);
+#define AM_SCORE(C, M)                                                                          \
+  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M>), gs, bs, 0, a.stream,          \
+                     (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.n, a.T, \
+                     a.group, c2, a.heads)
+  if (a.causal) {
+    if (a.mode == 0) AM_SCORE(true, 0); else if (a.mode == 1) AM_SCORE(true, 1); else AM_SCORE(true, 2);
+  } else {
+    if (a.mode == 0) AM_SCORE(false, 0); else if (a.mode == 1) AM_SCORE(false, 1); else AM_SCORE(false, 2);
+  }
+#undef AM_SCORE
   return hipGetLastError();
 }
 
@@ -487,13 +571,11 @@ static hipError_t launch_cmp_t(const CmpAttnArgs& a) {
     hipLaunchKernelGGL((transpose_v_kernel<float, T, D>), g, dim3(256), 0, a.stream, a.Cv,
                        (T*)a.Vt, a.t, Tpad);
   }
-  const int BM = kFlashWaves * 32;
   FlashParams fp;
   fp.Q = a.Q; fp.K = a.Ck; fp.Vt = a.Vt;
   fp.bias = a.bias; fp.keypos = a.keypos; fp.Y = a.Y;
   fp.lse = a.lse; fp.rowstat = a.rowstat; fp.O = a.O; fp.rowres = a.rowres;
   fp.n = a.n; fp.Tk = a.t; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
-  fp.n_qtiles = (a.n + BM - 1) / BM;
   fp.c2 = a.scale * kLog2e;
   launch_flash<T, D, true>(fp, a.causal, a.Cv != nullptr, a.stream);
   return hipGetLastError();
