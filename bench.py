@@ -31,6 +31,28 @@ FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 (used for fp32-input workloads)
 HBM_PEAK_GBS = 8000.0
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "flash_fwd_causal8_T32k_gqa4_traffic.txt")
+
+
+def flash_traffic(workload: str):
+    """HBM bytes per flash-pass launch from the committed counter profile, or None when the
+    profile is for another workload or the kernel source changed since it was taken."""
+    import hashlib
+    if workload != "causal8_T32k_gqa4" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and not line.startswith((" ", "#")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, kv.get("source", ""))
+    if not os.path.isfile(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -84,6 +106,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="causal8_T32k_gqa4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one plain 256 MiB device copy; hardware "
+                         "byte counters of that copy calibrate the HBM traffic of the kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -142,6 +167,15 @@ def main():
     achieved = flops_flash / (ms_flash * 1e-3) / 1e12
     score_tflops = flops_scores / (ms_targets * 1e-3) / 1e12
 
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written",
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on a bounded sample (host cores)",
@@ -164,7 +198,7 @@ def main():
         "config": {"workload": w.name, "heads": w.heads, "d": w.d, "T": w.T, "n": w.n, "t": w.t,
                    "causal": w.causal, "group": w.group, "visible_pairs": pairs},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": flash_traffic(w.name),
                      "kernel": "flash_fwd_kernel (with the 0.1% V transpose in the timed call)"},
         "cpu_baseline": cpu,
         "stages_ms": {"flash_pass": ms_flash, "score_passes": ms_targets, "select": ms_select,

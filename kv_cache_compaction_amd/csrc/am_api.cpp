@@ -260,7 +260,10 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
   fa.w_lo = opt->w_lo; fa.w_hi = opt->w_hi; fa.tol = opt->nnls_tol;
   fa.max_iter = opt->nnls_max_iter;
   fa.lambda = opt->ridge_lambda;
+  fa.keep_cmp_stats = true;
   if ((e = launch_fit_beta(fa)) != hipSuccess) return AM_ERR_DEVICE;
+  fa.keep_cmp_stats = false;
+  fa.have_cmp_stats = true;
   fa.beta_in = beta; fa.O = O; fa.Cv = Cv;
   fa.mass_resid = nullptr;
   fa.keep_status = true;

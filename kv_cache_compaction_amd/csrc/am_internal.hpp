@@ -65,7 +65,9 @@ struct FitArgs {
   bool causal, bf16, absolute;
   float scale, w_lo, w_hi, tol, lambda;
   int max_iter;
-  bool keep_status;  // value fit after the beta fit: OR into head_status instead of clearing
+  bool keep_status;     // value fit after the beta fit: OR into head_status instead of clearing
+  bool keep_cmp_stats;  // beta fit: leave the compacted row statistics at the workspace start
+  bool have_cmp_stats;  // value fit: those statistics (same beta) are already there
   void* ws; size_t ws_bytes;
   hipStream_t stream;
 };

@@ -29,6 +29,8 @@
 #include "am_common.hpp"
 #include "am_internal.hpp"
 
+#include <type_traits>
+
 namespace amc {
 
 constexpr int kGT = 128;  // Gram tile (keys per side)
@@ -62,48 +64,65 @@ struct GramParams {
   float c2;
 };
 
+// Workgroup shape: 8 waves (two per SIMD, so one wave's exponentials overlap another's
+// Gram MFMAs). Off-diagonal tiles: wave w owns key block w (a0..a3, b0..b3) and computes
+// its 32 x 32 score blocks for every 32-query half of a step with one register copy of
+// the C_k fragment; diagonal tiles split the four key blocks over the two query halves.
+// A step's design fragments go to one of two LDS buffers; the Gram product of step i-1
+// runs from the other buffer while step i's scores are computed, with one barrier per
+// step. Q (and Y) tiles are prefetched through registers one step ahead.
+template <typename T> constexpr int gram_gq() { return sizeof(T) == 4 ? 32 : 64; }
+
 template <typename T, int D, bool VALUE>
-__global__ __launch_bounds__(256, 1) void gram_kernel(const GramParams p) {
+__global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
   typedef typename V8<T>::type v8;
-  constexpr int E = epcf<T>(), QP = D + E, KC = D / 16, YP = kGQ + 8;
-  __shared__ __align__(16) T qs[kGQ * QP];
-  __shared__ float shs[kGQ], tgs[kGQ];
-  __shared__ __align__(16) bf16x8 mb[8][2][64];
-  __shared__ __align__(16) bf16 yts[VALUE ? D * YP : 8];
+  constexpr int GQ = gram_gq<T>();          // queries per step
+  constexpr int QH = GQ / 32;               // 32-query halves per step
+  constexpr int NT = 512;
+  constexpr int E = epcf<T>(), QP = D + E, KC = D / 16, YP = GQ + 8;
+  constexpr int QCPR = D / E;               // 16-byte chunks per Q row
+  constexpr int QCH = GQ * QCPR;            // chunks per Q tile
+  constexpr int QPT = (QCH + NT - 1) / NT;
+  constexpr int YCH = VALUE ? GQ * D / 4 : 0;  // float4 chunks per Y tile
+  constexpr int YPT = VALUE ? (YCH + NT - 1) / NT : 0;
+  __shared__ __align__(16) T qs[2][GQ * QP];
+  __shared__ float shs[2][GQ], tgs[2][GQ];
+  __shared__ __align__(16) bf16x8 mb[2][8][QH][2][64];
+  __shared__ __align__(16) bf16 yts[VALUE ? 2 : 1][VALUE ? D * YP : 8];
+  __shared__ float hl[8][32];
 
   const int tri = blockIdx.x, chunk = blockIdx.y, head = blockIdx.z;
   int ta, tb;
   tri_index(tri, ta, tb);
   const bool diag = ta == tb;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = p.n, t = p.t;
   const T* Qh = (const T*)p.Q + (size_t)head * n * D;
   const T* Ch = (const T*)p.Ck + (size_t)head * t * D;
   const float* Sh = p.shift2 + (size_t)head * n;
+  const float* Yh = VALUE ? p.Y + (size_t)head * n * D : nullptr;
 
-  const int nblk = diag ? 1 : 2;
-  const int bid[2] = {diag ? wave : 2 * wave, 2 * wave + 1};
-  v8 bck[2][KC];
-  int kpos[2] = {0, 0};
-  float kb2[2] = {0.f, 0.f};
-  bool kval[2] = {false, false};
+  // this wave's score work: key block `kbid` (0-3 a, 4-7 b) for query halves [qh0, qh1)
+  const int kbid = diag ? (wave & 3) : wave;
+  const int qh0 = diag ? (QH == 2 ? (wave >> 2) : 0) : 0;
+  const int qh1 = diag ? (QH == 2 ? qh0 + 1 : (wave < 4 ? 1 : 0)) : QH;
+  const int key = (kbid < 4) ? ta * kGT + 32 * kbid + r : tb * kGT + 32 * (kbid - 4) + r;
+  const bool kval = key < t;
+  const int kr = min(key, t - 1);
+  v8 bck[KC];
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi) {
-    if (bi < nblk) {
-      const int s = bid[bi];
-      const int key = (s < 4) ? ta * kGT + 32 * s + r : tb * kGT + 32 * (s - 4) + r;
-      kval[bi] = key < t;
-      const int kr = min(key, t - 1);
+  for (int kc = 0; kc < KC; ++kc) bck[kc] = *(const v8*)(Ch + (size_t)kr * D + kc * 16 + hh * 8);
+  // first query that sees this key under the causal mask; keys past t get a -inf bias
+  const int kq0 = p.causal ? p.keypos[(size_t)head * t + kr] * p.group : 0;
+  const float kb2 = !kval ? -INFINITY : (VALUE ? p.bias[(size_t)head * t + kr] * kLog2e : 0.f);
+  int kq0max = kval ? kq0 : 0;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) bck[bi][kc] = *(const v8*)(Ch + (size_t)kr * D + kc * 16 + hh * 8);
-      kpos[bi] = p.keypos[(size_t)head * t + kr];
-      if (VALUE) kb2[bi] = p.bias[(size_t)head * t + kr] * kLog2e;
-    } else {
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) bck[bi][kc] = bck[0][kc];
-    }
-  }
+  for (int o = 32; o > 0; o >>= 1) kq0max = max(kq0max, __shfl_xor(kq0max, o, 64));
+  kq0max = __builtin_amdgcn_readfirstlane(kq0max);
+
+  // this wave's Gram blocks: a-block gx, b-blocks gy0, gy0 + 1 (and R blocks on diagonal)
+  const int gx = wave >> 1, gy0 = 2 * (wave & 1);
 
   const int qa = chunk * p.chunk;
   const int qb = min(n, qa + p.chunk);
@@ -112,112 +131,211 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(const GramParams p) {
     // queries before the later of the two blocks' first positions see nothing in one block
     const int f = max(p.keypos[(size_t)head * t + min(ta * kGT, t - 1)],
                       p.keypos[(size_t)head * t + min(tb * kGT, t - 1)]);
-    qstart = max(qa, (int)min((long long)f * p.group, (long long)qb) / kGQ * kGQ);
+    qstart = max(qa, (int)min((long long)f * p.group, (long long)qb) / 32 * 32);
   }
+  const int nsteps = (qb - qstart + GQ - 1) / GQ;
 
-  f32x16 gacc[2][2];
-  f32x16 racc[VALUE ? D / 32 : 1];
+  u32x4 qreg[QPT];
+  float4 yreg[YPT > 0 ? YPT : 1];
+  float sreg = 0.f, treg = 1.f;
+  auto qload = [&](int st) {
+    const int q0 = qstart + st * GQ;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int c = tid + i * NT;
+      if (QCH % NT == 0 || c < QCH) {
+        const int row = c / QCPR, col = (c % QCPR) * E;
+        qreg[i] = *(const u32x4*)(Qh + (size_t)min(q0 + row, n - 1) * D + col);
+      }
+    }
+    if (tid < GQ) {
+      const int q = min(q0 + tid, n - 1);
+      sreg = Sh[q];
+      treg = p.target ? p.target[(size_t)head * n + q] : 1.f;
+    }
+  };
+  auto qstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int c = tid + i * NT;
+      if (QCH % NT == 0 || c < QCH)
+        *(u32x4*)&qs[buf][(c / QCPR) * QP + (c % QCPR) * E] = qreg[i];
+    }
+    if (tid < GQ) {
+      shs[buf][tid] = sreg;
+      tgs[buf][tid] = treg;
+    }
+  };
+  auto yload = [&](int st) {
+    if constexpr (VALUE) {
+      const int q0 = qstart + st * GQ;
+#pragma unroll
+      for (int i = 0; i < YPT; ++i) {
+        const int c = tid + i * NT;
+        if (YCH % NT == 0 || c < YCH) {
+          const int row = c / (D / 4), col = (c % (D / 4)) * 4;
+          yreg[i] = *(const float4*)(Yh + (size_t)min(q0 + row, n - 1) * D + col);
+        }
+      }
+    }
+  };
+  auto ystore = [&](int buf) {
+    if constexpr (VALUE) {
+#pragma unroll
+      for (int i = 0; i < YPT; ++i) {
+        const int c = tid + i * NT;
+        if (YCH % NT == 0 || c < YCH) {
+          const int row = c / (D / 4), col = (c % (D / 4)) * 4;
+          yts[buf][(col + 0) * YP + row] = (bf16)yreg[i].x;
+          yts[buf][(col + 1) * YP + row] = (bf16)yreg[i].y;
+          yts[buf][(col + 2) * YP + row] = (bf16)yreg[i].z;
+          yts[buf][(col + 3) * YP + row] = (bf16)yreg[i].w;
+        }
+      }
+    }
+  };
+
+  f32x16 gacc[2];
+  f32x16 racc[VALUE ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int j = 0; j < 16; ++j) gacc[i][j] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) gacc[i][jj][j] = 0.f;
+  for (int i = 0; i < (VALUE ? 2 : 1); ++i)
 #pragma unroll
-  for (int db = 0; db < (VALUE ? D / 32 : 1); ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) racc[db][j] = 0.f;
+    for (int j = 0; j < 16; ++j) racc[i][j] = 0.f;
   float hacc = 0.f;
-  const int wa = wave >> 1, wb = wave & 1;
 
-  for (int q0 = qstart; q0 < qb; q0 += kGQ) {
-    for (int c = tid; c < kGQ * D / E; c += 256) {
-      const int row = c / (D / E), col = (c % (D / E)) * E;
-      *(uint4*)&qs[row * QP + col] = *(const uint4*)(Qh + (size_t)min(q0 + row, n - 1) * D + col);
-    }
-    if (tid < kGQ) {
-      const int q = min(q0 + tid, n - 1);
-      shs[tid] = Sh[q];
-      tgs[tid] = p.target ? p.target[(size_t)head * n + q] : 1.f;
-    }
-    if (VALUE && diag) {
-      const float* Yh = p.Y + (size_t)head * n * D;
-      for (int c = tid; c < kGQ * D / 4; c += 256) {
-        const int row = c / (D / 4), col = (c % (D / 4)) * 4;
-        const float4 y = *(const float4*)(Yh + (size_t)min(q0 + row, n - 1) * D + col);
-        yts[(col + 0) * YP + row] = (bf16)y.x;
-        yts[(col + 1) * YP + row] = (bf16)y.y;
-        yts[(col + 2) * YP + row] = (bf16)y.z;
-        yts[(col + 3) * YP + row] = (bf16)y.w;
+  // Gram (and R) MFMAs over the design fragments of one finished step
+  auto gram_part = [&](int buf) {
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 av = mb[buf][gx][qh][ks][lane];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int y = gy0 + i;
+          mma16(gacc[i], av, mb[buf][diag ? y : 4 + y][qh][ks][lane]);
+        }
+        if (VALUE && diag) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            if ((gy0 + i) * 32 < D)   // d = 64 has two 32-column blocks
+              mma16(racc[i], av,
+                    *(const bf16x8*)&yts[buf][((gy0 + i) * 32 + r) * YP + qh * 32 + ks * 16 + hh * 8]);
+        }
       }
-    }
-    __syncthreads();
+  };
+
+  if (nsteps > 0) {
+    qload(0);
+    qstore(0);
+    if (nsteps > 1) qload(1);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (diag) yload(st);   // this step's targets (diagonal tiles only); staged as Y^T below
+    if (st > 0) gram_part(buf ^ 1);
+    // scores, design entries, fragments for this step; NH independent 32-query halves are
+    // interleaved so their MFMA chains overlap. MASK (wave-uniform) is needed only where
+    // some query of the step cannot see a key of this wave's block, or past the chunk end.
+    const int q0 = qstart + st * GQ;
+    auto scores = [&](auto nh_tag, int qhb, auto mask_tag) {
+      constexpr int NH = decltype(nh_tag)::value;
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 sacc[NH];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      if (bi < nblk) {
-        f32x16 s;
+      for (int u = 0; u < NH; ++u)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[j] = 0.f;
-        const T* arow = qs + kperm(r) * QP + hh * 8;
+        for (int j = 0; j < 16; ++j) sacc[u][j] = 0.f;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) mma16(s, *(const v8*)(arow + kc * 16), bck[bi][kc]);
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int u = 0; u < NH; ++u)
+          mma16(sacc[u], *(const v8*)&qs[buf][((qhb + u) * 32 + kperm(r)) * QP + hh * 8 + kc * 16],
+                bck[kc]);
+#pragma unroll
+      for (int u = 0; u < NH; ++u) {
+        const int qh = qhb + u;
+        // row shifts of this lane's 16 queries: rows 8h..8h+7 and 16+8h..16+8h+7 of the half
+        const float4* s4 = (const float4*)&shs[buf][qh * 32 + 8 * hh];
+        const float4 sa = s4[0], sb = s4[1], sc = s4[4], sd = s4[5];
+        const float shv[16] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w,
+                               sc.x, sc.y, sc.z, sc.w, sd.x, sd.y, sd.z, sd.w};
         float mv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int ql = j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8);
-          const int q = q0 + ql;
-          const float sh = shs[ql];
-          const float v = ex2(s[j] * p.c2 + kb2[bi] - sh);
-          const bool vis = kval[bi] && q < qb && sh > -INFINITY &&
-                           (!p.causal || kpos[bi] <= q / p.group);
-          mv[j] = vis ? v : 0.f;
-          if (!VALUE && diag) hacc += mv[j] * tgs[ql];
+          float v = ex2(sacc[u][j] * p.c2 + kb2 - shv[j]);
+          if (MASK) {
+            const int q = q0 + qh * 32 + (j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8));
+            v = (q < qb && q >= kq0 && shv[j] > -INFINITY) ? v : 0.f;
+          }
+          mv[j] = v;
         }
-        mb[bid[bi]][0][lane] = AM_PACK8(bf16, mv, 0);
-        mb[bid[bi]][1][lane] = AM_PACK8(bf16, mv, 8);
+        if (!VALUE && diag) {
+          const float4* t4 = (const float4*)&tgs[buf][qh * 32 + 8 * hh];
+          const float4 ta4 = t4[0], tb4 = t4[1], tc4 = t4[4], td4 = t4[5];
+          const float tg[16] = {ta4.x, ta4.y, ta4.z, ta4.w, tb4.x, tb4.y, tb4.z, tb4.w,
+                                tc4.x, tc4.y, tc4.z, tc4.w, td4.x, td4.y, td4.z, td4.w};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) hacc += mv[j] * tg[j];
+        }
+        mb[buf][kbid][qh][0][lane] = AM_PACK8(bf16, mv, 0);
+        mb[buf][kbid][qh][1][lane] = AM_PACK8(bf16, mv, 8);
       }
-    }
-    __syncthreads();
+    };
+    const bool mask = (q0 < kq0max) || (q0 + GQ > qb);
+    if (!diag) {
+      if constexpr (VALUE) {   // one query half at a time keeps the value variant in registers
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int ai = 2 * wa + i;
-        const int bj = diag ? 2 * wb + jj : 4 + 2 * wb + jj;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) mma16(gacc[i][jj], mb[ai][ks][lane], mb[bj][ks][lane]);
+        for (int qh = 0; qh < QH; ++qh) {
+          if (mask) scores(std::integral_constant<int, 1>{}, qh, std::true_type{});
+          else scores(std::integral_constant<int, 1>{}, qh, std::false_type{});
+        }
+      } else {
+        if (mask) scores(std::integral_constant<int, QH>{}, 0, std::true_type{});
+        else scores(std::integral_constant<int, QH>{}, 0, std::false_type{});
       }
-    if (VALUE && diag) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          mma16(racc[db], mb[wave][ks][lane],
-                *(const bf16x8*)&yts[(db * 32 + r) * YP + ks * 16 + hh * 8]);
+    } else if (qh0 < qh1) {
+      if (mask) scores(std::integral_constant<int, 1>{}, qh0, std::true_type{});
+      else scores(std::integral_constant<int, 1>{}, qh0, std::false_type{});
     }
+    if (diag) ystore(buf);   // read by the Gram part of the next step
+    // next step's query tile
+    if (st + 1 < nsteps) qstore(buf ^ 1);
+    if (st + 2 < nsteps) qload(st + 2);
     __syncthreads();
   }
+  if (nsteps > 0) gram_part((nsteps - 1) & 1);
 
   float* Gp = p.Gpart + (((size_t)head * p.nch + chunk) * p.ntri + tri) * kGT * kGT;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        Gp[((2 * wa + i) * 32 + crow(j, hh)) * kGT + (2 * wb + jj) * 32 + r] = gacc[i][jj][j];
+    for (int j = 0; j < 16; ++j)
+      Gp[(gx * 32 + crow(j, hh)) * kGT + (gy0 + i) * 32 + r] = gacc[i][j];
   if (diag) {
     if (!VALUE) {
-      hacc += shfl_xor32(hacc);
-      if (hh == 0) p.Vpart[((size_t)head * p.nch + chunk) * p.tpad + ta * kGT + 32 * wave + r] = hacc;
+      hacc += shfl_xor32(hacc);   // (off-diagonal tiles never write h)
+      if (hh == 0) hl[wave][r] = hacc;
+      __syncthreads();
+      if (wave < 4 && hh == 0) {
+        const float hv = hl[wave][r] + (QH == 2 ? hl[wave + 4][r] : 0.f);
+        p.Vpart[((size_t)head * p.nch + chunk) * p.tpad + ta * kGT + 32 * wave + r] = hv;
+      }
     } else {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int i = 0; i < 2; ++i)
+        if ((gy0 + i) * 32 < D)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int row = ta * kGT + 32 * wave + crow(j, hh);
-          p.Vpart[(((size_t)head * p.nch + chunk) * p.tpad + row) * D + db * 32 + r] = racc[db][j];
-        }
+          for (int j = 0; j < 16; ++j) {
+            const int row = ta * kGT + 32 * gx + crow(j, hh);
+            p.Vpart[(((size_t)head * p.nch + chunk) * p.tpad + row) * D + (gy0 + i) * 32 + r] =
+                racc[i][j];
+          }
     }
   }
 }
@@ -270,6 +388,22 @@ __global__ __launch_bounds__(256) void vec_reduce_kernel(const float* __restrict
 //   mode 0: shift = lse * log2 e (relative mass design)
 //   mode 1: shift = max_i lse_i * log2 e, target = 2^(lse_i log2 e - shift) (absolute)
 //   mode 2: shift = m + log2 l of the biased compacted pass (value design)
+__global__ __launch_bounds__(256) void shift_rows_kernel(const float* __restrict__ lse,
+                                                         const float2* __restrict__ rowstat,
+                                                         float* __restrict__ shift2, int n,
+                                                         int mode) {
+  const int head = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const size_t o = (size_t)head * n + i;
+  if (mode == 0) {
+    shift2[o] = lse[o] * kLog2e;
+  } else {
+    const float2 st = rowstat[o];
+    shift2[o] = st.x + st.y;
+  }
+}
+
 __global__ __launch_bounds__(256) void shift_kernel(const float* __restrict__ lse,
                                                     const float2* __restrict__ rowstat,
                                                     float* __restrict__ shift2,
@@ -316,6 +450,7 @@ struct NnlsState {
   float* TK;        // [h, 2] momentum scalars
   float* hsmax;     // [h]
   int* iters;       // [h]
+  int* fin;         // [h] ring slot of the converged iterate, -1 while running
   int t, nblk;
   float lo, hi, tol;
 };
@@ -373,6 +508,7 @@ __global__ __launch_bounds__(256) void nnls_prep_kernel(NnlsState s, int32_t* st
     s.hsmax[head] = hm;
     s.TK[head * 2 + 0] = 1.f;
     s.iters[head] = 0;
+    s.fin[head] = -1;
     if (status) status[head] = nb > 0.f ? AM_HEAD_NONFINITE_BIT : 0;
   }
 }
@@ -421,6 +557,7 @@ __global__ __launch_bounds__(256) void nnls_step_kernel(NnlsState s, int k) {
   __shared__ float ys[kMaxFitT];
   __shared__ float red[4];
   const int head = blockIdx.y, blk = blockIdx.x, t = s.t;
+  if (s.fin[head] >= 0) return;   // converged in an earlier launch: nothing left to do
   const float L = nnls_L(s, head);
   const float2* P = s.P + ((size_t)head * 2 + (k & 1)) * s.nblk;
   float dot = 0.f, gm = 0.f;
@@ -483,6 +620,7 @@ __global__ __launch_bounds__(256) void nnls_step_kernel(NnlsState s, int k) {
     if (blk == 0) {
       s.TK[head * 2 + ((k + 1) & 1)] = tn;
       if (!done) s.iters[head] = k + 1;
+      else s.fin[head] = k % 3;   // later launches exit at once
     }
   }
 }
@@ -491,10 +629,14 @@ __global__ __launch_bounds__(256) void nnls_finish_kernel(NnlsState s, int K, fl
                                                           float* beta, int32_t* status) {
   __shared__ float red[4];
   const int head = blockIdx.x, t = s.t;
-  const float* v = s.V + ((size_t)head * 3 + K % 3) * t;
-  const float2* P = s.P + ((size_t)head * 2 + (K & 1)) * s.nblk;
+  const int fin = s.fin[head];
+  const float* v = s.V + ((size_t)head * 3 + (fin >= 0 ? fin : K % 3)) * t;
+  // converged heads were stopped on the tolerance; otherwise check the last partials
   float gm = 0.f;
-  for (int b = 0; b < s.nblk; ++b) gm = fmaxf(gm, P[b].y);
+  if (fin < 0) {
+    const float2* P = s.P + ((size_t)head * 2 + (K & 1)) * s.nblk;
+    for (int b = 0; b < s.nblk; ++b) gm = fmaxf(gm, P[b].y);
+  }
   const float thr = s.tol * fmaxf(s.hsmax[head], 1e-30f);
   bool bad = false;
   for (int j = threadIdx.x; j < t; j += 256) {
@@ -510,47 +652,175 @@ __global__ __launch_bounds__(256) void nnls_finish_kernel(NnlsState s, int K, fl
     status[head] |= (gm > thr ? AM_HEAD_NNLS_BIT : 0) | (nb > 0.f ? AM_HEAD_NONFINITE_BIT : 0);
 }
 
+// Persistent solver for t <= kNnlsSingle: one workgroup per head runs the same iteration
+// (Jacobi scaling, step 1/L from power iteration, restarted momentum, stop on the scaled
+// gradient-mapping norm) with all vectors in LDS. Thread i owns row i; by symmetry it
+// forms (G z)_i as sum_j G[j][i] z_j, so every step of j reads one row of G coalesced.
+// G itself is staged in LDS when it fits (t <= 128), otherwise read from L2.
+constexpr int kNnlsSingle = 1024;
+constexpr int kNnlsLdsG = 128;
+
+__global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, int max_iter,
+                                                                  float* w_out, float* beta,
+                                                                  int32_t* status) {
+  __shared__ float zs[kNnlsSingle];
+  __shared__ float Gl[kNnlsLdsG * kNnlsLdsG];
+  __shared__ float red[kNnlsSingle / 64], red2[kNnlsSingle / 64];
+  const int head = blockIdx.x, t = s.t, i = threadIdx.x;
+  const bool own = i < t;
+  const float* Gg = s.G + (size_t)head * t * t;
+  const bool in_lds = t <= kNnlsLdsG;
+  if (in_lds)
+    for (int e = i; e < t * t; e += kNnlsSingle) Gl[e] = Gg[e];
+  __syncthreads();
+  const float* Gs = in_lds ? Gl : Gg;
+
+  auto bsum = [&](float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((i & 63) == 0) red[i >> 6] = v;
+    __syncthreads();
+    float r = 0.f;
+    for (int w = 0; w < kNnlsSingle / 64; ++w) r += red[w];
+    return r;
+  };
+  auto bmax2 = [&](float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    __syncthreads();
+    if ((i & 63) == 0) red2[i >> 6] = v;
+    __syncthreads();
+    float r = red2[0];
+    for (int w = 1; w < kNnlsSingle / 64; ++w) r = fmaxf(r, red2[w]);
+    return r;
+  };
+  // (D^-1 G D^-1 x)_i with zs = D^-1 x already in LDS
+  auto row = [&](float di) {
+    float acc = 0.f;
+    if (own)
+      for (int j = 0; j < t; ++j) acc += Gs[(size_t)j * t + i] * zs[j];
+    return acc * di;
+  };
+
+  float di = 0.f, hsi = 0.f, gii = 0.f, hi_ = 0.f;
+  if (own) {
+    gii = Gs[(size_t)i * t + i];
+    hi_ = s.hv[(size_t)head * t + i];
+    di = gii > 0.f ? rsqrtf(gii) : 0.f;
+    hsi = hi_ * di;
+  }
+  const float bad = bmax2((own && (!isfinite(gii) || !isfinite(hi_))) ? 1.f : 0.f);
+  const float hsmax = bmax2(fabsf(hsi));
+  const float lo_i = di > 0.f ? s.lo / di : 0.f;
+  const float hi_i = di > 0.f ? (isinf(s.hi) ? INFINITY : s.hi / di) : 0.f;
+
+  // power iteration for L = lambda_max(D^-1 G D^-1)
+  float x = own ? rsqrtf((float)t) : 0.f;
+  float nrm = 1.f;
+  for (int k = 0; k < kPow; ++k) {
+    __syncthreads();
+    zs[i] = x * di;
+    __syncthreads();
+    const float y = row(di);
+    nrm = sqrtf(bsum(y * y));
+    x = nrm > 0.f ? y / nrm : 0.f;
+  }
+  const float L = 1.1f * nrm + 1e-30f;
+
+  float v = lo_i, vp = lo_i, tk = 1.f, dot = 0.f, gm = INFINITY;
+  const float thr = s.tol * fmaxf(hsmax, 1e-30f);
+  int it = 0;
+  for (; it < max_iter; ++it) {
+    if (it > 0 && gm <= thr) break;
+    const bool restart = dot > 0.f;
+    const float tn = restart ? 1.f : 0.5f * (1.f + sqrtf(1.f + 4.f * tk * tk));
+    const float mom = restart ? 0.f : (tk - 1.f) / tn;
+    const float y = v + mom * (v - vp);
+    __syncthreads();
+    zs[i] = y * di;
+    __syncthreads();
+    const float g = row(di) - hsi;
+    const float vn = di > 0.f ? fminf(fmaxf(y - g / L, lo_i), hi_i) : 0.f;
+    dot = bsum(own ? (vn - v) * (y - vn) : 0.f);
+    gm = bmax2(own ? fabsf(y - vn) * L : 0.f);
+    vp = v;
+    v = vn;
+    tk = tn;
+  }
+  bool badw = false;
+  if (own) {
+    float w = di > 0.f ? v * di : s.lo;
+    w = fminf(fmaxf(w, s.lo), s.hi);
+    badw = !isfinite(w);
+    if (w_out) w_out[(size_t)head * t + i] = w;
+    beta[(size_t)head * t + i] = w > 0.f ? logf(w) : -INFINITY;
+  }
+  const float nbw = bmax2(badw ? 1.f : 0.f);
+  if (i == 0) {
+    s.iters[head] = it;
+    if (status)
+      status[head] = (gm > thr ? AM_HEAD_NNLS_BIT : 0) |
+                     ((bad > 0.f || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0);
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // Blocked fp64 Cholesky and triangular solves on A [h, ld, ld], R [h, ld, D]
 // ------------------------------------------------------------------------------------
 // Factor the diagonal block kb in place (lower) and store its inverse in Linv[h, nb, 64, 64].
+// Right-looking on the unscaled column: step c subtracts a_ic a_jc / a_cc from the trailing
+// lower triangle (one barrier per column; the pivot is read by every thread), and the
+// column is scaled by 1 / sqrt(pivot) once at the end.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
                                                         int nb, int32_t* status) {
   __shared__ double a[kNB][kNB + 1];
   __shared__ double li[kNB][kNB + 1];
-  __shared__ int flag;
+  __shared__ double dinv[kNB];
   const int head = blockIdx.x, tid = threadIdx.x;
   double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
   for (int e = tid; e < kNB * kNB; e += 256) a[e / kNB][e % kNB] = Ah[(size_t)(e / kNB) * ld + e % kNB];
-  if (tid == 0) flag = 0;
   __syncthreads();
+  bool bad = false;
   for (int c = 0; c < kNB; ++c) {
-    if (tid == 0) {
-      double pv = a[c][c];
-      if (!(pv > 0.0)) {
-        flag = 1;
-        pv = 1e-300;
-      }
-      a[c][c] = sqrt(pv);
+    double pv = a[c][c];
+    if (!(pv > 0.0)) {
+      bad = true;
+      pv = 1e-300;
     }
-    __syncthreads();
-    const double dc = a[c][c];
-    for (int i = c + 1 + tid; i < kNB; i += 256) a[i][c] /= dc;
-    __syncthreads();
-    const int m = kNB - c - 1;
-    for (int e = tid; e < m * m; e += 256) {
-      const int i = c + 1 + e / m, j = c + 1 + e % m;
-      if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+    const double ipv = 1.0 / pv;
+    // lower triangle of the trailing block: (i, j) with c < j <= i, fixed 64 x 64 map
+#pragma unroll
+    for (int k2 = 0; k2 < kNB * kNB / 256; ++k2) {
+      const int e = tid + 256 * k2;
+      const int i = e >> 6, j = e & 63;
+      if (j > c && j <= i) a[i][j] -= a[i][c] * a[j][c] * ipv;
     }
     __syncthreads();
   }
+  if (tid < kNB) {
+    const double pv = a[tid][tid];
+    dinv[tid] = pv > 0.0 ? 1.0 / sqrt(pv) : 1.0 / sqrt(1e-300);
+  }
+  __syncthreads();
+  // L_ic = a_ic / sqrt(pivot_c) (i > c), L_cc = sqrt(pivot_c)
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int i = e / kNB, c = e % kNB;
+    if (c < i) a[i][c] *= dinv[c];
+    else if (c == i) a[i][c] = 1.0 / dinv[c];
+  }
+  __syncthreads();
   // inverse of the lower factor, one column per thread (forward substitution)
   if (tid < kNB) {
     const int j = tid;
     for (int i = 0; i < kNB; ++i) {
+      if (i < j) {
+        li[i][j] = 0.0;
+        continue;
+      }
       double v = (i == j) ? 1.0 : 0.0;
       for (int k2 = j; k2 < i; ++k2) v -= a[i][k2] * li[k2][j];
-      li[i][j] = (i < j) ? 0.0 : v / a[i][i];
+      li[i][j] = v * dinv[i];
     }
   }
   __syncthreads();
@@ -559,7 +829,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv,
     Ah[(size_t)i * ld + j] = j <= i ? a[i][j] : 0.0;
     Linv[(((size_t)head * nb + kb) * kNB + i) * kNB + j] = li[i][j];
   }
-  if (tid == 0 && flag && status) status[head] |= AM_HEAD_CHOL_BIT;
+  if (tid == 0 && bad && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
 }
 
 // L_ik = A_ik Linv_kk^T for block rows i > kb.
@@ -670,36 +940,41 @@ __global__ __launch_bounds__(256) void store_cv_kernel(const double* R, float* C
 // ------------------------------------------------------------------------------------
 // residual reductions (one workgroup per head, fixed order)
 // ------------------------------------------------------------------------------------
-// mass: mean_i (2^(lc_i - sh_i) - b_i)^2 with lc from the biased compacted pass.
-__global__ __launch_bounds__(256) void mass_resid_kernel(const float2* __restrict__ rowstat_cmp,
-                                                         const float* __restrict__ shift2,
-                                                         const float* __restrict__ target,
-                                                         float* __restrict__ out, int n) {
+// Two-level, fixed-order reductions: kResBlk workgroups per head write partial sums
+// (fp64) that one workgroup per head then adds in order.
+constexpr int kResBlk = 64;
+
+// mass: per-query (Z_cmp / Z - b)^2 with Z_cmp / Z = 2^(lc - shift) from the biased pass
+__global__ __launch_bounds__(256) void mass_resid_part_kernel(const float2* __restrict__ rowstat_cmp,
+                                                              const float* __restrict__ shift2,
+                                                              const float* __restrict__ target,
+                                                              double2* __restrict__ part, int n) {
   __shared__ double red[256];
-  const int head = blockIdx.x;
+  const int head = blockIdx.y;
   double acc = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += kResBlk * 256) {
     const size_t o = (size_t)head * n + i;
     const float2 st = rowstat_cmp[o];
     const float b = target ? target[o] : 1.f;
-    const double z = (st.y == -INFINITY) ? 0.0 : exp2((double)st.x + (double)st.y - (double)shift2[o]);
-    acc += (z - b) * (z - b);
+    const float z = (st.y == -INFINITY) ? 0.f : ex2((st.x - shift2[o]) + st.y);
+    acc += (double)(z - b) * (double)(z - b);
   }
   red[threadIdx.x] = acc;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (threadIdx.x < s2) red[threadIdx.x] += red[threadIdx.x + s2];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[head] = (float)(red[0] / n);
+  if (threadIdx.x == 0)
+    part[(size_t)head * kResBlk + blockIdx.x] = make_double2(red[0], blockIdx.x == 0 ? (double)n : 0.0);
 }
 
-__global__ __launch_bounds__(256) void out_resid_kernel(const float2* __restrict__ rowres,
-                                                        float* __restrict__ out, int n) {
+__global__ __launch_bounds__(256) void out_resid_part_kernel(const float2* __restrict__ rowres,
+                                                             double2* __restrict__ part, int n) {
   __shared__ double re[256], ry[256];
-  const int head = blockIdx.x;
+  const int head = blockIdx.y;
   double e = 0.0, y = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += kResBlk * 256) {
     const float2 v = rowres[(size_t)head * n + i];
     e += v.x;
     y += v.y;
@@ -707,14 +982,28 @@ __global__ __launch_bounds__(256) void out_resid_kernel(const float2* __restrict
   re[threadIdx.x] = e;
   ry[threadIdx.x] = y;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      re[threadIdx.x] += re[threadIdx.x + s];
-      ry[threadIdx.x] += ry[threadIdx.x + s];
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (threadIdx.x < s2) {
+      re[threadIdx.x] += re[threadIdx.x + s2];
+      ry[threadIdx.x] += ry[threadIdx.x + s2];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[head] = (float)(ry[0] > 0.0 ? re[0] / ry[0] : 0.0);
+  if (threadIdx.x == 0) part[(size_t)head * kResBlk + blockIdx.x] = make_double2(re[0], ry[0]);
+}
+
+// out[h] = sum(x) / sum(y) over the partials (mass: y holds n, so this is the mean)
+__global__ void resid_final_kernel(const double2* __restrict__ part, float* __restrict__ out,
+                                   int heads) {
+  const int head = blockIdx.x * 64 + threadIdx.x;
+  if (head >= heads) return;
+  double x = 0.0, y = 0.0;
+  for (int b = 0; b < kResBlk; ++b) {
+    const double2 v = part[(size_t)head * kResBlk + b];
+    x += v.x;
+    y += v.y;
+  }
+  out[head] = (float)(y > 0.0 ? x / y : 0.0);
 }
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
@@ -750,7 +1039,7 @@ struct Carve {
 struct BetaPlan {
   float* shift2; float* target; float* Gpart; float* hpart; float* G; float* hv;
   float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float* TK; float* hsmax;
-  int* iters; float2* rowstat_cmp; int32_t* status;
+  int* iters; int* fin; float2* rowstat_cmp; double2* part; int32_t* status;
   size_t bytes;
 };
 
@@ -762,6 +1051,8 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
   const int ntri = gram_ntri((int)t);
   const int nblk = ((int)t + kRB - 1) / kRB;
   BetaPlan p;
+  p.rowstat_cmp = c.take<float2>(heads * n);   // first in both plans: shared with the value fit
+  p.part = c.take<double2>(heads * kResBlk);
   p.shift2 = c.take<float>(heads * n);
   p.target = c.take<float>(heads * n);
   p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
@@ -777,15 +1068,15 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
   p.TK = c.take<float>(heads * 2);
   p.hsmax = c.take<float>(heads);
   p.iters = c.take<int>(heads);
-  p.rowstat_cmp = c.take<float2>(heads * n);
+  p.fin = c.take<int>(heads);
   p.status = c.take<int32_t>(heads);
   p.bytes = c.off;
   return p;
 }
 
 struct ValuePlan {
-  float2* rowstat_cmp; float* shift2; float* Gpart; float* Rpart; double* A; double* R;
-  double* Linv; void* Vt; float2* rowres; int32_t* status;
+  float2* rowstat_cmp; double2* part; float* shift2; float* Gpart; float* Rpart; double* A;
+  double* R; double* Linv; void* Vt; float2* rowres; int32_t* status;
   size_t bytes;
 };
 
@@ -799,6 +1090,7 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   const int ld = chol_ld((int)t);
   ValuePlan p;
   p.rowstat_cmp = c.take<float2>(heads * n);
+  p.part = c.take<double2>(heads * kResBlk);
   p.shift2 = c.take<float>(heads * n);
   p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
   p.Rpart = c.take<float>((size_t)heads * nch * tpad * d);
@@ -821,7 +1113,7 @@ size_t fit_values_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d) {
 
 template <typename T, int D, bool VALUE>
 static void launch_gram(const GramParams& gp, int heads, hipStream_t st) {
-  hipLaunchKernelGGL((gram_kernel<T, D, VALUE>), dim3(gp.ntri, gp.nch, heads), dim3(256), 0, st, gp);
+  hipLaunchKernelGGL((gram_kernel<T, D, VALUE>), dim3(gp.ntri, gp.nch, heads), dim3(512), 0, st, gp);
 }
 
 static void launch_gram_any(const GramParams& gp, int heads, int d, bool bf, bool value,
@@ -844,8 +1136,12 @@ hipError_t launch_fit_beta(const FitArgs& a) {
   int32_t* status = a.head_status ? a.head_status : pl.status;
   const int tpad = gram_ntile(t) * kGT, nch = gram_nch(H, n, t), ntri = gram_ntri(t);
   // row shifts and right-hand side
-  hipLaunchKernelGGL(shift_kernel, dim3(H), dim3(256), 0, st, a.lse, (const float2*)nullptr,
-                     pl.shift2, pl.target, n, a.absolute ? 1 : 0);
+  if (a.absolute)
+    hipLaunchKernelGGL(shift_kernel, dim3(H), dim3(256), 0, st, a.lse, (const float2*)nullptr,
+                       pl.shift2, pl.target, n, 1);
+  else
+    hipLaunchKernelGGL(shift_rows_kernel, dim3(cdiv(n, 256), H), dim3(256), 0, st, a.lse,
+                       (const float2*)nullptr, pl.shift2, n, 0);
   GramParams gp;
   gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = nullptr;
   gp.shift2 = pl.shift2; gp.target = a.absolute ? pl.target : nullptr; gp.Y = nullptr;
@@ -861,17 +1157,24 @@ hipError_t launch_fit_beta(const FitArgs& a) {
   NnlsState s;
   s.G = pl.G; s.hv = pl.hv; s.dinv = pl.dinv; s.hs = pl.hs; s.V = pl.V; s.X = pl.X;
   s.PN = pl.PN; s.P = pl.P; s.TK = pl.TK; s.hsmax = pl.hsmax; s.iters = pl.iters;
+  s.fin = pl.fin;
   s.t = t; s.nblk = (t + kRB - 1) / kRB;
   s.lo = a.w_lo; s.hi = a.w_hi; s.tol = a.tol;
-  hipLaunchKernelGGL(nnls_prep_kernel, dim3(H), dim3(256), 0, st, s, status);
-  for (int k = 0; k < kPow; ++k)
-    hipLaunchKernelGGL(nnls_power_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
-  for (int k = 0; k < a.max_iter; ++k)
-    hipLaunchKernelGGL(nnls_step_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
-  hipLaunchKernelGGL(nnls_finish_kernel, dim3(H), dim3(256), 0, st, s, a.max_iter, a.w, a.beta,
-                     status);
-  // mass residual from the biased compacted pass: Z_cmp / Z = 2^(lc - lse2)
-  if (a.mass_resid) {
+  if (t <= kNnlsSingle) {
+    hipLaunchKernelGGL(nnls_single_kernel, dim3(H), dim3(kNnlsSingle), 0, st, s, a.max_iter, a.w,
+                       a.beta, status);
+  } else {
+    hipLaunchKernelGGL(nnls_prep_kernel, dim3(H), dim3(256), 0, st, s, status);
+    for (int k = 0; k < kPow; ++k)
+      hipLaunchKernelGGL(nnls_power_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
+    for (int k = 0; k < a.max_iter; ++k)
+      hipLaunchKernelGGL(nnls_step_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
+    hipLaunchKernelGGL(nnls_finish_kernel, dim3(H), dim3(256), 0, st, s, a.max_iter, a.w, a.beta,
+                       status);
+  }
+  // mass residual from the biased compacted pass: Z_cmp / Z = 2^(lc - lse2); the pass's row
+  // statistics are also what the value fit needs, so they are kept when asked for
+  if (a.mass_resid || a.keep_cmp_stats) {
     CmpAttnArgs ca;
     ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = a.beta; ca.keypos = a.idx; ca.Y = nullptr;
     ca.Vt = nullptr; ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
@@ -879,8 +1182,12 @@ hipError_t launch_fit_beta(const FitArgs& a) {
     ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
     hipError_t e = launch_cmp_attention(ca);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mass_resid_kernel, dim3(H), dim3(256), 0, st, pl.rowstat_cmp, pl.shift2,
-                       a.absolute ? pl.target : nullptr, a.mass_resid, n);
+    if (a.mass_resid) {
+      hipLaunchKernelGGL(mass_resid_part_kernel, dim3(kResBlk, H), dim3(256), 0, st,
+                         pl.rowstat_cmp, pl.shift2, a.absolute ? pl.target : nullptr, pl.part, n);
+      hipLaunchKernelGGL(resid_final_kernel, dim3(cdiv(H, 64)), dim3(64), 0, st,
+                         (const double2*)pl.part, a.mass_resid, H);
+    }
   }
   return hipGetLastError();
 }
@@ -900,10 +1207,13 @@ hipError_t launch_fit_values(const FitArgs& a) {
   ca.Vt = pl.Vt; ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
   ca.heads = H; ca.n = n; ca.t = t; ca.d = d; ca.group = a.group; ca.causal = a.causal;
   ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
-  hipError_t e = launch_cmp_attention(ca);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(shift_kernel, dim3(H), dim3(256), 0, st, (const float*)nullptr,
-                     (const float2*)pl.rowstat_cmp, pl.shift2, (float*)nullptr, n, 2);
+  hipError_t e = hipSuccess;
+  if (!a.have_cmp_stats) {   // else the beta fit left them at the start of the workspace
+    e = launch_cmp_attention(ca);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(shift_rows_kernel, dim3(cdiv(n, 256), H), dim3(256), 0, st,
+                     (const float*)nullptr, (const float2*)pl.rowstat_cmp, pl.shift2, n, 2);
   GramParams gp;
   gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = a.beta_in;
   gp.shift2 = pl.shift2; gp.target = nullptr; gp.Y = a.O;
@@ -949,7 +1259,10 @@ hipError_t launch_fit_values(const FitArgs& a) {
     cr.Cv = a.Cv; cr.Y = a.O; cr.rowstat = nullptr; cr.rowres = pl.rowres;
     e = launch_cmp_attention(cr);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(out_resid_kernel, dim3(H), dim3(256), 0, st, pl.rowres, a.out_resid, n);
+    hipLaunchKernelGGL(out_resid_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, pl.rowres,
+                       pl.part, n);
+    hipLaunchKernelGGL(resid_final_kernel, dim3(cdiv(H, 64)), dim3(64), 0, st,
+                       (const double2*)pl.part, a.out_resid, H);
   }
   return hipGetLastError();
 }
