@@ -186,6 +186,16 @@ def nnls_gram(G: np.ndarray, h: np.ndarray, tol: float | None = None):
     t = h.size
     if tol is None:
         tol = 1e-12 * max(1.0, float(np.abs(h).max())) * max(1.0, float(np.abs(np.diag(G)).max()))
+    # An interior optimum: if the unconstrained minimiser is strictly positive it is feasible,
+    # hence optimal for the constrained problem too (the KKT conditions hold with every
+    # variable free). Verified, not assumed.
+    try:
+        z = scipy.linalg.cho_solve(scipy.linalg.cho_factor(G, lower=True, check_finite=False), h,
+                                   check_finite=False)
+        if np.all(np.isfinite(z)) and np.all(z > 0) and nnls_kkt_residual(G, h, z) <= tol * 1e3:
+            return z
+    except np.linalg.LinAlgError:
+        pass
     w = np.zeros(t)
     P = np.zeros(t, dtype=bool)
     barred = np.zeros(t, dtype=bool)
