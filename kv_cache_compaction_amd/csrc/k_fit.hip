@@ -769,110 +769,200 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
 // Blocked fp64 Cholesky and triangular solves on A [h, ld, ld], R [h, ld, D]
 // ------------------------------------------------------------------------------------
 // Factor the diagonal block kb in place (lower) and store its inverse in Linv[h, nb, 64, 64].
-// Right-looking on the unscaled column: step c subtracts a_ic a_jc / a_cc from the trailing
-// lower triangle (one barrier per column; the pivot is read by every thread), and the
-// column is scaled by 1 / sqrt(pivot) once at the end.
+// 256 threads; thread (r, q) = (tid / 4, tid % 4) keeps entries (r, q + 4m), m < 16, of the
+// block in registers. Right-looking on unscaled columns: step c posts the current column c
+// (rows >= c) to LDS, and every thread subtracts a_rc a_jc / a_cc from its entries; the
+// posted columns are kept, so L_rc = col[c][r] / sqrt(col[c][c]) afterwards. The inverse X of
+// L is formed the same way, one posted row per step: X_k /= L_kk, then X_i -= L_ik X_k for
+// i > k. Every register index is a compile-time constant (the owner of column c is picked by
+// selects), so nothing lands in scratch memory.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
                                                         int nb, int32_t* status) {
-  __shared__ double a[kNB][kNB + 1];
-  __shared__ double li[kNB][kNB + 1];
-  __shared__ double dinv[kNB];
-  const int head = blockIdx.x, tid = threadIdx.x;
+  __shared__ double col[kNB][kNB];   // col[c][r] = a_rc at step c (r >= c)
+  __shared__ double xrow[kNB][kNB];  // xrow[k][j] = (L^-1)_kj
+  __shared__ double dinv[kNB];       // 1 / L_cc
+  const int head = blockIdx.x, tid = threadIdx.x, r = tid >> 2, q = tid & 3;
   double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
-  for (int e = tid; e < kNB * kNB; e += 256) a[e / kNB][e % kNB] = Ah[(size_t)(e / kNB) * ld + e % kNB];
-  __syncthreads();
+  double a[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) a[m] = Ah[(size_t)r * ld + q + 4 * m];
   bool bad = false;
   for (int c = 0; c < kNB; ++c) {
-    double pv = a[c][c];
+    double own = 0.0;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) own = (m == (c >> 2)) ? a[m] : own;
+    if (q == (c & 3) && r >= c) col[c][r] = own;
+    __syncthreads();
+    double pv = col[c][c];
     if (!(pv > 0.0)) {
       bad = true;
       pv = 1e-300;
     }
-    const double ipv = 1.0 / pv;
-    // lower triangle of the trailing block: (i, j) with c < j <= i, fixed 64 x 64 map
+    const double lr = r > c ? col[c][r] / pv : 0.0;
 #pragma unroll
-    for (int k2 = 0; k2 < kNB * kNB / 256; ++k2) {
-      const int e = tid + 256 * k2;
-      const int i = e >> 6, j = e & 63;
-      if (j > c && j <= i) a[i][j] -= a[i][c] * a[j][c] * ipv;
+    for (int m = 0; m < 16; ++m)
+      if (q + 4 * m > c) a[m] -= lr * col[c][q + 4 * m];
+  }
+  if (tid < kNB) {
+    const double pv = col[tid][tid];
+    dinv[tid] = 1.0 / sqrt(pv > 0.0 ? pv : 1e-300);
+  }
+  __syncthreads();
+  double x[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) x[m] = (q + 4 * m == r) ? 1.0 : 0.0;
+  for (int k = 0; k < kNB; ++k) {
+    if (r == k) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        x[m] *= dinv[k];
+        xrow[k][q + 4 * m] = x[m];
+      }
     }
     __syncthreads();
-  }
-  if (tid < kNB) {
-    const double pv = a[tid][tid];
-    dinv[tid] = pv > 0.0 ? 1.0 / sqrt(pv) : 1.0 / sqrt(1e-300);
-  }
-  __syncthreads();
-  // L_ic = a_ic / sqrt(pivot_c) (i > c), L_cc = sqrt(pivot_c)
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, c = e % kNB;
-    if (c < i) a[i][c] *= dinv[c];
-    else if (c == i) a[i][c] = 1.0 / dinv[c];
-  }
-  __syncthreads();
-  // inverse of the lower factor, one column per thread (forward substitution)
-  if (tid < kNB) {
-    const int j = tid;
-    for (int i = 0; i < kNB; ++i) {
-      if (i < j) {
-        li[i][j] = 0.0;
-        continue;
-      }
-      double v = (i == j) ? 1.0 : 0.0;
-      for (int k2 = j; k2 < i; ++k2) v -= a[i][k2] * li[k2][j];
-      li[i][j] = v * dinv[i];
+    if (r > k) {
+      const double lrk = col[k][r] * dinv[k];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) x[m] -= lrk * xrow[k][q + 4 * m];
     }
   }
   __syncthreads();
+  double* Lo = Linv + ((size_t)head * nb + kb) * kNB * kNB;
   for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    Ah[(size_t)i * ld + j] = j <= i ? a[i][j] : 0.0;
-    Linv[(((size_t)head * nb + kb) * kNB + i) * kNB + j] = li[i][j];
+    const int i = e >> 6, j = e & 63;
+    Ah[(size_t)i * ld + j] = j < i ? col[j][i] * dinv[j] : (j == i ? 1.0 / dinv[i] : 0.0);
+    Lo[e] = j <= i ? xrow[i][j] : 0.0;
   }
-  if (tid == 0 && bad && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
+  if (bad && q == 0 && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
 }
 
-// L_ik = A_ik Linv_kk^T for block rows i > kb.
+// 64-row fp64 blocks staged through LDS for the block kernels below. A loader issues all of
+// its global loads (16-byte, one per register pair) before it writes any of them to LDS, so
+// a block costs one memory latency rather than one per element.
+constexpr int kLdp = kNB + 1;   // LDS row pitch (odd: column reads by 16 rows hit 16 banks)
+
+template <int W>
+struct BlockRegs {
+  static constexpr int N = kNB * W / 2 / 256;   // double2 per thread (256 threads)
+  double2 r[N];
+  // src[u][v], 0 <= u < 64, 0 <= v < W, row stride `stride` doubles
+  __device__ __forceinline__ void load(const double* src, size_t stride, int tid) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const int e = (tid + 256 * q) * 2, u = e / W, v = e % W;
+      r[q] = *(const double2*)&src[(size_t)u * stride + v];
+    }
+  }
+  // dst[u][v] = src[u][v]  (TR = false)  or  dst[v][u] = src[u][v]  (TR = true)
+  template <bool TR, int P>
+  __device__ __forceinline__ void store(double (*dst)[P], int tid) const {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const int e = (tid + 256 * q) * 2, u = e / W, v = e % W;
+      if (TR) {
+        dst[v][u] = r[q].x;
+        dst[v + 1][u] = r[q].y;
+      } else {
+        dst[u][v] = r[q].x;
+        dst[u][v + 1] = r[q].y;
+      }
+    }
+  }
+};
+
+// acc[a][b] = sum_k P[ti + 16 a][k] Q[tj + 16 b][k] over k < 64, for ti = tid / 16,
+// tj = tid % 16 (a 64 x 64 product of two row-major LDS blocks, 4 x 4 per thread).
+__device__ __forceinline__ void mm_rows64(double (&acc)[4][4], const double (*P)[kLdp],
+                                          const double (*Q)[kLdp], int tid) {
+  const int ti = tid >> 4, tj = tid & 15;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+#pragma unroll 4
+  for (int k = 0; k < kNB; ++k) {
+    double p[4], q[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) p[a] = P[ti + 16 * a][k];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) q[b] = Q[tj + 16 * b][k];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] += p[a] * q[b];
+  }
+}
+
+// L_ik = A_ik Linv_kk^T for block rows i > kb: (A_ik Linv^T)[u][v] = sum_k A_ik[u][k] Linv[v][k].
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double* Linv, int ld,
                                                          int kb, int nb) {
-  __shared__ double x[kNB][kNB + 1];
-  __shared__ double li[kNB][kNB + 1];
+  __shared__ double x[kNB][kLdp];
+  __shared__ double li[kNB][kLdp];
   const int head = blockIdx.y, ib = kb + 1 + blockIdx.x, tid = threadIdx.x;
   double* Ai = A + (size_t)head * ld * ld + (size_t)ib * kNB * ld + kb * kNB;
-  const double* Lh = Linv + ((size_t)head * nb + kb) * kNB * kNB;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    x[e / kNB][e % kNB] = Ai[(size_t)(e / kNB) * ld + e % kNB];
-    li[e / kNB][e % kNB] = Lh[e];
-  }
+  BlockRegs<kNB> ra, rl;
+  ra.load(Ai, ld, tid);
+  rl.load(Linv + ((size_t)head * nb + kb) * kNB * kNB, kNB, tid);
+  ra.store<false>(x, tid);
+  rl.store<false>(li, tid);
   __syncthreads();
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    double v = 0.0;
-    for (int k2 = 0; k2 <= j; ++k2) v += x[i][k2] * li[j][k2];
-    Ai[(size_t)i * ld + j] = v;
-  }
+  double acc[4][4];
+  mm_rows64(acc, x, li, tid);
+  const int ti = tid >> 4, tj = tid & 15;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Ai[(size_t)(ti + 16 * a) * ld + tj + 16 * b] = acc[a][b];
 }
 
 // A_ij -= L_ik L_jk^T for kb < j <= i (lower block pairs enumerated by blockIdx.x).
 __global__ __launch_bounds__(256) void chol_update_kernel(double* A, int ld, int kb, int nb) {
-  __shared__ double li[kNB][kNB + 1];
-  __shared__ double lj[kNB][kNB + 1];
+  __shared__ double li[kNB][kLdp];
+  __shared__ double lj[kNB][kLdp];
   const int head = blockIdx.y, tid = threadIdx.x;
-  int a, b;
-  tri_index(blockIdx.x, a, b);
-  const int ib = kb + 1 + a, jb = kb + 1 + b;
+  int a0, b0;
+  tri_index(blockIdx.x, a0, b0);
+  const int ib = kb + 1 + a0, jb = kb + 1 + b0;
   double* Ah = A + (size_t)head * ld * ld;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    li[e / kNB][e % kNB] = Ah[(size_t)(ib * kNB + e / kNB) * ld + kb * kNB + e % kNB];
-    lj[e / kNB][e % kNB] = Ah[(size_t)(jb * kNB + e / kNB) * ld + kb * kNB + e % kNB];
-  }
+  double* Aij = Ah + (size_t)ib * kNB * ld + jb * kNB;
+  BlockRegs<kNB> ri, rj;
+  ri.load(Ah + (size_t)ib * kNB * ld + kb * kNB, ld, tid);
+  rj.load(Ah + (size_t)jb * kNB * ld + kb * kNB, ld, tid);
+  const int ti = tid >> 4, tj = tid & 15;
+  double cur[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur[a][b] = Aij[(size_t)(ti + 16 * a) * ld + tj + 16 * b];
+  ri.store<false>(li, tid);
+  rj.store<false>(lj, tid);
   __syncthreads();
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    double v = 0.0;
-#pragma unroll 8
-    for (int k2 = 0; k2 < kNB; ++k2) v += li[i][k2] * lj[j][k2];
-    Ah[(size_t)(ib * kNB + i) * ld + jb * kNB + j] -= v;
+  double acc[4][4];
+  mm_rows64(acc, li, lj, tid);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Aij[(size_t)(ti + 16 * a) * ld + tj + 16 * b] = cur[a][b] - acc[a][b];
+}
+
+// out[r][c] = sum_k M[r][k] X[k][c] for a 64 x 32 slice: rows tr, tr + 32 (tr = tid / 8),
+// columns tc + 8 b (tc = tid % 8).
+__device__ __forceinline__ void mm_slice(double (&acc)[2][4], const double (*M)[kLdp],
+                                         const double (*X)[33], int tid) {
+  const int tr = tid >> 3, tc = tid & 7;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+#pragma unroll 4
+  for (int k = 0; k < kNB; ++k) {
+    const double m0 = M[tr][k], m1 = M[tr + 32][k];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const double xv = X[k][tc + 8 * b];
+      acc[0][b] += m0 * xv;
+      acc[1][b] += m1 * xv;
+    }
   }
 }
 
@@ -880,51 +970,58 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* A, int ld, int
 // (head, 32-column slice of R).
 __global__ __launch_bounds__(256) void trsm_diag_kernel(double* R, const double* Linv, int ld,
                                                         int D, int kb, int nb, int trans) {
-  __shared__ double li[kNB][kNB + 1];
+  __shared__ double m[kNB][kLdp];
   __shared__ double x[kNB][33];
   const int head = blockIdx.y, c0 = blockIdx.x * 32, tid = threadIdx.x;
-  const double* Lh = Linv + ((size_t)head * nb + kb) * kNB * kNB;
   double* Rh = R + ((size_t)head * ld + (size_t)kb * kNB) * D + c0;
-  for (int e = tid; e < kNB * kNB; e += 256) li[e / kNB][e % kNB] = Lh[e];
-  for (int e = tid; e < kNB * 32; e += 256) x[e / 32][e % 32] = Rh[(size_t)(e / 32) * D + e % 32];
+  BlockRegs<kNB> rm;
+  BlockRegs<32> rx;
+  rm.load(Linv + ((size_t)head * nb + kb) * kNB * kNB, kNB, tid);
+  rx.load(Rh, D, tid);
+  if (trans) rm.store<true>(m, tid);
+  else rm.store<false>(m, tid);
+  rx.store<false>(x, tid);
   __syncthreads();
-  for (int e = tid; e < kNB * 32; e += 256) {
-    const int i = e / 32, c = e % 32;
-    double v = 0.0;
-    if (!trans)
-      for (int k2 = 0; k2 <= i; ++k2) v += li[i][k2] * x[k2][c];
-    else
-      for (int k2 = i; k2 < kNB; ++k2) v += li[k2][i] * x[k2][c];
-    Rh[(size_t)i * D + c] = v;
-  }
+  double acc[2][4];
+  mm_slice(acc, m, x, tid);
+  const int tr = tid >> 3, tc = tid & 7;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Rh[(size_t)(tr + 32 * a) * D + tc + 8 * b] = acc[a][b];
 }
 
 // forward: R_i -= L_{i,kb} R_kb for i > kb;  backward: R_i -= L_{kb,i}^T R_kb for i < kb.
 __global__ __launch_bounds__(256) void trsm_update_kernel(double* R, const double* A, int ld,
                                                           int D, int kb, int trans) {
-  __shared__ double l[kNB][kNB + 1];
+  __shared__ double m[kNB][kLdp];
   __shared__ double x[kNB][33];
   const int head = blockIdx.z, c0 = blockIdx.y * 32, tid = threadIdx.x;
   const int ib = trans ? blockIdx.x : kb + 1 + blockIdx.x;
   const double* Ah = A + (size_t)head * ld * ld;
-  double* Rh = R + (size_t)head * ld * D;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    l[i][j] = trans ? Ah[(size_t)(kb * kNB + i) * ld + ib * kNB + j]
-                    : Ah[(size_t)(ib * kNB + i) * ld + kb * kNB + j];
-  }
-  for (int e = tid; e < kNB * 32; e += 256)
-    x[e / 32][e % 32] = Rh[(size_t)(kb * kNB + e / 32) * D + c0 + e % 32];
+  double* Rh = R + (size_t)head * ld * D + c0;
+  BlockRegs<kNB> rm;
+  BlockRegs<32> rx;
+  if (trans) rm.load(Ah + (size_t)kb * kNB * ld + ib * kNB, ld, tid);
+  else rm.load(Ah + (size_t)ib * kNB * ld + kb * kNB, ld, tid);
+  rx.load(Rh + (size_t)kb * kNB * D, D, tid);
+  const int tr = tid >> 3, tc = tid & 7;
+  double* Ri = Rh + (size_t)ib * kNB * D;
+  double cur[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur[a][b] = Ri[(size_t)(tr + 32 * a) * D + tc + 8 * b];
+  if (trans) rm.store<true>(m, tid);
+  else rm.store<false>(m, tid);
+  rx.store<false>(x, tid);
   __syncthreads();
-  for (int e = tid; e < kNB * 32; e += 256) {
-    const int i = e / 32, c = e % 32;
-    double v = 0.0;
-    if (!trans)
-      for (int k2 = 0; k2 < kNB; ++k2) v += l[i][k2] * x[k2][c];
-    else
-      for (int k2 = 0; k2 < kNB; ++k2) v += l[k2][i] * x[k2][c];
-    Rh[(size_t)(ib * kNB + i) * D + c0 + c] -= v;
-  }
+  double acc[2][4];
+  mm_slice(acc, m, x, tid);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Ri[(size_t)(tr + 32 * a) * D + tc + 8 * b] = cur[a][b] - acc[a][b];
 }
 
 __global__ __launch_bounds__(256) void store_cv_kernel(const double* R, float* Cv, int t, int ld,
