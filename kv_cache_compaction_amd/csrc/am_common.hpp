@@ -83,4 +83,9 @@ __device__ __forceinline__ constexpr int kperm(int r) {
 
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Maximum of finite or infinite floats as v_maximum(3)_f32: unlike fmaxf, it needs no
+// quieting of its operands, which would cost one extra instruction per operand.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 }  // namespace amc

@@ -19,11 +19,11 @@
 // the end. Scores are kept in the log2 domain (x = s * scale * log2 e).
 //
 // Column-score pass (one workgroup = WAVES waves x 32 keys): K fragments stay in
-// registers, query tiles stream through LDS with their (m, log2 l) row statistics, and
-// p = 2^((x - m) - log2 l) reproduces the flash pass's normalisation bit for bit (same
-// MFMA operands and order, same row statistics). Each lane accumulates 16 queries of its
-// key in fp32 and folds the partial into fp64 once per 32-query block; the two lane
-// halves are combined at the end. No atomics: every key is owned by one lane.
+// registers, query tiles stream through LDS with one shift per query, u = m + log2 l from
+// the flash pass's row statistics, and p = 2^(x - u) with the same MFMA operands and order
+// as the flash pass. Each lane accumulates 16 queries of its key in fp32 and folds the
+// partial into fp64 once per 32-query block; the two lane halves are combined at the end.
+// No atomics: every key is owned by one lane.
 #include "am_common.hpp"
 #include "am_internal.hpp"
 
@@ -246,10 +246,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
         }
         x[kb * 16 + j] = v;
       }
-    float tmax = fmaxf(x[0], x[1]);
+    float tmax = x[0];
 #pragma unroll
-    for (int i = 2; i < NKB * 16; i += 2) tmax = fmaxf(tmax, fmaxf(x[i], x[i + 1]));
-    tmax = fmaxf(tmax, shfl_xor32(tmax));
+    for (int i = 1; i < NKB * 16; i += 2) tmax = vmax3(tmax, x[i], i + 1 < NKB * 16 ? x[i + 1] : x[i]);
+    tmax = vmax(tmax, shfl_xor32(tmax));
     if (!BIASED) tmax *= p.c2;
     const bool need = tmax > m + kLazyTau;
     if (__ballot(need)) {
@@ -348,8 +348,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 // Column-score pass.
 // ------------------------------------------------------------------------------------
 // MODE: 0 = RMS (sum of p^2), 1 = MEAN (sum of p), 2 = MAX (max of p). Only the requested
-// statistic is computed: RMS exponentiates 2 ((x - m) - log2 l) directly (p^2, the doubling
-// is exact) and MAX keeps the max of the exponent and exponentiates once at the end.
+// statistic is computed: with the row shift u = m + log2 l, RMS exponentiates 2 (x - u)
+// directly (p^2; the doubling is exact) and MAX keeps the max of the exponent and
+// exponentiates once at the end.
 template <typename T, int D> constexpr int colscore_kb() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
 
 template <typename T, int D, int WAVES, bool CAUSAL, int MODE>
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   const float f = MODE == 0 ? 2.f : 1.f;   // exponent factor
 
   __shared__ __align__(16) T qs[2][kBQ * QP];
-  __shared__ float2 rs[2][kBQ];
+  __shared__ __align__(16) float rs[2][kBQ];   // f (m + log2 l) per query
 
   const int b = blockIdx.x;
   const int head = b % heads;
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   const int ntiles = (n - qbeg + kBQ - 1) / kBQ;
 
   u32x4 qreg[QPT];
-  float2 rreg = make_float2(0.f, 0.f);
+  float rreg = 0.f;
   auto gload = [&](int it) {
     const int qt0 = qbeg + it * kBQ;
 #pragma unroll
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     }
     if (tid < kBQ) {
       const float2 st = RSh[min(qt0 + tid, n - 1)];
-      rreg = make_float2(f * st.x, f * st.y);
+      rreg = f * (st.x + st.y);
     }
   };
   auto sstore = [&](int buf) {
@@ -450,27 +451,30 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mma16(s[kb], a, bk[kb][kc]);
       }
-      float st_m[16], st_l[16];
+      // rows crow(4a .. 4a + 3, hh) are consecutive: one 16-byte read per four elements
+      float sh[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float2 st = rs[buf][qb * 32 + crow(j, hh)];
-        st_m[j] = st.x;
-        st_l[j] = st.y;
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 v = *(const float4*)&rs[buf][qb * 32 + a4 * 8 + hh * 4];
+        sh[4 * a4 + 0] = v.x;
+        sh[4 * a4 + 1] = v.y;
+        sh[4 * a4 + 2] = v.z;
+        sh[4 * a4 + 3] = v.w;
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float part = MODE == 2 ? -INFINITY : 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float e = __builtin_fmaf(s[kb][j], fc2, -st_m[j]) - st_l[j];
+          float e = __builtin_fmaf(s[kb][j], fc2, -sh[j]);
           if (MASK) {
             const int q = qt0 + qb * 32 + crow(j, hh);
             e = (q < n && (!CAUSAL || key[kb] <= q / group)) ? e : -INFINITY;
           }
-          if (MODE == 2) part = fmaxf(part, e);
+          if (MODE == 2) part = vmax(part, e);
           else part += ex2(e);
         }
-        if (MODE == 2) amx[kb] = fmaxf(amx[kb], part);
+        if (MODE == 2) amx[kb] = vmax(amx[kb], part);
         else acc[kb] += (double)part;
       }
     }
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   for (int kb = 0; kb < KB; ++kb) {
     float out;
     if (MODE == 2) {
-      const float mx = fmaxf(amx[kb], shfl_xor32(amx[kb]));
+      const float mx = vmax(amx[kb], shfl_xor32(amx[kb]));
       out = ex2(mx);
     } else {
       const double tot = acc[kb] + __shfl_xor(acc[kb], 32, 64);
