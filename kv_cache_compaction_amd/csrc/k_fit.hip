@@ -113,9 +113,10 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
   v8 bck[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) bck[kc] = *(const v8*)(Ch + (size_t)kr * D + kc * 16 + hh * 8);
-  // first query that sees this key under the causal mask; keys past t get a -inf bias
+  // first query that sees this key under the causal mask. Keys past t (padding of the last
+  // tile) repeat key t - 1: their Gram rows and columns are finite and never read.
   const int kq0 = p.causal ? p.keypos[(size_t)head * t + kr] * p.group : 0;
-  const float kb2 = !kval ? -INFINITY : (VALUE ? p.bias[(size_t)head * t + kr] * kLog2e : 0.f);
+  const float kb2 = VALUE ? p.bias[(size_t)head * t + kr] * kLog2e : 0.f;
   int kq0max = kval ? kq0 : 0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) kq0max = max(kq0max, __shfl_xor(kq0max, o, 64));
@@ -243,9 +244,11 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
     // interleaved so their MFMA chains overlap. MASK (wave-uniform) is needed only where
     // some query of the step cannot see a key of this wave's block, or past the chunk end.
     const int q0 = qstart + st * GQ;
+    // MASK: 0 none, 1 causal (first visible query kq0 of this lane's key), 2 causal and the
+    // chunk end. Element j of a lane holds query qbase + o_j with o_j = j (j < 8) or j + 8.
     auto scores = [&](auto nh_tag, int qhb, auto mask_tag) {
       constexpr int NH = decltype(nh_tag)::value;
-      constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr int MASK = decltype(mask_tag)::value;
       f32x16 sacc[NH];
 #pragma unroll
       for (int u = 0; u < NH; ++u)
@@ -266,14 +269,17 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
         const float shv[16] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w,
                                sc.x, sc.y, sc.z, sc.w, sd.x, sd.y, sd.z, sd.w};
         float mv[16];
+        const int qbase = q0 + qh * 32 + 8 * hh;
+        const int lo = kq0 - qbase, hi = qb - qbase;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float v = ex2(sacc[u][j] * p.c2 + kb2 - shv[j]);
-          if (MASK) {
-            const int q = q0 + qh * 32 + (j < 8 ? 8 * hh + j : 16 + 8 * hh + (j - 8));
-            v = (q < qb && q >= kq0 && shv[j] > -INFINITY) ? v : 0.f;
-          }
-          mv[j] = v;
+          // masked entries get exponent -inf (so pairs of fp32 values stay packable)
+          float x = VALUE ? __builtin_fmaf(sacc[u][j], p.c2, kb2) - shv[j]
+                          : __builtin_fmaf(sacc[u][j], p.c2, -shv[j]);
+          const int o = j < 8 ? j : j + 8;
+          if (MASK == 1) x = o >= lo ? x : -INFINITY;
+          if (MASK == 2) x = (o >= lo && o < hi) ? x : -INFINITY;
+          mv[j] = ex2(x);
         }
         if (!VALUE && diag) {
           const float4* t4 = (const float4*)&tgs[buf][qh * 32 + 8 * hh];
@@ -287,21 +293,24 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
         mb[buf][kbid][qh][1][lane] = AM_PACK8(bf16, mv, 8);
       }
     };
-    const bool mask = (q0 < kq0max) || (q0 + GQ > qb);
+    const int mask = (q0 + GQ > qb) ? 2 : (q0 < kq0max ? 1 : 0);
+    using M0 = std::integral_constant<int, 0>;
+    using M1 = std::integral_constant<int, 1>;
+    using M2 = std::integral_constant<int, 2>;
+    auto scores_m = [&](auto nh_tag, int qhb) {
+      if (mask == 0) scores(nh_tag, qhb, M0{});
+      else if (mask == 1) scores(nh_tag, qhb, M1{});
+      else scores(nh_tag, qhb, M2{});
+    };
     if (!diag) {
       if constexpr (VALUE) {   // one query half at a time keeps the value variant in registers
 #pragma unroll
-        for (int qh = 0; qh < QH; ++qh) {
-          if (mask) scores(std::integral_constant<int, 1>{}, qh, std::true_type{});
-          else scores(std::integral_constant<int, 1>{}, qh, std::false_type{});
-        }
+        for (int qh = 0; qh < QH; ++qh) scores_m(std::integral_constant<int, 1>{}, qh);
       } else {
-        if (mask) scores(std::integral_constant<int, QH>{}, 0, std::true_type{});
-        else scores(std::integral_constant<int, QH>{}, 0, std::false_type{});
+        scores_m(std::integral_constant<int, QH>{}, 0);
       }
     } else if (qh0 < qh1) {
-      if (mask) scores(std::integral_constant<int, 1>{}, qh0, std::true_type{});
-      else scores(std::integral_constant<int, 1>{}, qh0, std::false_type{});
+      scores_m(std::integral_constant<int, 1>{}, qh0);
     }
     if (diag) ystore(buf);   // read by the Gram part of the next step
     // next step's query tile
@@ -384,6 +393,12 @@ __global__ __launch_bounds__(256) void vec_reduce_kernel(const float* __restrict
   out[(size_t)head * ld * width + e] = (OT)acc;
 }
 
+// A query that sees no selected key with w > 0 has compacted log-normalizer -inf and a zero
+// row of A. Its shift is made a huge finite number instead, so that every design entry
+// 2^(x + bias - shift) of the row underflows to 0 with no per-entry test (x + bias is at
+// most a few hundred, or -inf for w = 0).
+__device__ __forceinline__ float value_shift(float u) { return u == -INFINITY ? 1e30f : u; }
+
 // Per-query shift (log2 domain) and mass right-hand side.
 //   mode 0: shift = lse * log2 e (relative mass design)
 //   mode 1: shift = max_i lse_i * log2 e, target = 2^(lse_i log2 e - shift) (absolute)
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(256) void shift_rows_kernel(const float* __restrict
     shift2[o] = lse[o] * kLog2e;
   } else {
     const float2 st = rowstat[o];
-    shift2[o] = st.x + st.y;
+    shift2[o] = value_shift(st.x + st.y);
   }
 }
 
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(256) void shift_kernel(const float* __restrict__ ls
       target[o] = ex2(lse[o] * kLog2e - c);
     } else {
       const float2 st = rowstat[o];
-      shift2[o] = st.x + st.y;
+      shift2[o] = value_shift(st.x + st.y);
     }
   }
 }
