@@ -71,6 +71,34 @@ struct FitArgs {
   void* ws; size_t ws_bytes;
   hipStream_t stream;
 };
+// Gram builds for t > kSyrkMinT: the bf16 design X (key rows, then Y^T rows for the value
+// fit) is stored once and its Gram formed by a tiled MFMA product with split-K partials.
+constexpr int kSyrkMinT = 256;
+struct SyrkBuffers {
+  void* X;        // [h, xrows, npad] bf16
+  float* part;    // [h, chunks, tiles, 256, 256] Gram partials
+  float* hpart;   // mass: [h, tpad, npad / 128] partials of M^T b
+};
+bool syrk_path(int t);
+// carve the buffers at base + off (base null: sizing only); off advances past them
+SyrkBuffers syrk_carve(char* base, size_t& off, int64_t heads, int64_t n, int64_t t, int64_t d,
+                       bool value);
+struct SyrkGramArgs {
+  const void* Q; const void* Ck; const int32_t* keypos;
+  const float* bias;     // value: beta of the selected keys
+  const float* shift2;   // per query, log2 domain
+  const float* target;   // mass: right-hand side (null = 1)
+  const float* Y;        // value: targets [h, n, d]
+  SyrkBuffers buf;
+  float* Gf; float* hv;   // mass outputs: G [h, t, t], M^T b [h, t]
+  double* Gd; double* R;  // value outputs: A^T A + lambda I [h, ld, ld], A^T Y [h, ld, d]
+  int heads, n, t, d, group, ld;
+  bool causal, bf16, value;
+  float c2, lambda;
+  hipStream_t stream;
+};
+hipError_t launch_syrk_gram(const SyrkGramArgs& a);
+
 hipError_t launch_fit_beta(const FitArgs& a);
 hipError_t launch_fit_values(const FitArgs& a);
 size_t fit_beta_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d);

@@ -1152,6 +1152,7 @@ struct BetaPlan {
   float* shift2; float* target; float* Gpart; float* hpart; float* G; float* hv;
   float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float* TK; float* hsmax;
   int* iters; int* fin; float2* rowstat_cmp; double2* part; int32_t* status;
+  SyrkBuffers sy;
   size_t bytes;
 };
 
@@ -1167,8 +1168,14 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
   p.part = c.take<double2>(heads * kResBlk);
   p.shift2 = c.take<float>(heads * n);
   p.target = c.take<float>(heads * n);
-  p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
-  p.hpart = c.take<float>((size_t)heads * nch * tpad);
+  if (syrk_path((int)t)) {
+    p.Gpart = p.hpart = nullptr;
+    p.sy = syrk_carve(base, c.off, heads, n, t, d, false);
+  } else {
+    p.sy = SyrkBuffers{nullptr, nullptr, nullptr};
+    p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
+    p.hpart = c.take<float>((size_t)heads * nch * tpad);
+  }
   p.G = c.take<float>((size_t)heads * t * t);
   p.hv = c.take<float>(heads * t);
   p.dinv = c.take<float>(heads * t);
@@ -1189,6 +1196,7 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
 struct ValuePlan {
   float2* rowstat_cmp; double2* part; float* shift2; float* Gpart; float* Rpart; double* A;
   double* R; double* Linv; void* Vt; float2* rowres; int32_t* status;
+  SyrkBuffers sy;
   size_t bytes;
 };
 
@@ -1204,8 +1212,14 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   p.rowstat_cmp = c.take<float2>(heads * n);
   p.part = c.take<double2>(heads * kResBlk);
   p.shift2 = c.take<float>(heads * n);
-  p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
-  p.Rpart = c.take<float>((size_t)heads * nch * tpad * d);
+  if (syrk_path((int)t)) {
+    p.Gpart = p.Rpart = nullptr;
+    p.sy = syrk_carve(base, c.off, heads, n, t, d, true);
+  } else {
+    p.sy = SyrkBuffers{nullptr, nullptr, nullptr};
+    p.Gpart = c.take<float>((size_t)heads * nch * ntri * kGT * kGT);
+    p.Rpart = c.take<float>((size_t)heads * nch * tpad * d);
+  }
   p.A = c.take<double>((size_t)heads * ld * ld);
   p.R = c.take<double>((size_t)heads * ld * d);
   p.Linv = c.take<double>((size_t)heads * (ld / kNB) * kNB * kNB);
@@ -1254,17 +1268,29 @@ hipError_t launch_fit_beta(const FitArgs& a) {
   else
     hipLaunchKernelGGL(shift_rows_kernel, dim3(cdiv(n, 256), H), dim3(256), 0, st, a.lse,
                        (const float2*)nullptr, pl.shift2, n, 0);
-  GramParams gp;
-  gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = nullptr;
-  gp.shift2 = pl.shift2; gp.target = a.absolute ? pl.target : nullptr; gp.Y = nullptr;
-  gp.Gpart = pl.Gpart; gp.Vpart = pl.hpart;
-  gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
-  gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
-  launch_gram_any(gp, H, d, a.bf16, false, st);
-  hipLaunchKernelGGL((gram_reduce_kernel<float>), dim3(cdiv((long long)t * t, 256), H), dim3(256),
-                     0, st, pl.Gpart, pl.G, t, t, ntri, nch, 0.f);
-  hipLaunchKernelGGL((vec_reduce_kernel<float>), dim3(cdiv(t, 256), H), dim3(256), 0, st,
-                     pl.hpart, pl.hv, t, tpad, t, 1, nch);
+  if (syrk_path(t)) {
+    SyrkGramArgs sa;
+    sa.Q = a.Q; sa.Ck = a.Ck; sa.keypos = a.idx; sa.bias = nullptr; sa.shift2 = pl.shift2;
+    sa.target = a.absolute ? pl.target : nullptr; sa.Y = nullptr; sa.buf = pl.sy;
+    sa.Gf = pl.G; sa.hv = pl.hv; sa.Gd = nullptr; sa.R = nullptr;
+    sa.heads = H; sa.n = n; sa.t = t; sa.d = d; sa.group = a.group; sa.ld = t;
+    sa.causal = a.causal; sa.bf16 = a.bf16; sa.value = false;
+    sa.c2 = a.scale * kLog2e; sa.lambda = 0.f; sa.stream = st;
+    const hipError_t e = launch_syrk_gram(sa);
+    if (e != hipSuccess) return e;
+  } else {
+    GramParams gp;
+    gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = nullptr;
+    gp.shift2 = pl.shift2; gp.target = a.absolute ? pl.target : nullptr; gp.Y = nullptr;
+    gp.Gpart = pl.Gpart; gp.Vpart = pl.hpart;
+    gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
+    gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
+    launch_gram_any(gp, H, d, a.bf16, false, st);
+    hipLaunchKernelGGL((gram_reduce_kernel<float>), dim3(cdiv((long long)t * t, 256), H),
+                       dim3(256), 0, st, pl.Gpart, pl.G, t, t, ntri, nch, 0.f);
+    hipLaunchKernelGGL((vec_reduce_kernel<float>), dim3(cdiv(t, 256), H), dim3(256), 0, st,
+                       pl.hpart, pl.hv, t, tpad, t, 1, nch);
+  }
   // NNLS
   NnlsState s;
   s.G = pl.G; s.hv = pl.hv; s.dinv = pl.dinv; s.hs = pl.hs; s.V = pl.V; s.X = pl.X;
@@ -1326,17 +1352,29 @@ hipError_t launch_fit_values(const FitArgs& a) {
   }
   hipLaunchKernelGGL(shift_rows_kernel, dim3(cdiv(n, 256), H), dim3(256), 0, st,
                      (const float*)nullptr, (const float2*)pl.rowstat_cmp, pl.shift2, n, 2);
-  GramParams gp;
-  gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = a.beta_in;
-  gp.shift2 = pl.shift2; gp.target = nullptr; gp.Y = a.O;
-  gp.Gpart = pl.Gpart; gp.Vpart = pl.Rpart;
-  gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
-  gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
-  launch_gram_any(gp, H, d, a.bf16, true, st);
-  hipLaunchKernelGGL((gram_reduce_kernel<double>), dim3(cdiv((long long)ld * ld, 256), H),
-                     dim3(256), 0, st, pl.Gpart, pl.A, t, ld, ntri, nch, a.lambda);
-  hipLaunchKernelGGL((vec_reduce_kernel<double>), dim3(cdiv((long long)ld * d, 256), H),
-                     dim3(256), 0, st, pl.Rpart, pl.R, t, tpad, ld, d, nch);
+  if (syrk_path(t)) {
+    SyrkGramArgs sa;
+    sa.Q = a.Q; sa.Ck = a.Ck; sa.keypos = a.idx; sa.bias = a.beta_in; sa.shift2 = pl.shift2;
+    sa.target = nullptr; sa.Y = a.O; sa.buf = pl.sy;
+    sa.Gf = nullptr; sa.hv = nullptr; sa.Gd = pl.A; sa.R = pl.R;
+    sa.heads = H; sa.n = n; sa.t = t; sa.d = d; sa.group = a.group; sa.ld = ld;
+    sa.causal = a.causal; sa.bf16 = a.bf16; sa.value = true;
+    sa.c2 = a.scale * kLog2e; sa.lambda = a.lambda; sa.stream = st;
+    e = launch_syrk_gram(sa);
+    if (e != hipSuccess) return e;
+  } else {
+    GramParams gp;
+    gp.Q = a.Q; gp.Ck = a.Ck; gp.keypos = a.idx; gp.bias = a.beta_in;
+    gp.shift2 = pl.shift2; gp.target = nullptr; gp.Y = a.O;
+    gp.Gpart = pl.Gpart; gp.Vpart = pl.Rpart;
+    gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
+    gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
+    launch_gram_any(gp, H, d, a.bf16, true, st);
+    hipLaunchKernelGGL((gram_reduce_kernel<double>), dim3(cdiv((long long)ld * ld, 256), H),
+                       dim3(256), 0, st, pl.Gpart, pl.A, t, ld, ntri, nch, a.lambda);
+    hipLaunchKernelGGL((vec_reduce_kernel<double>), dim3(cdiv((long long)ld * d, 256), H),
+                       dim3(256), 0, st, pl.Rpart, pl.R, t, tpad, ld, d, nch);
+  }
   // Cholesky
   for (int kb = 0; kb < nb; ++kb) {
     hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv, ld, kb, nb,

@@ -27,6 +27,10 @@ CASES = [
     (Workload("ragged_t", 2, 128, 1000, 1000, 200, "bf16", False, 1), [0, 1]),
     (Workload("ragged_causal_g3", 2, 64, 333, 999, 45, "bf16", True, 3), [0, 1]),
     (Workload("t1", 1, 128, 300, 300, 1, "bf16", False, 1), [0]),
+    # t > 256: stored design + tiled Gram product (ragged t and n, causal GQA, fp32 inputs)
+    (Workload("big_t_causal_g4", 2, 128, 1536, 6144, 384, "bf16", True, 4), [0, 1]),
+    (Workload("big_t_ragged_d64", 1, 64, 1500, 1500, 300, "bf16", False, 1), [0]),
+    (Workload("big_t_causal_g3_f32", 1, 64, 800, 2400, 290, "f32", True, 3), [0]),
 ]
 
 
