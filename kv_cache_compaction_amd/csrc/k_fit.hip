@@ -466,6 +466,8 @@ struct NnlsState {
   float* hsmax;     // [h]
   int* iters;       // [h]
   int* fin;         // [h] ring slot of the converged iterate, -1 while running
+  float2* init;     // [h, nblk] (max |hs|, non-finite flag) partials (multi-workgroup solver)
+  int* bar;         // [h] barrier counters of the multi-workgroup solver (zero before a launch)
   int t, nblk;
   float lo, hi, tol;
 };
@@ -777,6 +779,227 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
     if (status)
       status[head] = (gm > thr ? AM_HEAD_NNLS_BIT : 0) |
                      ((bad > 0.f || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0);
+  }
+}
+
+// Multi-workgroup solver for t > kNnlsCoopMinT: the same iteration, with the rows of each
+// head split over P workgroups and a barrier among those P between steps. The grid is
+// launched cooperatively, which guarantees that every workgroup is resident (the barrier
+// waits on the others). A workgroup keeps its rows of G in LDS when they fit, else reads
+// them from L2; the iterate vectors go through global memory. All workgroups of a head
+// reduce the head's per-workgroup partials in the same fixed order, so they take the same
+// decisions (momentum, convergence, exit) and pass the same number of barriers; heads are
+// independent and stop on their own.
+constexpr int kNnlsCoopMinT = 256;            // smaller systems: one workgroup per head
+constexpr size_t kNnlsCoopLds = 144 * 1024;   // dynamic LDS for G rows + the vector
+constexpr int kNnlsSpin = 1 << 22;            // polls before a barrier wait gives up
+
+// Loads of data that decide control flow, at device scope.
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Barrier among the workgroups of one head: the m-th completes when the head's counter
+// reaches m * P. Every wave first waits until its own stores have reached L2 (vmcnt 0);
+// then one thread per workgroup adds to the counter with release semantics (the L2
+// write-back makes those stores visible device-wide), polls it with device-scope loads and
+// finishes with one acquire fence, which drops stale cache lines before any thread reads
+// what the others wrote. A wait longer than kNnlsSpin polls
+// (seconds) marks the workgroup as timed out, after which it waits no more and stops.
+__device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_out) {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0) only
+  __syncthreads();
+  if (threadIdx.x == 0 && !*timed_out) {
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kNnlsSpin) {
+        *timed_out = 1;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int max_iter, int g_lds,
+                                                        float* w_out, float* beta,
+                                                        int32_t* status) {
+  extern __shared__ float smem[];
+  __shared__ float red[4];
+  __shared__ float2 pst[256];   // staged partials of the head's workgroups (P <= 256)
+  __shared__ int timed_out;
+  const int H = gridDim.x / P, head = blockIdx.x % H, part = blockIdx.x / H, t = s.t;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rb = (t + P - 1) / P, r0 = min(t, part * rb), r1 = min(t, r0 + rb);
+  if (tid == 0) timed_out = 0;
+  float* xs = smem;
+  float* Gs = smem + t;
+  const float* G = s.G + (size_t)head * t * t;
+  if (g_lds)
+    for (int e = tid; e < (r1 - r0) * t; e += 256) Gs[e] = G[(size_t)r0 * t + e];
+  auto grow = [&](int i) { return g_lds ? Gs + (size_t)(i - r0) * t : G + (size_t)i * t; };
+  float* dinv = s.dinv + (size_t)head * t;
+  float* hs = s.hs + (size_t)head * t;
+  const size_t ps = (size_t)s.nblk;   // partial slots per head and parity
+  int* bar = s.bar + head;
+  int nbar = 0;
+  auto barrier = [&]() { head_barrier(bar, ++nbar * P, &timed_out); };
+  // the head's P partials (float2) staged once, one load per thread
+  auto stage = [&](const float2* src) {
+    for (int b = tid; b < P; b += 256) {
+      const float* q = (const float*)(src + b);
+      pst[b] = make_float2(ld_dev(q), ld_dev(q + 1));
+    }
+    __syncthreads();
+  };
+
+  // prep: own rows
+  float hm = 0.f, nb = 0.f;
+  for (int j = r0 + tid; j < r1; j += 256) {
+    const float g = G[(size_t)j * t + j];
+    const float h = s.hv[(size_t)head * t + j];
+    if (!isfinite(g) || !isfinite(h)) nb = 1.f;
+    const float di = g > 0.f ? rsqrtf(g) : 0.f;
+    dinv[j] = di;
+    const float hsj = h * di;
+    hs[j] = hsj;
+    hm = fmaxf(hm, fabsf(hsj));
+    const float v0 = di > 0.f ? s.lo / di : 0.f;
+    s.V[((size_t)head * 3 + 0) * t + j] = v0;
+    s.V[((size_t)head * 3 + 2) * t + j] = v0;
+    s.X[((size_t)head * 2 + 0) * t + j] = 1.f;
+  }
+  hm = block_max(hm, red);
+  nb = block_max(nb, red);
+  if (tid == 0) {
+    if (part == 0 && status) status[head] = 0;   // parts OR their flags in at the end
+    s.init[(size_t)head * ps + part] = make_float2(hm, nb);
+    s.PN[((size_t)head * 2 + 0) * ps + part] = part == 0 ? (float)t : 0.f;
+    s.P[((size_t)head * 2 + 0) * ps + part] = make_float2(0.f, INFINITY);
+  }
+  barrier();
+  stage(s.init + (size_t)head * ps);
+  float hsmax = 0.f;
+  bool bad = false;
+  for (int b = 0; b < P; ++b) {
+    hsmax = fmaxf(hsmax, pst[b].x);
+    bad |= pst[b].y > 0.f;
+  }
+  __syncthreads();
+  const float thr = s.tol * fmaxf(hsmax, 1e-30f);
+
+  // power iteration for L = lambda_max(D^-1 G D^-1)
+  float* pnl = (float*)pst;
+  auto head_norm = [&](int parity) {
+    const float* pn = s.PN + ((size_t)head * 2 + parity) * ps;
+    for (int b = tid; b < P; b += 256) pnl[b] = ld_dev(pn + b);
+    __syncthreads();
+    float nrm = 0.f;
+    for (int b = 0; b < P; ++b) nrm += pnl[b];
+    __syncthreads();
+    return nrm;
+  };
+  for (int k = 0; k < kPow && !timed_out; ++k) {
+    const float nrm = head_norm(k & 1);
+    const float sc = nrm > 0.f ? rsqrtf(nrm) : 0.f;
+    const float* xin = s.X + ((size_t)head * 2 + (k & 1)) * t;
+    float* xout = s.X + ((size_t)head * 2 + ((k + 1) & 1)) * t;
+    for (int j = tid; j < t; j += 256) xs[j] = xin[j] * sc * dinv[j];
+    __syncthreads();
+    float part2 = 0.f;
+    for (int i = r0 + wave; i < r1; i += 4) {
+      const float* gr = grow(i);
+      float acc = 0.f;
+      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const float y = acc * dinv[i];
+      if (lane == 0) {
+        xout[i] = y;
+        part2 += y * y;
+      }
+    }
+    part2 = block_sum(part2, red);
+    if (tid == 0) s.PN[((size_t)head * 2 + ((k + 1) & 1)) * ps + part] = part2;
+    barrier();
+  }
+  const float L = 1.1f * sqrtf(head_norm(kPow & 1)) + 1e-30f;
+
+  // accelerated projected gradient; iterate v_k in ring slot k % 3
+  float tk = 1.f, gm = INFINITY;
+  int k = 0;
+  for (; k < max_iter && !timed_out; ++k) {
+    // this head's previous-step partials, reduced in a fixed order
+    stage(s.P + ((size_t)head * 2 + (k & 1)) * ps);
+    float dot = 0.f;
+    gm = 0.f;
+    for (int b = 0; b < P; ++b) {
+      dot += pst[b].x;
+      gm = fmaxf(gm, pst[b].y);
+    }
+    __syncthreads();
+    if (k > 0 && gm <= thr) break;   // the same decision in every workgroup of the head
+    const bool restart = dot > 0.f;
+    const float tn = restart ? 1.f : 0.5f * (1.f + sqrtf(1.f + 4.f * tk * tk));
+    const float mom = restart ? 0.f : (tk - 1.f) / tn;
+    const float* vprev = s.V + ((size_t)head * 3 + (k + 2) % 3) * t;
+    const float* vcur = s.V + ((size_t)head * 3 + k % 3) * t;
+    float* vnext = s.V + ((size_t)head * 3 + (k + 1) % 3) * t;
+    for (int j = tid; j < t; j += 256) xs[j] = (vcur[j] + mom * (vcur[j] - vprev[j])) * dinv[j];
+    __syncthreads();
+    float pdot = 0.f, pgm = 0.f;
+    for (int i = r0 + wave; i < r1; i += 4) {
+      const float* gr = grow(i);
+      float acc = 0.f;
+      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const float di = dinv[i];
+      const float y = vcur[i] + mom * (vcur[i] - vprev[i]);
+      const float g = acc * di - hs[i];
+      float vn = 0.f;
+      if (di > 0.f) {
+        const float lo = s.lo / di;
+        const float hi = isinf(s.hi) ? INFINITY : s.hi / di;
+        vn = fminf(fmaxf(y - g / L, lo), hi);
+      }
+      if (lane == 0) {
+        vnext[i] = vn;
+        pdot += (vn - vcur[i]) * (y - vn);
+        pgm = fmaxf(pgm, fabsf(y - vn) * L);
+      }
+    }
+    pdot = block_sum(pdot, red);
+    pgm = block_max(pgm, red);
+    if (tid == 0) s.P[((size_t)head * 2 + ((k + 1) & 1)) * ps + part] = make_float2(pdot, pgm);
+    tk = tn;
+    barrier();
+  }
+  if (k == max_iter && !timed_out) {   // the last step's norm was not examined yet
+    stage(s.P + ((size_t)head * 2 + (k & 1)) * ps);
+    gm = 0.f;
+    for (int b = 0; b < P; ++b) gm = fmaxf(gm, pst[b].y);
+  }
+  // the answer is v_k
+  const float* v = s.V + ((size_t)head * 3 + k % 3) * t;
+  float nbw = 0.f;
+  for (int j = r0 + tid; j < r1; j += 256) {
+    const float di = dinv[j];
+    float w = di > 0.f ? v[j] * di : s.lo;
+    w = fminf(fmaxf(w, s.lo), s.hi);
+    if (!isfinite(w)) nbw = 1.f;
+    if (w_out) w_out[(size_t)head * t + j] = w;
+    beta[(size_t)head * t + j] = w > 0.f ? logf(w) : -INFINITY;
+  }
+  nbw = block_max(nbw, red);
+  if (tid == 0 && part == 0) s.iters[head] = k;
+  if (tid == 0 && status) {
+    const int bits = ((timed_out || k == 0 || !(gm <= thr)) ? AM_HEAD_NNLS_BIT : 0) |
+                     ((bad || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0);
+    if (bits) atomicOr(&status[head], bits);
   }
 }
 
@@ -1151,7 +1374,7 @@ struct Carve {
 struct BetaPlan {
   float* shift2; float* target; float* Gpart; float* hpart; float* G; float* hv;
   float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float* TK; float* hsmax;
-  int* iters; int* fin; float2* rowstat_cmp; double2* part; int32_t* status;
+  int* iters; int* fin; float2* init; int* bar; float2* rowstat_cmp; double2* part; int32_t* status;
   SyrkBuffers sy;
   size_t bytes;
 };
@@ -1188,6 +1411,8 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
   p.hsmax = c.take<float>(heads);
   p.iters = c.take<int>(heads);
   p.fin = c.take<int>(heads);
+  p.init = c.take<float2>(heads * nblk);
+  p.bar = c.take<int>(heads);
   p.status = c.take<int32_t>(heads);
   p.bytes = c.off;
   return p;
@@ -1295,10 +1520,41 @@ hipError_t launch_fit_beta(const FitArgs& a) {
   NnlsState s;
   s.G = pl.G; s.hv = pl.hv; s.dinv = pl.dinv; s.hs = pl.hs; s.V = pl.V; s.X = pl.X;
   s.PN = pl.PN; s.P = pl.P; s.TK = pl.TK; s.hsmax = pl.hsmax; s.iters = pl.iters;
-  s.fin = pl.fin;
+  s.fin = pl.fin; s.init = pl.init; s.bar = pl.bar;
   s.t = t; s.nblk = (t + kRB - 1) / kRB;
   s.lo = a.w_lo; s.hi = a.w_hi; s.tol = a.tol;
-  if (t <= kNnlsSingle) {
+  bool done = false;
+  if (t > kNnlsCoopMinT) {
+    // cooperative solver: P workgroups per head, all co-resident (one per CU)
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        ncu >= 4 * H) {
+      // one workgroup per CU: the rows of G then mostly fit in LDS (G read from L2 every
+      // step costs more than the extra barrier traffic of more workgroups)
+      int P = ncu / H;
+      if (P > s.nblk) P = s.nblk;
+      if (P > 256) P = 256;   // the partials of a head are staged in one pass
+      const int rb = (t + P - 1) / P;
+      int g_lds = (size_t)(t + (size_t)rb * t) * sizeof(float) <= kNnlsCoopLds ? 1 : 0;
+      const size_t shmem = (size_t)(t + (g_lds ? (size_t)rb * t : 0)) * sizeof(float);
+      int max_iter = a.max_iter;
+      float* wout = a.w;
+      float* beta = a.beta;
+      int32_t* stp = status;
+      void* args[] = {&s, &P, &max_iter, &g_lds, &wout, &beta, &stp};
+      hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(H, 256)), dim3(256), 0, st, pl.bar, H);
+      (void)hipFuncSetAttribute((const void*)nnls_coop_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+      if (hipLaunchCooperativeKernel((const void*)nnls_coop_kernel, dim3(H * P), dim3(256), args,
+                                     (unsigned)shmem, st) == hipSuccess)
+        done = true;
+      else
+        (void)hipGetLastError();   // refused (e.g. not co-resident): use the kernels below
+    }
+  }
+  if (done) {
+  } else if (t <= kNnlsSingle) {
     hipLaunchKernelGGL(nnls_single_kernel, dim3(H), dim3(kNnlsSingle), 0, st, s, a.max_iter, a.w,
                        a.beta, status);
   } else {
