@@ -37,6 +37,8 @@ struct CmpAttnArgs {
   const void* Q; const void* Ck; const float* Cv; const float* bias; const int32_t* keypos;
   const float* Y;
   void* Vt;             // workspace [h, d, round_up(t, 64)] when Cv is set
+  int2* tstat;          // causal: workspace [h, ceil(t / 32)] for per-tile (min, max)
+                        // positions, or null (every tile then takes the masked path)
   float* lse; float2* rowstat; float* O; float2* rowres;
   int heads, n, t, d, group;
   bool causal, bf16;
@@ -45,6 +47,7 @@ struct CmpAttnArgs {
 };
 hipError_t launch_cmp_attention(const CmpAttnArgs& a);
 size_t cmp_vt_bytes(int64_t heads, int64_t t, int64_t d, int esize);
+size_t cmp_tstat_bytes(int64_t heads, int64_t t);
 
 struct SelectArgs {
   const float* score; const void* K; const void* V;

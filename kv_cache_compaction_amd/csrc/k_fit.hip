@@ -1374,7 +1374,7 @@ struct Carve {
 struct BetaPlan {
   float* shift2; float* target; float* Gpart; float* hpart; float* G; float* hv;
   float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float* TK; float* hsmax;
-  int* iters; int* fin; float2* init; int* bar; float2* rowstat_cmp; double2* part; int32_t* status;
+  int* iters; int* fin; float2* init; int* bar; int2* tstat; float2* rowstat_cmp; double2* part; int32_t* status;
   SyrkBuffers sy;
   size_t bytes;
 };
@@ -1413,6 +1413,7 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
   p.fin = c.take<int>(heads);
   p.init = c.take<float2>(heads * nblk);
   p.bar = c.take<int>(heads);
+  p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
   p.status = c.take<int32_t>(heads);
   p.bytes = c.off;
   return p;
@@ -1420,7 +1421,7 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
 
 struct ValuePlan {
   float2* rowstat_cmp; double2* part; float* shift2; float* Gpart; float* Rpart; double* A;
-  double* R; double* Linv; void* Vt; float2* rowres; int32_t* status;
+  double* R; double* Linv; void* Vt; int2* tstat; float2* rowres; int32_t* status;
   SyrkBuffers sy;
   size_t bytes;
 };
@@ -1449,6 +1450,7 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   p.R = c.take<double>((size_t)heads * ld * d);
   p.Linv = c.take<double>((size_t)heads * (ld / kNB) * kNB * kNB);
   p.Vt = c.take<char>(cmp_vt_bytes(heads, t, d, esize));
+  p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
   p.rowres = c.take<float2>(heads * n);
   p.status = c.take<int32_t>(heads);
   p.bytes = c.off;
@@ -1571,7 +1573,8 @@ hipError_t launch_fit_beta(const FitArgs& a) {
   if (a.mass_resid || a.keep_cmp_stats) {
     CmpAttnArgs ca;
     ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = a.beta; ca.keypos = a.idx; ca.Y = nullptr;
-    ca.Vt = nullptr; ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
+    ca.Vt = nullptr; ca.tstat = pl.tstat;
+    ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
     ca.heads = H; ca.n = n; ca.t = t; ca.d = d; ca.group = a.group; ca.causal = a.causal;
     ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
     hipError_t e = launch_cmp_attention(ca);
@@ -1598,7 +1601,8 @@ hipError_t launch_fit_values(const FitArgs& a) {
   // compacted log-normalizer per query (biased pass, statistics only)
   CmpAttnArgs ca;
   ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = a.beta_in; ca.keypos = a.idx; ca.Y = nullptr;
-  ca.Vt = pl.Vt; ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
+  ca.Vt = pl.Vt; ca.tstat = pl.tstat;
+  ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
   ca.heads = H; ca.n = n; ca.t = t; ca.d = d; ca.group = a.group; ca.causal = a.causal;
   ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
   hipError_t e = hipSuccess;

@@ -93,6 +93,7 @@ struct FlashLds {
 struct FlashParams {
   const void* Q; const void* K; const void* Vt;
   const float* bias; const int32_t* keypos; const float* Y;
+  const int2* tstat;   // biased causal: per key tile (min, max) original position, or null
   float* lse; float2* rowstat; float* O; float2* rowres;
   int n, Tk, Tpad, group, heads, n_qtiles;
   float c2;
@@ -152,10 +153,29 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 
   int kend = Tk;
   if (CAUSAL && !BIASED) kend = min(Tk, (min(q0 + BM, n) - 1) / group + 1);
-  const int ntiles = (kend + BN - 1) / BN;
   // leading tiles this wave can take without any mask
   int nfull = Tk / BN;
-  if (CAUSAL) nfull = BIASED ? 0 : min(nfull, (wq0 / group + 1) / BN);
+  if (CAUSAL && !BIASED) nfull = min(nfull, (wq0 / group + 1) / BN);
+  if (CAUSAL && BIASED) {
+    // compacted keys carry their original positions: tiles past the last one holding a
+    // key visible to the workgroup's last query are dropped, and leading tiles whose every
+    // key is visible to this wave's first query need no mask
+    int nf = 0, last = -1;
+    if (p.tstat) {
+      const int2* ts = p.tstat + (size_t)head * ((Tk + BN - 1) / BN);
+      const int qmax = (min(q0 + BM, n) - 1) / group, qmin = wq0 / group;
+      bool lead = true;
+      for (int i = 0; i < (Tk + BN - 1) / BN; ++i) {
+        const int2 v = ts[i];
+        if (v.x <= qmax) last = i;
+        lead = lead && v.y <= qmin;
+        if (lead) nf = i + 1;
+      }
+      kend = min(Tk, (last + 1) * BN);
+    }
+    nfull = min(nfull, nf);
+  }
+  const int ntiles = (kend + BN - 1) / BN;
   nfull = min(nfull, ntiles);
 
   u32x4 kreg[KPT];
@@ -540,7 +560,7 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   }
   FlashParams fp;
   fp.Q = a.Q; fp.K = a.K; fp.Vt = a.Vt;
-  fp.bias = nullptr; fp.keypos = nullptr; fp.Y = nullptr;
+  fp.bias = nullptr; fp.keypos = nullptr; fp.Y = nullptr; fp.tstat = nullptr;
   fp.lse = a.lse; fp.rowstat = (float2*)a.rowstat; fp.O = a.O; fp.rowres = nullptr;
   fp.n = a.n; fp.Tk = a.T; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
   fp.c2 = c2;
@@ -567,9 +587,30 @@ hipError_t launch_targets(const TargetsArgs& a) {
   return a.d == 128 ? launch_targets_t<float, 128>(a) : launch_targets_t<float, 64>(a);
 }
 
+// (min, max) original position of the keys of each BN-key tile of the compacted cache.
+__global__ __launch_bounds__(256) void tile_stat_kernel(const int32_t* __restrict__ keypos,
+                                                        int2* __restrict__ tstat, int t, int bn,
+                                                        int ntile) {
+  const int head = blockIdx.y, tile = blockIdx.x * 256 + threadIdx.x;
+  if (tile >= ntile) return;
+  const int32_t* kp = keypos + (size_t)head * t;
+  int lo = 0x7fffffff, hi = -1;
+  for (int j = tile * bn; j < min(t, tile * bn + bn); ++j) {
+    lo = min(lo, kp[j]);
+    hi = max(hi, kp[j]);
+  }
+  tstat[(size_t)head * ntile + tile] = make_int2(lo, hi);
+}
+
 template <typename T, int D>
 static hipError_t launch_cmp_t(const CmpAttnArgs& a) {
   const int Tpad = round_up(a.t, kBN);
+  if (a.causal && a.tstat) {
+    constexpr int BN = flash_bn<T, D>();
+    const int ntile = (a.t + BN - 1) / BN;
+    hipLaunchKernelGGL(tile_stat_kernel, dim3((ntile + 255) / 256, a.heads), dim3(256), 0,
+                       a.stream, a.keypos, a.tstat, a.t, BN, ntile);
+  }
   if (a.Cv) {
     dim3 g(Tpad / kBN, a.heads);
     hipLaunchKernelGGL((transpose_v_kernel<float, T, D>), g, dim3(256), 0, a.stream, a.Cv,
@@ -577,7 +618,7 @@ static hipError_t launch_cmp_t(const CmpAttnArgs& a) {
   }
   FlashParams fp;
   fp.Q = a.Q; fp.K = a.Ck; fp.Vt = a.Vt;
-  fp.bias = a.bias; fp.keypos = a.keypos; fp.Y = a.Y;
+  fp.bias = a.bias; fp.keypos = a.keypos; fp.Y = a.Y; fp.tstat = a.causal ? a.tstat : nullptr;
   fp.lse = a.lse; fp.rowstat = a.rowstat; fp.O = a.O; fp.rowres = a.rowres;
   fp.n = a.n; fp.Tk = a.t; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
   fp.c2 = a.scale * kLog2e;
@@ -605,5 +646,8 @@ size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize) {
 namespace amc {
 size_t cmp_vt_bytes(int64_t heads, int64_t t, int64_t d, int esize) {
   return align_up((size_t)heads * d * round_up((int)t, kBN) * esize);
+}
+size_t cmp_tstat_bytes(int64_t heads, int64_t t) {
+  return align_up((size_t)heads * ((t + 31) / 32) * sizeof(int2));   // 32-key tiles or larger
 }
 }  // namespace amc
