@@ -1006,143 +1006,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
 // ------------------------------------------------------------------------------------
 // Blocked fp64 Cholesky and triangular solves on A [h, ld, ld], R [h, ld, D]
 // ------------------------------------------------------------------------------------
-// Factor the diagonal block kb in place (lower) and store its inverse in Linv[h, nb, 64, 64].
-// The 64 x 64 block is split 2 x 2 into 32 x 32 blocks:
-//   L11 = chol(A11), L21 = A21 L11^-T, L22 = chol(A22 - L21 L21^T),
-//   L^-1 = [[L11^-1, 0], [-L22^-1 (L21 L11^-1), L22^-1]].
-// The two 32 x 32 factorizations (and inverses) run on one wave each, entirely in
-// registers: lane r holds row r, and the entries of other rows that a step needs are
-// broadcast with v_readlane at compile-time lane and register numbers, so the sequential
-// part has no barrier and no LDS round trip. The products between them use all 256 threads.
-
-// value of a double held by lane `lane` (wave-uniform result)
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffff), lane);
-  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-// step C of the right-looking factorization of a 32 x 32 block held by rows (a[j] = A[r][j])
-template <int C>
-__device__ __forceinline__ void chol32_step(double (&a)[32], int r, bool& bad) {
-  if constexpr (C < 32) {
-    double pv = readlane_f64(a[C], C);
-    if (!(pv > 0.0)) {
-      bad = true;
-      pv = 1e-300;
-    }
-    const double d = sqrt(pv), inv = 1.0 / d;
-    a[C] = r > C ? a[C] * inv : (r == C ? d : 0.0);
-#pragma unroll
-    for (int j = C + 1; j < 32; ++j) a[j] -= a[C] * readlane_f64(a[C], j);
-    chol32_step<C + 1>(a, r, bad);
-  }
-}
-// column `lane` of L^-1 by forward elimination (x starts as the unit vector e_lane)
-template <int I>
-__device__ __forceinline__ void chol32_inv_step(const double (&a)[32], double (&x)[32]) {
-  if constexpr (I < 32) {
-    x[I] *= 1.0 / readlane_f64(a[I], I);
-#pragma unroll
-    for (int m = I + 1; m < 32; ++m) x[m] -= readlane_f64(a[I], m) * x[I];
-    chol32_inv_step<I + 1>(a, x);
-  }
-}
-// One wave: factor the 32 x 32 block at L[o][o] (LDS, lower part read) in place and store
-// its inverse at Li[o][o]; lanes 32..63 repeat lanes 0..31 and store nothing.
-__device__ __forceinline__ void chol32_wave(double (*L)[kNB + 1], double (*Li)[kNB + 1], int o,
-                                            bool& bad) {
-  const int r = threadIdx.x & 31;
-  const bool st = (threadIdx.x & 63) < 32;
-  double a[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) a[j] = L[o + r][o + j];
-  chol32_step<0>(a, r, bad);
-  double x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = i == r ? 1.0 : 0.0;
-  chol32_inv_step<0>(a, x);
-  if (st) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) L[o + r][o + j] = j <= r ? a[j] : 0.0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) Li[o + i][o + r] = x[i];
-  }
-}
-
-// out[i][j] (i, j < 32; thread (tid / 8, tid % 8 + 8 m)) = sum_k P[i][k] Q[k][j] or
-// P[i][k] Q[j][k] (TQ)
-template <bool TQ>
-__device__ __forceinline__ void mm32(double (&out)[4], const double (*P)[kNB + 1], int pr, int pc,
-                                     const double (*Q)[kNB + 1], int qr, int qc, int tid) {
-  const int i = tid >> 3, j0 = tid & 7;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) out[m] = 0.0;
-#pragma unroll 8
-  for (int k = 0; k < 32; ++k) {
-    const double pv = P[pr + i][pc + k];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      out[m] += pv * (TQ ? Q[qr + j0 + 8 * m][qc + k] : Q[qr + k][qc + j0 + 8 * m]);
-  }
-}
-
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
-                                                        int nb, int32_t* status) {
-  __shared__ double L[kNB][kNB + 1];    // the block, then its factor
-  __shared__ double Li[kNB][kNB + 1];   // the inverse of the factor
-  __shared__ double T[32][kNB + 1];     // L21 L11^-1
-  __shared__ int badf;
-  const int head = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-  double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
-  for (int e = tid; e < kNB * kNB; e += 256) L[e >> 6][e & 63] = Ah[(size_t)(e >> 6) * ld + (e & 63)];
-  for (int e = tid; e < kNB * kNB; e += 256) Li[e >> 6][e & 63] = 0.0;
-  if (tid == 0) badf = 0;
-  __syncthreads();
-  bool bad = false;
-  if (wave == 0) chol32_wave(L, Li, 0, bad);
-  __syncthreads();
-  const int i = tid >> 3, j0 = tid & 7;
-  double acc[4];
-  // L21 = A21 L11^-T: L21[i][j] = sum_k A21[i][k] Li11[j][k]
-  mm32<true>(acc, L, 32, 0, Li, 0, 0, tid);
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < 4; ++m) L[32 + i][j0 + 8 * m] = acc[m];
-  __syncthreads();
-  // Schur complement A22 - L21 L21^T
-  mm32<true>(acc, L, 32, 0, L, 32, 0, tid);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) L[32 + i][32 + j0 + 8 * m] -= acc[m];
-  __syncthreads();
-  // wave 0: L22 and its inverse; the other waves meanwhile T = L21 L11^-1
-  if (wave == 0) {
-    chol32_wave(L, Li, 32, bad);
-  } else {
-    for (int e = tid - 64; e < 32 * 32; e += 192) {
-      const int ii = e >> 5, jj = e & 31;
-      double v = 0.0;
-      for (int k = jj; k < 32; ++k) v += L[32 + ii][k] * Li[k][jj];
-      T[ii][jj] = v;
-    }
-  }
-  __syncthreads();
-  // Li21 = -L22^-1 T
-  mm32<false>(acc, Li, 32, 32, T, 0, 0, tid);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) Li[32 + i][j0 + 8 * m] = -acc[m];
-  if (bad) badf = 1;
-  __syncthreads();
-  double* Lo = Linv + ((size_t)head * nb + kb) * kNB * kNB;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    Ah[(size_t)r * ld + c] = c <= r ? L[r][c] : 0.0;
-    Lo[e] = c <= r ? Li[r][c] : 0.0;
-  }
-  if (tid == 0 && badf && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
-}
-
-// 64-row fp64 blocks staged through LDS for the block kernels below. A loader issues all of
+// 64-row fp64 blocks staged through LDS for the block kernels. A loader issues all of
 // its global loads (16-byte, one per register pair) before it writes any of them to LDS, so
 // a block costs one memory latency rather than one per element.
 constexpr int kLdp = kNB + 1;   // LDS row pitch (odd: column reads by 16 rows hit 16 banks)
@@ -1175,6 +1039,160 @@ struct BlockRegs {
     }
   }
 };
+
+// Factor the diagonal block kb in place (lower) and store its inverse in Linv[h, nb, 64, 64].
+// The 64 x 64 block is split 2 x 2 into 32 x 32 blocks:
+//   L11 = chol(A11), L21 = A21 L11^-T, L22 = chol(A22 - L21 L21^T),
+//   L^-1 = [[L11^-1, 0], [-L22^-1 (L21 L11^-1), L22^-1]].
+// Each 32 x 32 factorization (with its inverse) runs on one wave as symmetric Gaussian
+// elimination without pivoting on [A | I]: lanes 0..31 hold the rows of A, lanes 32..63 the
+// rows of I. Step k subtracts (a_rk / a_kk) times pivot row k from every row r > k, in both
+// halves; the pivot rows go through LDS and are read as broadcasts. By symmetry of the
+// trailing block, a_rk is entry r of the pivot row. Afterwards row k of the A half is
+// u_k = L_kk L^T(k, :) with u_kk = L_kk^2 (the k-th pivot), and the I half holds the unit
+// lower triangle M = (L D^-1)^-1, D = diag(L_kk), so L(:, k) = u_k / sqrt(u_kk) and
+// L^-1(k, :) = M(k, :) / sqrt(u_kk).
+// The loop over k is not unrolled: register indices are all compile-time, only the
+// predicates depend on k.
+__device__ __forceinline__ void chol32_wave(double (*L)[kNB + 1], double (*Li)[kNB + 1], int o,
+                                            double (*piv)[32], bool& bad) {
+  const int lane = threadIdx.x & 63, r = lane & 31, half = lane >> 5;
+  double a[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const double v = L[o + (j <= r ? r : j)][o + (j <= r ? j : r)];   // lower triangle
+    a[j] = half ? (j == r ? 1.0 : 0.0) : v;
+  }
+  for (int k = 0; k < 32; ++k) {
+    if (r == k) {
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) *(double2*)&piv[half][j] = make_double2(a[j], a[j + 1]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // every read of the step is issued before any arithmetic waits on one
+    double2 x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = *(const double2*)&piv[half][2 * j];
+    double p = piv[0][k];
+    const double ark = piv[0][r];
+    __builtin_amdgcn_sched_barrier(0);
+    if (!(p > 0.0)) {
+      bad = true;
+      p = 1e-300;
+    }
+    // 1 / p from the hardware estimate and two Newton steps (p > 0 here)
+    double ip = __builtin_amdgcn_rcp(p);
+    ip = __builtin_fma(ip, __builtin_fma(-p, ip, 1.0), ip);
+    ip = __builtin_fma(ip, __builtin_fma(-p, ip, 1.0), ip);
+    const double m = r > k ? ark * ip : 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      a[2 * j] -= m * x[j].x;
+      a[2 * j + 1] -= m * x[j].y;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  // u_rr through LDS (lane r's own a[r] has a run-time register index)
+  double dr = a[0];
+#pragma unroll
+  for (int j = 1; j < 32; ++j) dr = j == r ? a[j] : dr;
+  if (half == 0) piv[0][r] = dr;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  double u = piv[0][r];
+  if (!(u > 0.0)) {
+    bad = true;
+    u = 1e-300;
+  }
+  const double inv = 1.0 / sqrt(u);
+  if (half == 0) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) L[o + j][o + r] = j >= r ? a[j] * inv : 0.0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) Li[o + r][o + j] = j <= r ? a[j] * inv : 0.0;
+  }
+}
+
+// out[i][j] (i, j < 32; thread (tid / 8, tid % 8 + 8 m)) = sum_k P[i][k] Q[k][j] or
+// P[i][k] Q[j][k] (TQ)
+template <bool TQ>
+__device__ __forceinline__ void mm32(double (&out)[4], const double (*P)[kNB + 1], int pr, int pc,
+                                     const double (*Q)[kNB + 1], int qr, int qc, int tid) {
+  const int i = tid >> 3, j0 = tid & 7;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) out[m] = 0.0;
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k) {
+    const double pv = P[pr + i][pc + k];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      out[m] += pv * (TQ ? Q[qr + j0 + 8 * m][qc + k] : Q[qr + k][qc + j0 + 8 * m]);
+  }
+}
+
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
+                                                        int nb, int32_t* status) {
+  __shared__ double L[kNB][kNB + 1];    // the block, then its factor
+  __shared__ double Li[kNB][kNB + 1];   // the inverse of the factor
+  __shared__ double T[32][kNB + 1];     // L21 L11^-1
+  __shared__ double piv[2][32];         // pivot rows of the wave-level eliminations
+  __shared__ int badf;
+  const int head = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
+  {
+    BlockRegs<kNB> ra;
+    ra.load(Ah, ld, tid);
+    ra.store<false>(L, tid);
+  }
+  for (int e = tid; e < kNB * kNB; e += 256) Li[e >> 6][e & 63] = 0.0;
+  if (tid == 0) badf = 0;
+  __syncthreads();
+  bool bad = false;
+  if (wave == 0) chol32_wave(L, Li, 0, piv, bad);
+  __syncthreads();
+  const int i = tid >> 3, j0 = tid & 7;
+  double acc[4];
+  // L21 = A21 L11^-T: L21[i][j] = sum_k A21[i][k] Li11[j][k]
+  mm32<true>(acc, L, 32, 0, Li, 0, 0, tid);
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 4; ++m) L[32 + i][j0 + 8 * m] = acc[m];
+  __syncthreads();
+  // Schur complement A22 - L21 L21^T
+  mm32<true>(acc, L, 32, 0, L, 32, 0, tid);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) L[32 + i][32 + j0 + 8 * m] -= acc[m];
+  __syncthreads();
+  // wave 0: L22 and its inverse; the other waves meanwhile T = L21 L11^-1
+  if (wave == 0) {
+    chol32_wave(L, Li, 32, piv, bad);
+  } else {
+    for (int e = tid - 64; e < 32 * 32; e += 192) {
+      const int ii = e >> 5, jj = e & 31;
+      double v = 0.0;
+      for (int k = jj; k < 32; ++k) v += L[32 + ii][k] * Li[k][jj];
+      T[ii][jj] = v;
+    }
+  }
+  __syncthreads();
+  // Li21 = -L22^-1 T
+  mm32<false>(acc, Li, 32, 32, T, 0, 0, tid);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) Li[32 + i][j0 + 8 * m] = -acc[m];
+  if (bad) badf = 1;
+  __syncthreads();
+  double* Lo = Linv + ((size_t)head * nb + kb) * kNB * kNB;
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    Ah[(size_t)r * ld + c] = c <= r ? L[r][c] : 0.0;
+    Lo[e] = c <= r ? Li[r][c] : 0.0;
+  }
+  if (tid == 0 && badf && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
+}
+
 
 // acc[a][b] = sum_k P[ti + 16 a][k] Q[tj + 16 b][k] over k < 64, for ti = tid / 16,
 // tj = tid % 16 (a 64 x 64 product of two row-major LDS blocks, 4 x 4 per thread).
