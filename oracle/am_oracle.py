@@ -30,6 +30,12 @@ exactly before they arrive here):
   E   the compacted attention itself, to evaluate any (idx, beta, C_v): biased scores
       l(q) = scale K_cmp q + b (Latent Compaction §3.1, Eq. 2), output Eq. 3 and
       normalizer Z_cmp = 1^T exp(l) (Eq. 4), plus the residuals compared in parity.
+  C   attention through a compacted cache followed by ordinary appended entries: each
+      branch gives an output and a log-normalizer (Latent Compaction App. A.2, the
+      normalizer-aware cache attention: biased and slot-masked document branch, causal
+      unbiased branch for the new tokens), combined by Eq. 5 in log space.
+  F   the fast variants of the "Compaction" blog: beta by uniform redistribution of the
+      missing mass (§Choosing beta) and direct values C_v = V[idx] (§Choosing C_v).
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
 masked keys are excluded (exp(-inf) = 0), which equals the pseudocode's finfo.min fill
@@ -328,6 +334,110 @@ def compacted_attention(Q, Ck, idx, beta, Cv, scale, causal=False, group=1):
         logz[fin] = m[fin] + np.log(z)
         A[fin] = (e / z[:, None]) @ np.asarray(Cv, np.float64)
     return logz, A
+
+
+# --------------------------------------------------------------------------------------
+# C: cache attention with appended entries, and the log-space combination
+# --------------------------------------------------------------------------------------
+def branch_attention(Q, keys, values, bias, valid, scale):
+    """Output [n, d] and log-normalizer [n] of one attention branch.
+
+    Scores scale * q.k, plus bias[j] when bias is given; entries where valid[i, j] is
+    False are excluded. A row without any valid entry gets log Z = -inf and a zero output:
+    the branch then carries no weight when combined (the pseudocode's finfo.min fill gives
+    the same combined result whenever the other branch has an entry).
+    """
+    Q = np.asarray(Q, np.float64)
+    keys = np.asarray(keys, np.float64)
+    n, d = Q.shape[0], np.asarray(values).shape[1]
+    out = np.zeros((n, d))
+    logz = np.full(n, -np.inf)
+    if keys.shape[0] == 0:
+        return out, logz
+    s = scale * (Q @ keys.T)
+    if bias is not None:
+        s = s + np.asarray(bias, np.float64)[None, :]
+    s = np.where(np.broadcast_to(valid, s.shape), s, -np.inf)
+    m = s.max(axis=1)
+    fin = np.isfinite(m)
+    if fin.any():
+        e = np.exp(s[fin] - m[fin, None])
+        z = e.sum(axis=1)
+        logz[fin] = m[fin] + np.log(z)
+        out[fin] = (e / z[:, None]) @ np.asarray(values, np.float64)
+    return out, logz
+
+
+def combine_attention(out1, logz1, out2, logz2):
+    """Eq. 5 in log space: log Z = logaddexp(log Z1, log Z2); out = the Z-weighted mixture.
+
+    Rows where both branches are empty keep log Z = -inf and a zero output.
+    """
+    logz = np.logaddexp(logz1, logz2)
+    out = np.zeros_like(np.asarray(out1, np.float64))
+    fin = np.isfinite(logz)
+    w1 = np.exp(logz1[fin] - logz[fin])
+    w2 = np.exp(logz2[fin] - logz[fin])
+    out[fin] = w1[:, None] * out1[fin] + w2[:, None] * out2[fin]
+    return out, logz
+
+
+def cache_attention(Q, Ck, Cv, bias, scale, keypos=None, nvalid=None, causal=False, group=1,
+                    Kn=None, Vn=None, new_causal=True):
+    """Attention of queries Q through a compacted cache (Ck, Cv, bias) and optional new
+    entries (Kn, Vn) appended after it.
+
+    Document slot j is valid when j < nvalid and, for causal problems, when its original
+    position keypos[j] <= i // group. New entry j is visible to query i when
+    j <= i // group (new_causal) or always. Returns (out [n, d], log Z [n], log Z_cmp [n]).
+    """
+    n = np.asarray(Q).shape[0]
+    t = np.asarray(Ck).shape[0]
+    slots = np.arange(t)
+    valid = np.ones((n, t), dtype=bool)
+    if nvalid is not None:
+        valid &= (slots < nvalid)[None, :]
+    if causal:
+        valid &= visible(np.arange(n), np.asarray(keypos), True, group)
+    out1, lz1 = branch_attention(Q, Ck, Cv, bias, valid, scale)
+    if Kn is None or np.asarray(Kn).shape[0] == 0:
+        return out1, lz1.copy(), lz1
+    m = np.asarray(Kn).shape[0]
+    nvis = visible(np.arange(n), np.arange(m), bool(new_causal), group)
+    out2, lz2 = branch_attention(Q, Kn, Vn, None, nvis, scale)
+    out, lz = combine_attention(out1, lz1, out2, lz2)
+    return out, lz, lz1
+
+
+# --------------------------------------------------------------------------------------
+# F: fast variants (no fits)
+# --------------------------------------------------------------------------------------
+def redistribute_beta(Q, Ck, idx, lse, scale, causal=False, group=1):
+    """beta by uniform redistribution of the missing mass ("Compaction" blog, §Choosing beta).
+
+    m_j   = (1/n) sum_i exp(s_{i, c_j}) over the queries that see c_j,
+    Delta = (1/n) sum_i [Z_i - sum_j exp(s_{i, c_j})] with Z_i = exp(lse_i) the mass of
+            query i over the reference key set (the full cache, or a shortlist),
+    beta_j = log((m_j + Delta / t) / m_j).
+    Every selected key receives the same share Delta / t of the mass the compacted keys miss.
+    """
+    Q = np.asarray(Q, np.float64)
+    lse = np.asarray(lse, np.float64)
+    n, t = Q.shape[0], np.asarray(Ck).shape[0]
+    c = lse.max()   # common factor e^c of every mass; beta does not depend on it
+    e = np.zeros((n, t))
+    for a, b in _chunks(n, t):
+        s = scale * (Q[a:b] @ np.asarray(Ck, np.float64).T)
+        vis = visible(np.arange(a, b), np.asarray(idx), causal, group)
+        e[a:b] = np.where(vis, np.exp(np.where(vis, s, 0.0) - c), 0.0)
+    m = e.sum(axis=0) / n
+    delta = (np.exp(lse - c).sum() - e.sum()) / n
+    return np.log((m + delta / t) / m)
+
+
+def direct_values(V, idx):
+    """C_v = V[idx] as float64 (blog, §Choosing C_v: the selected keys keep their values)."""
+    return np.asarray(V, np.float64)[np.asarray(idx)]
 
 
 def residuals(lse, O, logz_cmp, A_cmp):

@@ -328,3 +328,175 @@ def test_absolute_mass_mode_is_row_weighting():
     wa, _ = O.fit_beta(Ma, ba)
     ws, _ = scipy.optimize.nnls(Mr * z[:, None], z)
     np.testing.assert_allclose(Ma @ wa, Ma @ ws, atol=1e-10)
+
+
+# --------------------------------------------------------------------------------------
+# cache attention with appended entries (Latent Compaction §3.1 Eq. 2-5, App. A.2)
+# --------------------------------------------------------------------------------------
+def _cache_case(rng, n=37, t=23, m=11, d=8, group=2):
+    Q = rng.standard_normal((n, d))
+    Ck = rng.standard_normal((t, d))
+    Cv = rng.standard_normal((t, d))
+    bias = rng.standard_normal(t)
+    keypos = np.sort(rng.choice(3 * t, size=t, replace=False))
+    Kn = rng.standard_normal((m, d))
+    Vn = rng.standard_normal((m, d))
+    return Q, Ck, Cv, bias, keypos, Kn, Vn
+
+
+@pytest.mark.parametrize("causal,new_causal,nvalid", [(False, True, None), (True, True, 17),
+                                                      (True, False, 23), (False, False, 5)])
+def test_cache_attention_is_one_softmax_over_both_sets(causal, new_causal, nvalid):
+    """Eq. 5 equals a single softmax over the document slots (biased, masked) and the new
+    entries (unbiased, causal): computed here directly on the concatenation."""
+    rng = np.random.default_rng(11)
+    Q, Ck, Cv, bias, keypos, Kn, Vn = _cache_case(rng)
+    n, t, m, g, scale = Q.shape[0], Ck.shape[0], Kn.shape[0], 2, 0.4
+    out, lz, lz1 = O.cache_attention(Q, Ck, Cv, bias, scale, keypos=keypos, nvalid=nvalid,
+                                     causal=causal, group=g, Kn=Kn, Vn=Vn, new_causal=new_causal)
+    s = np.concatenate([scale * Q @ Ck.T + bias, scale * Q @ Kn.T], axis=1)
+    ok = np.ones_like(s, dtype=bool)
+    if nvalid is not None:
+        ok[:, nvalid:t] = False
+    pos = np.arange(n) // g
+    if causal:
+        ok[:, :t] &= keypos[None, :] <= pos[:, None]
+    if new_causal:
+        ok[:, t:] &= np.arange(m)[None, :] <= pos[:, None]
+    s = np.where(ok, s, -np.inf)
+    ref_lz = scipy.special.logsumexp(s, axis=1)
+    ref_out = np.exp(s - ref_lz[:, None]) @ np.concatenate([Cv, Vn])
+    np.testing.assert_allclose(lz, ref_lz, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+    ref_lz1 = scipy.special.logsumexp(s[:, :t], axis=1)
+    np.testing.assert_allclose(lz1, ref_lz1, rtol=0, atol=1e-12)
+
+
+def test_bias_is_log_multiplicity():
+    """A slot with bias log r weighs exactly like r unbiased copies of its key and value."""
+    rng = np.random.default_rng(12)
+    Q, Ck, Cv, _, _, _, _ = _cache_case(rng, t=6)
+    r = np.array([1, 3, 1, 2, 5, 1])
+    rep_k, rep_v = np.repeat(Ck, r, axis=0), np.repeat(Cv, r, axis=0)
+    out_b, lz_b, _ = O.cache_attention(Q, Ck, Cv, np.log(r), 0.7)
+    out_r, lz_r, _ = O.cache_attention(Q, rep_k, rep_v, np.zeros(r.sum()), 0.7)
+    np.testing.assert_allclose(out_b, out_r, atol=1e-12)
+    np.testing.assert_allclose(lz_b, lz_r, atol=1e-12)
+
+
+def test_cache_attention_hand_example():
+    """d = 1, q = 1, scale 1. Document: keys 0, 0 with biases 0, log 3 and values 1, 5, so
+    Z_cmp = 1 + 3 = 4 and A_cmp = (1 + 15) / 4 = 4. New entry: key log 4, value -2, so
+    Z_new = 4 and A_new = -2. Eq. 5: A = (4 * 4 + 4 * (-2)) / 8 = 1 and log Z = log 8."""
+    out, lz, lz1 = O.cache_attention(np.ones((1, 1)), np.zeros((2, 1)), np.array([[1.0], [5.0]]),
+                                     np.array([0.0, np.log(3.0)]), 1.0,
+                                     Kn=np.array([[np.log(4.0)]]), Vn=np.array([[-2.0]]))
+    assert abs(out[0, 0] - 1.0) < 1e-14
+    assert abs(lz[0] - np.log(8.0)) < 1e-14
+    assert abs(lz1[0] - np.log(4.0)) < 1e-14
+
+
+def test_cache_attention_empty_branches():
+    rng = np.random.default_rng(13)
+    Q, Ck, Cv, bias, keypos, Kn, Vn = _cache_case(rng)
+    # no new entries: the document branch alone
+    out, lz, lz1 = O.cache_attention(Q, Ck, Cv, bias, 0.5)
+    d_out, d_lz = O.branch_attention(Q, Ck, Cv, bias, np.ones((Q.shape[0], Ck.shape[0]), bool), 0.5)
+    np.testing.assert_array_equal(out, d_out)
+    np.testing.assert_array_equal(lz, d_lz)
+    # no valid slot: the new branch alone (unbiased causal attention over Kn)
+    out, lz, lz1 = O.cache_attention(Q, Ck, Cv, bias, 0.5, nvalid=0, Kn=Kn, Vn=Vn, group=4)
+    assert np.all(lz1 == -np.inf)
+    ref_lse, ref_O, _ = O.full_cache_stats(Q, Kn, Vn, 0.5, causal=True, group=4)
+    np.testing.assert_allclose(lz, ref_lse, atol=1e-12)
+    np.testing.assert_allclose(out, ref_O, atol=1e-12)
+    # both empty: -inf and zero rows
+    out, lz, _ = O.cache_attention(Q, Ck, Cv, bias, 0.5, nvalid=0)
+    assert np.all(lz == -np.inf) and np.all(out == 0.0)
+
+
+def test_unbiased_cache_attention_is_plain_attention():
+    rng = np.random.default_rng(14)
+    Q, Ck, Cv, _, _, _, _ = _cache_case(rng)
+    out, lz, _ = O.cache_attention(Q, Ck, Cv, np.zeros(Ck.shape[0]), 0.3)
+    lse, Oref, _ = O.full_cache_stats(Q, Ck, Cv, 0.3)
+    np.testing.assert_allclose(lz, lse, atol=1e-12)
+    np.testing.assert_allclose(out, Oref, atol=1e-12)
+
+
+def test_combine_weights_sum_to_one_and_commute():
+    rng = np.random.default_rng(15)
+    o1, o2 = rng.standard_normal((2, 9, 4))
+    l1 = rng.standard_normal(9) * 5
+    l2 = rng.standard_normal(9) * 5
+    l2[3] = -np.inf
+    a, la = O.combine_attention(o1, l1, o2, l2)
+    b, lb = O.combine_attention(o2, l2, o1, l1)
+    np.testing.assert_allclose(a, b, atol=1e-13)
+    np.testing.assert_array_equal(la, lb)
+    np.testing.assert_allclose(a[3], o1[3], atol=1e-15)
+    # equal normalizers: the plain average, and log Z grows by log 2
+    c, lc = O.combine_attention(o1, l1, o2, l1)
+    np.testing.assert_allclose(c, 0.5 * (o1 + o2), atol=1e-13)
+    np.testing.assert_allclose(lc, l1 + np.log(2.0), atol=1e-13)
+
+
+# --------------------------------------------------------------------------------------
+# fast variants ("Compaction" blog: redistribution beta, direct values)
+# --------------------------------------------------------------------------------------
+def _loop_redistribute(Q, Ck, idx, lse, scale, causal, group):
+    n, t = Q.shape[0], Ck.shape[0]
+    m = [0.0] * t
+    missing = 0.0
+    for i in range(n):
+        cmp_mass = 0.0
+        for j in range(t):
+            if not causal or idx[j] <= i // group:
+                e = float(np.exp(scale * float(Q[i] @ Ck[j])))
+                m[j] += e / n
+                cmp_mass += e
+        missing += (float(np.exp(lse[i])) - cmp_mass) / n
+    return np.array([np.log((m[j] + missing / t) / m[j]) for j in range(t)])
+
+
+@pytest.mark.parametrize("causal,group", [(False, 1), (True, 2)])
+def test_redistribute_beta_bruteforce(causal, group):
+    rng = np.random.default_rng(16)
+    T, d = 20, 6
+    n = group * T
+    Q, K, V = _qkv(n, T, d, rng)
+    lse, _, _ = O.full_cache_stats(Q, K, V, 0.5, causal, group)
+    idx = np.array([0, 3, 4, 9, 15, 19])
+    got = O.redistribute_beta(Q, K[idx], idx, lse, 0.5, causal, group)
+    ref = _loop_redistribute(Q, K[idx], idx, lse, 0.5, causal, group)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,group", [(False, 1), (True, 3)])
+def test_redistribute_beta_conserves_mean_mass(causal, group):
+    """With the redistributed biases the compacted cache's mass averaged over the reference
+    queries equals the full cache's (the missing mass is handed back in full)."""
+    rng = np.random.default_rng(17)
+    T, d = 64, 8
+    n = group * T
+    Q, K, V = _qkv(n, T, d, rng)
+    lse, _, _ = O.full_cache_stats(Q, K, V, 0.4, causal, group)
+    idx = np.sort(rng.choice(T, size=12, replace=False))
+    idx[0] = 0
+    beta = O.redistribute_beta(Q, K[idx], idx, lse, 0.4, causal, group)
+    logz, _ = O.compacted_attention(Q, K[idx], idx, beta, V[idx], 0.4, causal, group)
+    np.testing.assert_allclose(np.exp(logz).mean(), np.exp(lse).mean(), rtol=1e-12)
+    assert np.all(beta >= 0.0)   # the compacted keys never hold more than the full cache
+
+
+def test_redistribute_beta_full_budget_is_zero():
+    rng = np.random.default_rng(18)
+    Q, K, V = _qkv(30, 30, 5, rng)
+    lse, _, _ = O.full_cache_stats(Q, K, V, 0.6, True, 1)
+    beta = O.redistribute_beta(Q, K, np.arange(30), lse, 0.6, True, 1)
+    np.testing.assert_allclose(beta, 0.0, atol=1e-12)
+
+
+def test_direct_values_are_the_selected_rows():
+    V = np.arange(24.0).reshape(8, 3)
+    np.testing.assert_array_equal(O.direct_values(V, [1, 4, 6]), V[[1, 4, 6]])
