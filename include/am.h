@@ -162,13 +162,55 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
                           float* score_out, float* resid_out, int32_t* head_status,
                           void* ws, size_t ws_bytes, am_stream_t stream);
 
+/*
+ * am_cache_attention - attention of queries through a compacted cache whose slots carry
+ * learned biases, optionally followed by ordinary entries appended after it (Latent
+ * Compaction §3.1 Eq. 2-5; App. A.2, normalizer-aware cache attention: a biased,
+ * slot-masked document branch and an unbiased causal branch, combined through their
+ * log-normalizers). Here p->T is the number of cache slots t, p->n the queries per head,
+ * p->dtype the dtype of Q, Ck, Kn and Vn; p->causal masks the document branch by original
+ * position (no n == group * T requirement for this call).
+ *   document branch: l_ij = scale * q_i . Ck_j + bias_j over slots j < nvalid[h] (every
+ *     slot when nvalid is NULL; values are clamped to [0, t]); with p->causal, slot j is
+ *     also hidden from query i unless keypos[h, j] <= i / group (keypos required then,
+ *     ascending per head as am_select_keys returns it).
+ *     A_cmp = softmax(l) Cv and log Z_cmp = logsumexp(l).
+ *   new branch (m > 0): s_ij = scale * q_i . Kn_j, no bias; entry j is visible to query i
+ *     when j <= i / group (new_causal = 1) or always (new_causal = 0).
+ *   out[h, n, d] = (Z_cmp A_cmp + Z_new A_new) / (Z_cmp + Z_new), weights in log space;
+ *   lse[h, n] = log(Z_cmp + Z_new); lse_cmp[h, n] = log Z_cmp (optional, NULL skips).
+ *   A query with no visible entry in either branch gets lse = -inf and a zero row.
+ * Shapes: Ck [h, t, d] problem dtype; Cv [h, t, d] f32 (rounded to the problem dtype for
+ * the products); bias [h, t] f32; keypos [h, t] int32; nvalid [h] int32; Kn, Vn [h, m, d].
+ * Workspace: am_workspace_bytes(p, m, AM_CALL_CACHE_ATTENTION) (the budget argument is m).
+ */
+am_status am_cache_attention(const am_problem* p, const void* Q, const void* Ck, const float* Cv,
+                             const float* bias, const int32_t* keypos, const int32_t* nvalid,
+                             int64_t m, const void* Kn, const void* Vn, int32_t new_causal,
+                             float* out, float* lse, float* lse_cmp, void* ws, size_t ws_bytes,
+                             am_stream_t stream);
+
+/*
+ * am_attention_merge - combine two attention results over disjoint entry sets (Latent
+ * Compaction Eq. 5, in log space): for each of `rows` rows of d floats,
+ *   lse_out = logaddexp(lse1, lse2),
+ *   out = exp(lse1 - lse_out) O1 + exp(lse2 - lse_out) O2;
+ * rows where both normalizers are -inf get -inf and zeros. d must be a positive multiple
+ * of 4. out may be O1 or O2 and lse_out may be lse1 or lse2 (in-place merge); no
+ * workspace.
+ */
+am_status am_attention_merge(int64_t rows, int64_t d, const float* O1, const float* lse1,
+                             const float* O2, const float* lse2, float* out, float* lse_out,
+                             am_stream_t stream);
+
 /* Which call a workspace size is for. */
 typedef enum {
   AM_CALL_TARGETS = 0,
   AM_CALL_SELECT = 1,
   AM_CALL_FIT_BETA = 2,
   AM_CALL_FIT_VALUES = 3,
-  AM_CALL_COMPACT = 4
+  AM_CALL_COMPACT = 4,
+  AM_CALL_CACHE_ATTENTION = 5  /* the budget argument of am_workspace_bytes is m */
 } am_call;
 
 /* Workspace bytes a call needs for problem p and budget t (0 if the problem is invalid). */

@@ -20,7 +20,8 @@ AM_OK, AM_ERR_INVALID_ARG, AM_ERR_UNSUPPORTED, AM_ERR_WORKSPACE, AM_ERR_DEVICE =
 AM_F32, AM_BF16 = 0, 1
 SCORE_MODES = {"rms": 0, "mean": 1, "max": 2}
 MASS_MODES = {"relative": 0, "absolute": 1}
-CALL_TARGETS, CALL_SELECT, CALL_FIT_BETA, CALL_FIT_VALUES, CALL_COMPACT = range(5)
+CALL_TARGETS, CALL_SELECT, CALL_FIT_BETA, CALL_FIT_VALUES, CALL_COMPACT, CALL_CACHE_ATTENTION = \
+    range(6)
 HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE = 1, 2, 4
 
 
@@ -62,6 +63,11 @@ _PROTOS = {
     "am_compact_head": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, ctypes.c_int64,
                                        ctypes.POINTER(AmOptions), _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, ctypes.c_size_t, _P]),
+    "am_cache_attention": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_int64, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                          _P, ctypes.c_size_t, _P]),
+    "am_attention_merge": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
+                                          _P]),
 }
 
 
@@ -280,3 +286,57 @@ def compact_head(Q, K, V, t, *, causal=False, group=1, scale=None, options=None,
                                  _ptr(out["resid"]), _ptr(out["status"]), _ptr(ws), nb, _stream()),
            "am_compact_head")
     return out
+
+
+def cache_attention(Q, Ck, Cv, bias, *, keypos=None, nvalid=None, Kn=None, Vn=None,
+                    new_causal=True, causal=False, group=1, scale=None, want_lse_cmp=False):
+    """Attention through a compacted cache (slots Ck, Cv f32, bias f32; optional original
+    positions keypos for causal masking and per-head slot counts nvalid) followed by new
+    entries Kn, Vn. Returns out [h, n, d], lse [h, n] and, with want_lse_cmp, log Z_cmp."""
+    torch = _torch()
+    _need(Q, "Q"); _need(Ck, "Ck")
+    p = make_problem(Q, Ck, causal=causal, group=group, scale=scale)
+    h, n, t, d = p.heads, p.n, p.T, p.d
+    _need(Cv, "Cv", dtype=torch.float32, shape=(h, t, d))
+    _need(bias, "bias", dtype=torch.float32, shape=(h, t))
+    if keypos is not None:
+        _need(keypos, "keypos", dtype=torch.int32, shape=(h, t))
+    if nvalid is not None:
+        _need(nvalid, "nvalid", dtype=torch.int32, shape=(h,))
+    m = 0
+    if Kn is not None:
+        _need(Kn, "Kn", dtype=Q.dtype)
+        m = Kn.shape[1]
+        _need(Vn, "Vn", dtype=Q.dtype, shape=Kn.shape)
+        if Kn.shape[0] != h or Kn.shape[2] != d:
+            raise ValueError("Kn must be [h, m, d]")
+    dev = Q.device
+    out = torch.empty((h, n, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+    lz1 = torch.empty((h, n), dtype=torch.float32, device=dev) if want_lse_cmp else None
+    ws, nb = _workspace(p, m, CALL_CACHE_ATTENTION, dev)
+    _check(lib().am_cache_attention(ctypes.byref(p), _ptr(Q), _ptr(Ck), _ptr(Cv), _ptr(bias),
+                                    _ptr(keypos), _ptr(nvalid), m, _ptr(Kn) if m else None,
+                                    _ptr(Vn) if m else None, int(bool(new_causal)), _ptr(out),
+                                    _ptr(lse), _ptr(lz1), _ptr(ws), nb, _stream()),
+           "am_cache_attention")
+    return (out, lse, lz1) if want_lse_cmp else (out, lse)
+
+
+def attention_merge(O1, lse1, O2, lse2, *, out=None, lse_out=None):
+    """Log-space merge of two attention results over disjoint entry sets (Eq. 5).
+    O1, O2 [..., d] f32 and lse1, lse2 [...] f32; returns (out, lse)."""
+    torch = _torch()
+    for x, nm in ((O1, "O1"), (O2, "O2"), (lse1, "lse1"), (lse2, "lse2")):
+        _need(x, nm, dtype=torch.float32)
+    if O1.shape != O2.shape or lse1.shape != lse2.shape or tuple(O1.shape[:-1]) != tuple(lse1.shape):
+        raise ValueError("O1, O2 [..., d] and lse1, lse2 [...] must agree")
+    d = O1.shape[-1]
+    rows = lse1.numel()
+    out = torch.empty_like(O1) if out is None else out
+    lse_out = torch.empty_like(lse1) if lse_out is None else lse_out
+    _need(out, "out", dtype=torch.float32, shape=O1.shape)
+    _need(lse_out, "lse_out", dtype=torch.float32, shape=lse1.shape)
+    _check(lib().am_attention_merge(rows, d, _ptr(O1), _ptr(lse1), _ptr(O2), _ptr(lse2), _ptr(out),
+                                    _ptr(lse_out), _stream()), "am_attention_merge")
+    return out, lse_out

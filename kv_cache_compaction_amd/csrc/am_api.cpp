@@ -63,6 +63,38 @@ size_t ws_fit_beta(const am_problem* p, int64_t t) {
 size_t ws_fit_values(const am_problem* p, int64_t t) {
   return fit_values_ws_bytes(p->heads, p->n, t, p->d);
 }
+// The cache-attention problem: p->T is the slot count; causal masks by original position.
+am_status check_cache_problem(const am_problem* p) {
+  if (!p) return AM_ERR_INVALID_ARG;
+  if (p->heads < 1 || p->n < 1 || p->T < 1 || p->d < 1) return AM_ERR_INVALID_ARG;
+  if (p->group < 1 || (p->causal != 0 && p->causal != 1)) return AM_ERR_INVALID_ARG;
+  if (p->dtype != AM_F32 && p->dtype != AM_BF16) return AM_ERR_INVALID_ARG;
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return AM_ERR_INVALID_ARG;
+  if (p->d != 64 && p->d != 128) return AM_ERR_UNSUPPORTED;
+  if (p->n > (int64_t)1 << 30 || p->T > (int64_t)1 << 30 || p->heads > 65535)
+    return AM_ERR_UNSUPPORTED;
+  if ((p->heads * p->n) > ((int64_t)1 << 40) || (p->heads * p->T) > ((int64_t)1 << 40))
+    return AM_ERR_UNSUPPORTED;
+  return AM_OK;
+}
+
+struct CacheWs {
+  size_t vt, tstat, bias, lse1, vt_new, o2, lse2, total;
+};
+CacheWs cache_ws(const am_problem* p, int64_t m) {
+  CacheWs w;
+  const int es = esize(p);
+  w.vt = cmp_vt_bytes(p->heads, p->T, p->d, es);
+  w.tstat = p->causal ? cmp_tstat_bytes(p->heads, p->T) : 0;
+  w.bias = align_up((size_t)p->heads * p->T * 4);
+  w.lse1 = align_up((size_t)p->heads * p->n * 4);
+  w.vt_new = m > 0 ? targets_vt_bytes(p->heads, m, p->d, es) : 0;
+  w.o2 = m > 0 ? align_up((size_t)p->heads * p->n * p->d * 4) : 0;
+  w.lse2 = m > 0 ? align_up((size_t)p->heads * p->n * 4) : 0;
+  w.total = w.vt + w.tstat + w.bias + w.lse1 + w.vt_new + w.o2 + w.lse2;
+  return w;
+}
+
 size_t ws_compact(const am_problem* p, int64_t t) {
   // lse, O and score live in the workspace when the caller does not want them
   const size_t own = align_up((size_t)p->heads * p->n * 4) +
@@ -130,6 +162,10 @@ void am_default_options(am_options* o) {
 }
 
 size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
+  if (which == AM_CALL_CACHE_ATTENTION) {
+    if (check_cache_problem(p) != AM_OK || t < 0 || t > ((int64_t)1 << 30)) return 0;
+    return cache_ws(p, t).total;
+  }
   if (check_problem(p) != AM_OK) return 0;
   if (which != AM_CALL_TARGETS && check_t(p, t) != AM_OK) return 0;
   switch (which) {
@@ -270,6 +306,79 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
   fa.out_resid = resid_out ? resid_out + p->heads : nullptr;
   if ((e = launch_fit_values(fa)) != hipSuccess) return AM_ERR_DEVICE;
   return AM_OK;
+}
+
+am_status am_cache_attention(const am_problem* p, const void* Q, const void* Ck, const float* Cv,
+                             const float* bias, const int32_t* keypos, const int32_t* nvalid,
+                             int64_t m, const void* Kn, const void* Vn, int32_t new_causal,
+                             float* out, float* lse, float* lse_cmp, void* ws, size_t ws_bytes,
+                             am_stream_t stream) {
+  am_status st = check_cache_problem(p);
+  if (st != AM_OK) return st;
+  if (m < 0 || (new_causal != 0 && new_causal != 1)) return AM_ERR_INVALID_ARG;
+  if (m > ((int64_t)1 << 30) || p->heads * m > ((int64_t)1 << 40)) return AM_ERR_UNSUPPORTED;
+  if (!Q || !Ck || !Cv || !bias || !out || !lse || (p->causal && !keypos) ||
+      (m > 0 && (!Kn || !Vn)))
+    return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(Ck) || !al16(Cv) || !al16(bias) || !al16(out) || !al16(lse) ||
+      (keypos && !al16(keypos)) || (nvalid && !al16(nvalid)) || (lse_cmp && !al16(lse_cmp)) ||
+      (m > 0 && (!al16(Kn) || !al16(Vn))) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  const CacheWs w = cache_ws(p, m);
+  if (!ws || ws_bytes < w.total) return AM_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  char* c = (char*)ws;
+  void* vt = c;                 c += w.vt;
+  int2* tstat = (int2*)c;       c += w.tstat;
+  float* bias_eff = (float*)c;  c += w.bias;
+  float* lse1 = (float*)c;      c += w.lse1;
+  void* vt_new = c;             c += w.vt_new;
+  float* O2 = (float*)c;        c += w.o2;
+  float* lse2 = (float*)c;
+  if (lse_cmp) lse1 = lse_cmp;
+  hipError_t e = hipSuccess;
+  if (nvalid) {
+    e = launch_mask_bias(bias, nvalid, bias_eff, (int)p->heads, (int)p->T, s);
+    if (e != hipSuccess) return AM_ERR_DEVICE;
+  }
+  CmpAttnArgs ca;
+  ca.Q = Q; ca.Ck = Ck; ca.Cv = Cv; ca.bias = nvalid ? bias_eff : bias;
+  ca.keypos = p->causal ? keypos : nullptr; ca.Y = nullptr;
+  ca.Vt = vt; ca.tstat = p->causal ? tstat : nullptr;
+  ca.lse = lse1; ca.rowstat = nullptr; ca.O = out; ca.rowres = nullptr;
+  ca.heads = (int)p->heads; ca.n = (int)p->n; ca.t = (int)p->T; ca.d = (int)p->d;
+  ca.group = p->group; ca.causal = p->causal != 0; ca.bf16 = p->dtype == AM_BF16;
+  ca.scale = p->scale; ca.stream = s;
+  if ((e = launch_cmp_attention(ca)) != hipSuccess) return AM_ERR_DEVICE;
+  if (m > 0) {
+    TargetsArgs ta;
+    ta.Q = Q; ta.K = Kn; ta.V = Vn; ta.Vt = vt_new; ta.rowstat = nullptr;
+    ta.lse = lse2; ta.O = O2; ta.score = nullptr; ta.mode = 0;
+    ta.heads = (int)p->heads; ta.n = (int)p->n; ta.T = (int)m; ta.d = (int)p->d;
+    ta.group = p->group; ta.causal = new_causal != 0; ta.bf16 = p->dtype == AM_BF16;
+    ta.scale = p->scale; ta.stream = s;
+    if ((e = launch_targets(ta)) != hipSuccess) return AM_ERR_DEVICE;
+  }
+  MergeArgs ma;
+  ma.O1 = out; ma.lse1 = lse1; ma.O2 = m > 0 ? O2 : nullptr; ma.lse2 = m > 0 ? lse2 : nullptr;
+  ma.out = out; ma.lse = lse; ma.rows = (long long)p->heads * p->n; ma.d = (int)p->d;
+  ma.stream = s;
+  return from_hip(launch_attention_merge(ma));
+}
+
+am_status am_attention_merge(int64_t rows, int64_t d, const float* O1, const float* lse1,
+                             const float* O2, const float* lse2, float* out, float* lse_out,
+                             am_stream_t stream) {
+  if (rows < 0 || d < 4 || d % 4 != 0) return AM_ERR_INVALID_ARG;
+  if (rows > ((int64_t)1 << 40) || d > (1 << 20)) return AM_ERR_UNSUPPORTED;
+  if (!O1 || !lse1 || !O2 || !lse2 || !out || !lse_out) return AM_ERR_INVALID_ARG;
+  if (!al16(O1) || !al16(O2) || !al16(out) || (((uintptr_t)lse1 | (uintptr_t)lse2 |
+      (uintptr_t)lse_out) & 3u))
+    return AM_ERR_INVALID_ARG;
+  MergeArgs ma;
+  ma.O1 = O1; ma.lse1 = lse1; ma.O2 = O2; ma.lse2 = lse2; ma.out = out; ma.lse = lse_out;
+  ma.rows = (long long)rows; ma.d = (int)d; ma.stream = (hipStream_t)stream;
+  return from_hip(launch_attention_merge(ma));
 }
 
 }  // extern "C"

@@ -49,6 +49,18 @@ hipError_t launch_cmp_attention(const CmpAttnArgs& a);
 size_t cmp_vt_bytes(int64_t heads, int64_t t, int64_t d, int esize);
 size_t cmp_tstat_bytes(int64_t heads, int64_t t);
 
+// Log-space merge of two attention results (rows of d floats, d % 4 == 0); O2 may be null.
+struct MergeArgs {
+  const float* O1; const float* lse1; const float* O2; const float* lse2;
+  float* out; float* lse;
+  long long rows; int d;
+  hipStream_t stream;
+};
+hipError_t launch_attention_merge(const MergeArgs& a);
+// bias with the slots j >= nvalid[h] set to -inf
+hipError_t launch_mask_bias(const float* bias, const int32_t* nvalid, float* out, int heads,
+                            int t, hipStream_t st);
+
 struct SelectArgs {
   const float* score; const void* K; const void* V;
   int32_t* idx; void* Ck; void* Vsel;

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
     if (BIASED && tid < BN) {
       const int kr = min(k0 + tid, Tk - 1);
       breg = p.bias[(size_t)head * Tk + kr] * kLog2e;
-      preg = p.keypos[(size_t)head * Tk + kr];
+      if (CAUSAL) preg = p.keypos[(size_t)head * Tk + kr];   // positions only mask causal rows
     }
   };
   auto sstore = [&](int buf) {
@@ -274,7 +274,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
     const bool need = tmax > m + kLazyTau;
     if (__ballot(need)) {
       const float mnew = need ? tmax : m;
-      const float alpha = ex2(m - mnew);   // 0 when m was -inf, 1 when unchanged
+      // 0 when m was -inf, 1 when unchanged (also for a row that has seen no entry yet)
+      const float alpha = m == mnew ? 1.f : ex2(m - mnew);
       l *= alpha;
       if constexpr (WITH_O) {
 #pragma unroll
@@ -623,6 +624,71 @@ static hipError_t launch_cmp_t(const CmpAttnArgs& a) {
   fp.n = a.n; fp.Tk = a.t; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
   fp.c2 = a.scale * kLog2e;
   launch_flash<T, D, true>(fp, a.causal, a.Cv != nullptr, a.stream);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// Log-space merge of two attention results over disjoint entry sets, and slot masking
+// ------------------------------------------------------------------------------------
+// out = e^{l1 - L} O1 + e^{l2 - L} O2 with L = logaddexp(l1, l2) ("Latent Compaction with
+// Test-Time Training", §3.1 Eq. 5, normalizers and weights in log space). One thread per
+// four floats of a row; rows where both normalizers are -inf become -inf and zeros. O2
+// null: out = O1 and L = l1. out and O1 (or O2) may be the same buffer: each thread reads
+// its four floats of both inputs before writing them.
+__global__ __launch_bounds__(256) void merge_kernel(const float* O1, const float* __restrict__ l1,
+                                                    const float* O2, const float* __restrict__ l2,
+                                                    float* out, float* lse_out, long long rows,
+                                                    int d4) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= rows * d4) return;
+  const long long row = e / d4;
+  const int c = (int)(e - row * d4);
+  const float a = l1[row];
+  const float b = O2 ? l2[row] : -INFINITY;
+  const float mx = fmaxf(a, b);
+  float L = -INFINITY, w1 = 0.f, w2 = 0.f;
+  if (mx > -INFINITY) {
+    const float ea = expf(a - mx), eb = expf(b - mx);
+    L = mx + logf(ea + eb);
+    w1 = ea / (ea + eb);
+    w2 = eb / (ea + eb);
+  }
+  const float4 x = reinterpret_cast<const float4*>(O1 + row * d4 * 4)[c];
+  float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (O2) y = reinterpret_cast<const float4*>(O2 + row * d4 * 4)[c];
+  float4 r;
+  r.x = w1 * x.x + w2 * y.x;
+  r.y = w1 * x.y + w2 * y.y;
+  r.z = w1 * x.z + w2 * y.z;
+  r.w = w1 * x.w + w2 * y.w;
+  if (O2 || mx == -INFINITY) reinterpret_cast<float4*>(out + row * d4 * 4)[c] = r;
+  else if (out != O1) reinterpret_cast<float4*>(out + row * d4 * 4)[c] = x;
+  if (c == 0) lse_out[row] = O2 ? L : a;
+}
+
+hipError_t launch_attention_merge(const MergeArgs& a) {
+  const long long d4 = a.d / 4, nthr = a.rows * d4;
+  if (nthr == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, a.stream,
+                     a.O1, a.lse1, a.O2, a.lse2, a.out, a.lse, a.rows, (int)d4);
+  return hipGetLastError();
+}
+
+// bias_eff[h, j] = bias[h, j] for j < nvalid[h] (clamped to [0, t]), else -inf: padded slots
+// take no weight (the pseudocode's slot mask of the compacted branch).
+__global__ __launch_bounds__(256) void mask_bias_kernel(const float* __restrict__ bias,
+                                                        const int32_t* __restrict__ nvalid,
+                                                        float* __restrict__ out, int t) {
+  const int head = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= t) return;
+  const int nv = min(max(nvalid[head], 0), t);
+  out[(size_t)head * t + j] = j < nv ? bias[(size_t)head * t + j] : -INFINITY;
+}
+
+hipError_t launch_mask_bias(const float* bias, const int32_t* nvalid, float* out, int heads,
+                            int t, hipStream_t st) {
+  hipLaunchKernelGGL(mask_bias_kernel, dim3((t + 255) / 256, heads), dim3(256), 0, st, bias,
+                     nvalid, out, t);
   return hipGetLastError();
 }
 

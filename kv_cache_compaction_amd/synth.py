@@ -103,3 +103,42 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+def make_cache_case(seed: int, heads: int, n: int, T: int, t: int, m: int, d: int,
+                    dtype: str = "bf16", ragged: bool = True):
+    """A compacted cache and appended entries for the cache-attention calls (random draws).
+
+    Per head: keys and queries follow the recipe above on a T-key document; the slots are a
+    sorted random subset of t document positions (position 0 always kept), with values
+    Cv ~ N(0, 1) and biases ~ N(0, 0.5^2) in float32 (stand-ins for fitted ones); nvalid is
+    drawn in [t / 2, t] when ragged (else t); m new entries follow the same key/value
+    recipe. Returns Q [h, n, d], Ck [h, t, d], Cv, bias, keypos, nvalid, Kn, Vn [h, m, d];
+    Q, Ck, Kn, Vn in the input dtype (uint16 bf16 bits for "bf16").
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED0, 7, seed])))
+    Q = np.empty((heads, n, d), np.float32)
+    Ck = np.empty((heads, t, d), np.float32)
+    Kn = np.empty((heads, m, d), np.float32)
+    Vn = rng.standard_normal((heads, m, d), dtype=np.float32)
+    Cv = rng.standard_normal((heads, t, d), dtype=np.float32)
+    bias = (0.5 * rng.standard_normal((heads, t))).astype(np.float32)
+    keypos = np.empty((heads, t), np.int32)
+    nvalid = np.full(heads, t, np.int32)
+    for h in range(heads):
+        s = rng.lognormal(0.0, 0.5, size=d).astype(np.float32)
+        K = rng.standard_normal((T, d), dtype=np.float32) * s
+        pos = np.sort(rng.choice(np.arange(1, T), size=t - 1, replace=False)) if t > 1 else \
+            np.zeros(0, np.int64)
+        keypos[h] = np.concatenate([[0], pos]).astype(np.int32)
+        Ck[h] = K[keypos[h]]
+        Kn[h] = rng.standard_normal((m, d), dtype=np.float32) * s
+        Q[h] = rng.standard_normal((n, d), dtype=np.float32)
+        half = rng.permutation(n)[: n // 2]
+        Q[h, half] = K[rng.integers(0, T, size=half.size)] + \
+            np.float32(0.5) * rng.standard_normal((half.size, d), dtype=np.float32)
+        if ragged:
+            nvalid[h] = rng.integers(max(1, t // 2), t + 1)
+    if dtype == "bf16":
+        Q, Ck, Kn, Vn = (bf16_bits(x) for x in (Q, Ck, Kn, Vn))
+    return Q, Ck, Cv, bias, keypos, nvalid, Kn, Vn

@@ -383,27 +383,29 @@ def combine_attention(out1, logz1, out2, logz2):
 
 
 def cache_attention(Q, Ck, Cv, bias, scale, keypos=None, nvalid=None, causal=False, group=1,
-                    Kn=None, Vn=None, new_causal=True):
+                    Kn=None, Vn=None, new_causal=True, rows=None):
     """Attention of queries Q through a compacted cache (Ck, Cv, bias) and optional new
     entries (Kn, Vn) appended after it.
 
     Document slot j is valid when j < nvalid and, for causal problems, when its original
     position keypos[j] <= i // group. New entry j is visible to query i when
-    j <= i // group (new_causal) or always. Returns (out [n, d], log Z [n], log Z_cmp [n]).
+    j <= i // group (new_causal) or always. `rows` gives the query indices of the rows of Q
+    when Q is a subset. Returns (out [n, d], log Z [n], log Z_cmp [n]).
     """
     n = np.asarray(Q).shape[0]
     t = np.asarray(Ck).shape[0]
+    rows = np.arange(n) if rows is None else np.asarray(rows)
     slots = np.arange(t)
     valid = np.ones((n, t), dtype=bool)
     if nvalid is not None:
         valid &= (slots < nvalid)[None, :]
     if causal:
-        valid &= visible(np.arange(n), np.asarray(keypos), True, group)
+        valid &= visible(rows, np.asarray(keypos), True, group)
     out1, lz1 = branch_attention(Q, Ck, Cv, bias, valid, scale)
     if Kn is None or np.asarray(Kn).shape[0] == 0:
         return out1, lz1.copy(), lz1
     m = np.asarray(Kn).shape[0]
-    nvis = visible(np.arange(n), np.arange(m), bool(new_causal), group)
+    nvis = visible(rows, np.arange(m), bool(new_causal), group)
     out2, lz2 = branch_attention(Q, Kn, Vn, None, nvis, scale)
     out, lz = combine_attention(out1, lz1, out2, lz2)
     return out, lz, lz1
