@@ -85,6 +85,15 @@ typedef struct {
   am_dtype dtype;  /* dtype of Q, K, V and C_k */
 } am_problem;
 
+/* How am_compact_head sets beta: NNLS on the mass equations (blog §Choosing beta, the
+ * Attention Matching fit), or uniform redistribution of the missing mass (same section,
+ * the fast variant; see am_beta_redistribute). */
+typedef enum { AM_BETA_NNLS = 0, AM_BETA_REDISTRIBUTE = 1 } am_beta_mode;
+
+/* How am_compact_head sets C_v: ridge least squares on the output equations (blog
+ * §Choosing C_v), or the selected keys' own values C_v = V[idx] ("direct", same section). */
+typedef enum { AM_VALUES_FIT = 0, AM_VALUES_DIRECT = 1 } am_value_mode;
+
 typedef struct {
   am_score_mode score;   /* key selection statistic (default RMS) */
   am_mass_mode mass;     /* mass-equation weighting (default RELATIVE) */
@@ -92,6 +101,8 @@ typedef struct {
   int32_t nnls_max_iter; /* projected-gradient iterations cap (default 500) */
   float nnls_tol;        /* relative KKT tolerance (default 1e-6) */
   float ridge_lambda;    /* absolute ridge on A^T A (default 1e-3) */
+  am_beta_mode beta;     /* default AM_BETA_NNLS */
+  am_value_mode values;  /* default AM_VALUES_FIT */
 } am_options;
 
 /* Fills *opt with the defaults listed above. */
@@ -150,11 +161,43 @@ am_status am_fit_values_ols(const am_problem* p, const void* Q, const void* Ck,
                             am_stream_t stream);
 
 /*
+ * am_beta_redistribute - beta without a fit: uniform redistribution of the missing mass
+ * ("Compaction" blog, §Choosing beta). With m_j = (1/n) sum_i exp(s_i,c_j) over the
+ * queries that see compacted key j and Delta = (1/n) sum_i Z_i - sum_j m_j, where
+ * Z_i = exp(lse_i) is query i's mass over the reference key set (lse from am_targets, or
+ * over a shortlist), beta_j = log((m_j + Delta / t) / m_j): every selected key receives the
+ * same share of the mass the compacted keys miss. A key with m_j = 0 in fp32 on the common
+ * scale exp(s - max_i lse_i) gets +inf (0 when Delta <= 0). Optional outputs: w = exp(beta),
+ * mass_resid[h] as for am_fit_beta_nnls. idx ascending as am_select_keys returns it.
+ */
+am_status am_beta_redistribute(const am_problem* p, const void* Q, const void* Ck,
+                               const int32_t* idx, const float* lse, int64_t t, float* beta,
+                               float* w, float* mass_resid, void* ws, size_t ws_bytes,
+                               am_stream_t stream);
+
+/*
+ * am_eval_residuals - quality of a compacted cache on a set of queries (for instance a
+ * held-out set; "Compaction" blog, §Choosing beta and §Choosing C_v report errors on
+ * held-out queries): the full-cache targets of Q against K, V, then
+ *   resid_out[0, h] = mean_i (Z_cmp,i / Z_i - 1)^2                 (mass)
+ *   resid_out[1, h] = sum_i ||A_cmp(q_i) - O_i||^2 / sum_i ||O_i||^2 (output)
+ * with Z_cmp and A_cmp the biased compacted attention (Latent Compaction Eq. 2-4) of
+ * (idx, Ck, beta, Cv). p describes the queries and the full cache (p->n queries, p->T
+ * keys; causal problems need n == group * T).
+ */
+am_status am_eval_residuals(const am_problem* p, const void* Q, const void* K, const void* V,
+                            const int32_t* idx, const void* Ck, const float* beta,
+                            const float* Cv, int64_t t, float* resid_out, void* ws,
+                            size_t ws_bytes, am_stream_t stream);
+
+/*
  * am_compact_head - the whole path per head (the per-layer map over H heads of "The
  * Optimization Landscape of Learning Compacted Context Models", §2 Eq. 1): targets ->
  * selection -> beta -> C_v. Outputs idx, C_k, beta, C_v; optional lse_out, O_out,
  * score_out (full-cache statistics), resid_out[2, h] (row 0: mass residuals, row 1: output
- * residuals, as defined for the two fit calls) and head_status[h].
+ * residuals, as defined for the two fit calls) and head_status[h]. opt->beta and
+ * opt->values choose the fits or the blog's fast variants (redistributed beta, direct
+ * values); the fast variants skip the Gram builds and solves they replace.
  */
 am_status am_compact_head(const am_problem* p, const void* Q, const void* K, const void* V,
                           int64_t t, const am_options* opt, int32_t* idx, void* Ck,
@@ -210,7 +253,9 @@ typedef enum {
   AM_CALL_FIT_BETA = 2,
   AM_CALL_FIT_VALUES = 3,
   AM_CALL_COMPACT = 4,
-  AM_CALL_CACHE_ATTENTION = 5  /* the budget argument of am_workspace_bytes is m */
+  AM_CALL_CACHE_ATTENTION = 5, /* the budget argument of am_workspace_bytes is m */
+  AM_CALL_BETA_REDIST = 6,
+  AM_CALL_EVAL = 7
 } am_call;
 
 /* Workspace bytes a call needs for problem p and budget t (0 if the problem is invalid). */

@@ -20,8 +20,11 @@ AM_OK, AM_ERR_INVALID_ARG, AM_ERR_UNSUPPORTED, AM_ERR_WORKSPACE, AM_ERR_DEVICE =
 AM_F32, AM_BF16 = 0, 1
 SCORE_MODES = {"rms": 0, "mean": 1, "max": 2}
 MASS_MODES = {"relative": 0, "absolute": 1}
-CALL_TARGETS, CALL_SELECT, CALL_FIT_BETA, CALL_FIT_VALUES, CALL_COMPACT, CALL_CACHE_ATTENTION = \
-    range(6)
+(CALL_TARGETS, CALL_SELECT, CALL_FIT_BETA, CALL_FIT_VALUES, CALL_COMPACT, CALL_CACHE_ATTENTION,
+ CALL_BETA_REDIST, CALL_EVAL) = range(8)
+BETA_MODES = {"nnls": 0, "redistribute": 1}
+VALUE_MODES = {"fit": 0, "direct": 1}
+ABI_VERSION = 2
 HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE = 1, 2, 4
 
 
@@ -34,7 +37,8 @@ class AmProblem(ctypes.Structure):
 class AmOptions(ctypes.Structure):
     _fields_ = [("score", ctypes.c_int), ("mass", ctypes.c_int), ("w_lo", ctypes.c_float),
                 ("w_hi", ctypes.c_float), ("nnls_max_iter", ctypes.c_int32),
-                ("nnls_tol", ctypes.c_float), ("ridge_lambda", ctypes.c_float)]
+                ("nnls_tol", ctypes.c_float), ("ridge_lambda", ctypes.c_float),
+                ("beta", ctypes.c_int), ("values", ctypes.c_int)]
 
 
 class AmError(RuntimeError):
@@ -68,6 +72,10 @@ _PROTOS = {
                                           _P, ctypes.c_size_t, _P]),
     "am_attention_merge": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
                                           _P]),
+    "am_beta_redistribute": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P,
+                                            ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "am_eval_residuals": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -152,9 +160,9 @@ def make_problem(Q, K, *, causal=False, group=1, scale=None) -> AmProblem:
 
 
 def make_options(score="rms", mass="relative", w_lo=0.0, w_hi=math.inf, nnls_max_iter=500,
-                 nnls_tol=1e-6, ridge_lambda=1e-3) -> AmOptions:
+                 nnls_tol=1e-6, ridge_lambda=1e-3, beta="nnls", values="fit") -> AmOptions:
     return AmOptions(SCORE_MODES[score], MASS_MODES[mass], w_lo, w_hi, nnls_max_iter, nnls_tol,
-                     ridge_lambda)
+                     ridge_lambda, BETA_MODES[beta], VALUE_MODES[values])
 
 
 def workspace_bytes(p: AmProblem, t: int, which: int) -> int:
@@ -340,3 +348,44 @@ def attention_merge(O1, lse1, O2, lse2, *, out=None, lse_out=None):
     _check(lib().am_attention_merge(rows, d, _ptr(O1), _ptr(lse1), _ptr(O2), _ptr(lse2), _ptr(out),
                                     _ptr(lse_out), _stream()), "am_attention_merge")
     return out, lse_out
+
+
+def beta_redistribute(Q, Ck, idx, lse, *, causal=False, group=1, scale=None, T=None):
+    """beta by uniform redistribution of the missing mass; returns (beta, w, mass_resid).
+    T (full-cache keys) is only used to describe the problem (causal needs n == group * T)."""
+    torch = _torch()
+    _need(Q, "Q"); _need(Ck, "Ck")
+    h, n, d = Q.shape
+    t = Ck.shape[1]
+    _need(idx, "idx", dtype=torch.int32, shape=(h, t))
+    _need(lse, "lse", dtype=torch.float32, shape=(h, n))
+    T = T if T is not None else (n // group if causal else max(t, 1))
+    p = AmProblem(h, n, T, d, int(bool(causal)), int(group),
+                  float(1.0 / math.sqrt(d) if scale is None else scale), _dtype_code(Q))
+    dev = Q.device
+    beta = torch.empty((h, t), dtype=torch.float32, device=dev)
+    w = torch.empty((h, t), dtype=torch.float32, device=dev)
+    res = torch.empty((h,), dtype=torch.float32, device=dev)
+    ws, nb = _workspace(p, t, CALL_BETA_REDIST, dev)
+    _check(lib().am_beta_redistribute(ctypes.byref(p), _ptr(Q), _ptr(Ck), _ptr(idx), _ptr(lse), t,
+                                      _ptr(beta), _ptr(w), _ptr(res), _ptr(ws), nb, _stream()),
+           "am_beta_redistribute")
+    return beta, w, res
+
+
+def eval_residuals(Q, K, V, idx, Ck, beta, Cv, *, causal=False, group=1, scale=None):
+    """[2, h] mass and output residuals of a compacted cache on the queries Q."""
+    torch = _torch()
+    _need(Q, "Q"); _need(K, "K"); _need(V, "V", dtype=K.dtype, shape=K.shape)
+    p = make_problem(Q, K, causal=causal, group=group, scale=scale)
+    h, t, d = p.heads, Ck.shape[1], p.d
+    _need(Ck, "Ck", dtype=Q.dtype, shape=(h, t, d))
+    _need(idx, "idx", dtype=torch.int32, shape=(h, t))
+    _need(beta, "beta", dtype=torch.float32, shape=(h, t))
+    _need(Cv, "Cv", dtype=torch.float32, shape=(h, t, d))
+    res = torch.empty((2, h), dtype=torch.float32, device=Q.device)
+    ws, nb = _workspace(p, t, CALL_EVAL, Q.device)
+    _check(lib().am_eval_residuals(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(Ck),
+                                   _ptr(beta), _ptr(Cv), t, _ptr(res), _ptr(ws), nb, _stream()),
+           "am_eval_residuals")
+    return res

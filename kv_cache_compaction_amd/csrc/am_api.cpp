@@ -11,7 +11,7 @@ using namespace amc;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -49,6 +49,8 @@ am_status check_opts(const am_options* o) {
   if (o->nnls_max_iter < 1 || !(o->nnls_tol >= 0.f) || !(o->ridge_lambda >= 0.f) ||
       !isfinite(o->ridge_lambda))
     return AM_ERR_INVALID_ARG;
+  if (o->beta != AM_BETA_NNLS && o->beta != AM_BETA_REDISTRIBUTE) return AM_ERR_INVALID_ARG;
+  if (o->values != AM_VALUES_FIT && o->values != AM_VALUES_DIRECT) return AM_ERR_INVALID_ARG;
   return AM_OK;
 }
 
@@ -95,6 +97,9 @@ CacheWs cache_ws(const am_problem* p, int64_t m) {
   return w;
 }
 
+size_t ws_fast(const am_problem* p, int64_t t, int64_t T_eval) {
+  return fast_ws_bytes(p->heads, p->n, t, p->d, esize(p), T_eval);
+}
 size_t ws_compact(const am_problem* p, int64_t t) {
   // lse, O and score live in the workspace when the caller does not want them
   const size_t own = align_up((size_t)p->heads * p->n * 4) +
@@ -103,6 +108,8 @@ size_t ws_compact(const am_problem* p, int64_t t) {
   size_t fit = ws_fit_beta(p, t);
   const size_t fv = ws_fit_values(p, t);
   if (fv > fit) fit = fv;
+  const size_t ff = ws_fast(p, t, 0);
+  if (ff > fit) fit = ff;
   size_t stage = ws_targets(p);
   if (fit > stage) stage = fit;
   return own + stage;
@@ -159,6 +166,8 @@ void am_default_options(am_options* o) {
   o->nnls_max_iter = 500;
   o->nnls_tol = 1e-6f;
   o->ridge_lambda = 1e-3f;
+  o->beta = AM_BETA_NNLS;
+  o->values = AM_VALUES_FIT;
 }
 
 size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
@@ -174,6 +183,9 @@ size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
     case AM_CALL_FIT_BETA: return t > kMaxFitT ? 0 : ws_fit_beta(p, t);
     case AM_CALL_FIT_VALUES: return t > kMaxFitT ? 0 : ws_fit_values(p, t);
     case AM_CALL_COMPACT: return t > kMaxFitT ? 0 : ws_compact(p, t);
+    case AM_CALL_BETA_REDIST: return ws_fast(p, t, 0);
+    case AM_CALL_EVAL: return ws_fast(p, t, p->T);
+    case AM_CALL_CACHE_ATTENTION: return 0;
   }
   return 0;
 }
@@ -296,16 +308,60 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
   fa.w_lo = opt->w_lo; fa.w_hi = opt->w_hi; fa.tol = opt->nnls_tol;
   fa.max_iter = opt->nnls_max_iter;
   fa.lambda = opt->ridge_lambda;
-  fa.keep_cmp_stats = true;
-  if ((e = launch_fit_beta(fa)) != hipSuccess) return AM_ERR_DEVICE;
+  const bool redist = opt->beta == AM_BETA_REDISTRIBUTE;
+  if (redist) {
+    if (head_status && (e = launch_zero_status(head_status, (int)p->heads, s)) != hipSuccess)
+      return AM_ERR_DEVICE;
+    if ((e = launch_beta_redistribute(fa)) != hipSuccess) return AM_ERR_DEVICE;
+  } else {
+    fa.keep_cmp_stats = true;
+    if ((e = launch_fit_beta(fa)) != hipSuccess) return AM_ERR_DEVICE;
+  }
   fa.keep_cmp_stats = false;
-  fa.have_cmp_stats = true;
+  fa.have_cmp_stats = !redist;   // the NNLS path left the compacted row statistics
   fa.beta_in = beta; fa.O = O; fa.Cv = Cv;
   fa.mass_resid = nullptr;
   fa.keep_status = true;
   fa.out_resid = resid_out ? resid_out + p->heads : nullptr;
-  if ((e = launch_fit_values(fa)) != hipSuccess) return AM_ERR_DEVICE;
-  return AM_OK;
+  if (opt->values == AM_VALUES_DIRECT)
+    e = launch_values_direct(fa, V, (int)p->T);
+  else
+    e = launch_fit_values(fa);
+  return e == hipSuccess ? AM_OK : AM_ERR_DEVICE;
+}
+
+am_status am_beta_redistribute(const am_problem* p, const void* Q, const void* Ck,
+                               const int32_t* idx, const float* lse, int64_t t, float* beta,
+                               float* w, float* mass_resid, void* ws, size_t ws_bytes,
+                               am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if (!Q || !Ck || !idx || !lse || !beta) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(Ck) || !al16(idx) || !al16(lse) || !al16(beta) || (w && !al16(w)) ||
+      (mass_resid && !al16(mass_resid)) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_fast(p, t, 0)) return AM_ERR_WORKSPACE;
+  FitArgs a = fit_args(p, Q, Ck, idx, t, ws, ws_bytes, (hipStream_t)stream);
+  a.lse = lse; a.beta = beta; a.w = w; a.mass_resid = mass_resid;
+  return from_hip(launch_beta_redistribute(a));
+}
+
+am_status am_eval_residuals(const am_problem* p, const void* Q, const void* K, const void* V,
+                            const int32_t* idx, const void* Ck, const float* beta,
+                            const float* Cv, int64_t t, float* resid_out, void* ws,
+                            size_t ws_bytes, am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if (!Q || !K || !V || !idx || !Ck || !beta || !Cv || !resid_out) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(K) || !al16(V) || !al16(idx) || !al16(Ck) || !al16(beta) || !al16(Cv) ||
+      !al16(resid_out) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_fast(p, t, p->T)) return AM_ERR_WORKSPACE;
+  FitArgs a = fit_args(p, Q, Ck, idx, t, ws, ws_bytes, (hipStream_t)stream);
+  a.beta_in = beta; a.Cv = (float*)Cv;
+  return from_hip(launch_eval_residuals(a, K, V, (int)p->T, resid_out));
 }
 
 am_status am_cache_attention(const am_problem* p, const void* Q, const void* Ck, const float* Cv,

@@ -49,6 +49,19 @@ hipError_t launch_cmp_attention(const CmpAttnArgs& a);
 size_t cmp_vt_bytes(int64_t heads, int64_t t, int64_t d, int esize);
 size_t cmp_tstat_bytes(int64_t heads, int64_t t);
 
+// Per-key masses m_j = (1/n) sum over queries i that see key j of exp(scale q_i . Ck_j -
+// shift_h), shift2[h] = shift_h log2(e), in log form: log2 m_j = kmax_j + log2 kmean_j
+// (keys carry original positions keypos[h, t])
+struct KeyMassArgs {
+  const void* Q; const void* Ck; const int32_t* keypos; const float* shift2;
+  float* kmax; float* kmean;
+  int heads, n, t, d, group;
+  bool causal, bf16;
+  float scale;
+  hipStream_t stream;
+};
+hipError_t launch_key_mass(const KeyMassArgs& a);
+
 // Log-space merge of two attention results (rows of d floats, d % 4 == 0); O2 may be null.
 struct MergeArgs {
   const float* O1; const float* lse1; const float* O2; const float* lse2;
@@ -113,6 +126,20 @@ struct SyrkGramArgs {
   hipStream_t stream;
 };
 hipError_t launch_syrk_gram(const SyrkGramArgs& a);
+
+// Fast variants and evaluation (workspace: fast_ws_bytes; T_eval = keys of the full cache
+// for the evaluation, else 0).
+// beta by uniform redistribution from a.lse (writes a.beta, a.w, a.mass_resid if set)
+hipError_t launch_beta_redistribute(const FitArgs& a);
+// C_v = V[idx] in f32 (a.Cv); a.out_resid against a.O with a.beta_in if set
+hipError_t launch_values_direct(const FitArgs& a, const void* V, int T);
+// resid[0, h]: mass residual, resid[1, h]: output residual of (a.idx, a.Ck, a.beta_in, a.Cv)
+// on the queries a.Q against the full cache K, V (T keys)
+hipError_t launch_eval_residuals(const FitArgs& a, const void* K, const void* V, int T,
+                                 float* resid);
+size_t fast_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d, int esize, int64_t T_eval);
+
+hipError_t launch_zero_status(int32_t* status, int heads, hipStream_t st);
 
 hipError_t launch_fit_beta(const FitArgs& a);
 hipError_t launch_fit_values(const FitArgs& a);

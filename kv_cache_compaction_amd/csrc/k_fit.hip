@@ -1763,4 +1763,240 @@ hipError_t launch_fit_values(const FitArgs& a) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------
+// Fast variants of the "Compaction" blog (no fits) and evaluation on other queries
+// ------------------------------------------------------------------------------------
+// Uniform redistribution (§Choosing beta): with m_j = (1/n) sum_i exp(s_i,c_j) over the
+// queries that see c_j and Delta = (1/n) sum_i Z_i - sum_j m_j, beta_j = log(1 +
+// Delta / (t m_j)). Every mass is taken on the common scale e^-C, C = max_i lse_i, which
+// cancels in beta; m_j comes from the column passes in log form (log2 m_j = kmax_j +
+// log2 kmean_j), and beta_j = logaddexp(log(Delta / t), log m_j) - log m_j, so keys of
+// mass far below the scale still get a finite bias. Delta, a mass by definition, is
+// clamped at 0 (a negative value is rounding).
+
+// per head: shift2 = C log2(e) and zsum = sum_i exp(lse_i - C)
+__global__ __launch_bounds__(256) void redist_prep_kernel(const float* __restrict__ lse, int n,
+                                                          float* __restrict__ shift2,
+                                                          double* __restrict__ zsum) {
+  __shared__ float red[4];
+  __shared__ double dred[256];
+  const int head = blockIdx.x, tid = threadIdx.x;
+  const float* l = lse + (size_t)head * n;
+  float mx = -INFINITY;
+  for (int i = tid; i < n; i += 256) mx = fmaxf(mx, l[i]);
+  mx = block_max(mx, red);
+  const float c2 = mx == -INFINITY ? 0.f : mx * kLog2e;
+  double acc = 0.0;
+  for (int i = tid; i < n; i += 256) acc += (double)ex2(__builtin_fmaf(l[i], kLog2e, -c2));
+  dred[tid] = acc;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (tid < s2) dred[tid] += dred[tid + s2];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    shift2[head] = c2;
+    zsum[head] = dred[0];
+  }
+}
+
+// beta (and w = e^beta) from the per-key masses in log form; a key that no query sees
+// (log mass -inf) gets +inf when there is mass to hand out, else 0
+__global__ __launch_bounds__(256) void redist_beta_kernel(const float* __restrict__ kmax,
+                                                          const float* __restrict__ kmean,
+                                                          const double* __restrict__ zsum, int n,
+                                                          int t, float* __restrict__ beta,
+                                                          float* __restrict__ w) {
+  __shared__ double dred[256];
+  const int head = blockIdx.x, tid = threadIdx.x;
+  const size_t o = (size_t)head * t;
+  auto lg2m = [&](int j) {   // log2 m_j on the common scale
+    const double mx = (double)kmax[o + j], me = (double)kmean[o + j];
+    return (mx == -INFINITY || !(me > 0.0)) ? -(double)INFINITY : mx + log2(me);
+  };
+  double acc = 0.0;
+  for (int j = tid; j < t; j += 256) acc += exp2(lg2m(j));
+  dred[tid] = acc;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (tid < s2) dred[tid] += dred[tid + s2];
+    __syncthreads();
+  }
+  const double delta = fmax(zsum[head] / (double)n - dred[0], 0.0);
+  const double la = delta > 0.0 ? log2(delta / (double)t) : -(double)INFINITY;
+  for (int j = tid; j < t; j += 256) {
+    const double lm = lg2m(j);
+    double b2;   // beta in log2 units
+    if (la == -INFINITY) b2 = 0.0;
+    else if (lm == -INFINITY) b2 = INFINITY;
+    else {
+      const double hi = fmax(la, lm), lo = fmin(la, lm);
+      b2 = hi + log2(1.0 + exp2(lo - hi)) - lm;
+    }
+    const double b = b2 * 0.69314718055994530942;
+    beta[o + j] = (float)b;
+    if (w) w[o + j] = (float)exp2(b2);
+  }
+}
+
+// Direct values (§Choosing C_v): C_v[h, j] = V[h, idx[h, j]] in f32. One thread per 4 values.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_f32_kernel(const T* __restrict__ V,
+                                                         const int32_t* __restrict__ idx,
+                                                         float* __restrict__ Cv, int Tk, int t,
+                                                         int d) {
+  const int head = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int d4 = d / 4;
+  if (e >= (long long)t * d4) return;
+  const int j = (int)(e / d4), c = (int)(e - (long long)j * d4) * 4;
+  const int src = min(max(idx[(size_t)head * t + j], 0), Tk - 1);
+  const T* v = V + ((size_t)head * Tk + src) * d + c;
+  float4 o;
+  o.x = (float)v[0];
+  o.y = (float)v[1];
+  o.z = (float)v[2];
+  o.w = (float)v[3];
+  *(float4*)(Cv + ((size_t)head * t + j) * d + c) = o;
+}
+
+struct FastPlan {
+  float* shift2h; double* zsum; float* kmax; float* kmean;   // redistribution
+  float2* rowstat_cmp; float* shift2; double2* part;     // mass residual
+  int2* tstat; void* Vt; float2* rowres;                 // output residual
+  float* lse; float* O; void* tws;                       // evaluation: targets on the queries
+  size_t bytes;
+};
+
+static FastPlan plan_fast(char* base, int64_t heads, int64_t n, int64_t t, int64_t d,
+                          int esize, int64_t T_eval) {
+  Carve c{base, 0};
+  FastPlan p;
+  p.shift2h = c.take<float>(heads);
+  p.zsum = c.take<double>(heads);
+  p.kmax = c.take<float>(heads * t);
+  p.kmean = c.take<float>(heads * t);
+  p.rowstat_cmp = c.take<float2>(heads * n);
+  p.shift2 = c.take<float>(heads * n);
+  p.part = c.take<double2>(heads * kResBlk);
+  p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
+  p.Vt = c.take<char>(cmp_vt_bytes(heads, t, d, esize));
+  p.rowres = c.take<float2>(heads * n);
+  p.lse = p.O = nullptr;
+  p.tws = nullptr;
+  if (T_eval > 0) {
+    p.lse = c.take<float>(heads * n);
+    p.O = c.take<float>((size_t)heads * n * d);
+    p.tws = c.take<char>(targets_ws_bytes(heads, n, T_eval, d, esize));
+  }
+  p.bytes = c.off;
+  return p;
+}
+
+size_t fast_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d, int esize, int64_t T_eval) {
+  return plan_fast(nullptr, heads, n, t, d, esize, T_eval).bytes;
+}
+
+// mass residual mean_i (Z_cmp,i / Z_i - 1)^2 of (idx, beta) on queries with log-normalizers lse
+static hipError_t mass_residual(const FitArgs& a, const float* lse, const float* beta,
+                                const FastPlan& pl, float* out) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads, n = a.n;
+  hipLaunchKernelGGL(shift_rows_kernel, dim3(cdiv(n, 256), H), dim3(256), 0, st, lse,
+                     (const float2*)nullptr, pl.shift2, n, 0);
+  CmpAttnArgs ca;
+  ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = beta; ca.keypos = a.idx; ca.Y = nullptr;
+  ca.Vt = nullptr; ca.tstat = pl.tstat;
+  ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
+  ca.heads = H; ca.n = n; ca.t = a.t; ca.d = a.d; ca.group = a.group; ca.causal = a.causal;
+  ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
+  const hipError_t e = launch_cmp_attention(ca);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mass_resid_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, pl.rowstat_cmp,
+                     pl.shift2, (const float*)nullptr, pl.part, n);
+  hipLaunchKernelGGL(resid_final_kernel, dim3(cdiv(H, 64)), dim3(64), 0, st,
+                     (const double2*)pl.part, out, H);
+  return hipGetLastError();
+}
+
+// output residual sum ||A C_v - Y||^2 / sum ||Y||^2 of (idx, beta, C_v) against targets Y
+static hipError_t output_residual(const FitArgs& a, const float* beta, const float* Cv,
+                                  const float* Y, const FastPlan& pl, float* out) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads, n = a.n;
+  CmpAttnArgs cr;
+  cr.Q = a.Q; cr.Ck = a.Ck; cr.Cv = Cv; cr.bias = beta; cr.keypos = a.idx; cr.Y = Y;
+  cr.Vt = pl.Vt; cr.tstat = pl.tstat;
+  cr.lse = nullptr; cr.rowstat = nullptr; cr.O = nullptr; cr.rowres = pl.rowres;
+  cr.heads = H; cr.n = n; cr.t = a.t; cr.d = a.d; cr.group = a.group; cr.causal = a.causal;
+  cr.bf16 = a.bf16; cr.scale = a.scale; cr.stream = st;
+  const hipError_t e = launch_cmp_attention(cr);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(out_resid_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, pl.rowres,
+                     pl.part, n);
+  hipLaunchKernelGGL(resid_final_kernel, dim3(cdiv(H, 64)), dim3(64), 0, st,
+                     (const double2*)pl.part, out, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_status(int32_t* status, int heads, hipStream_t st) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(heads, 256)), dim3(256), 0, st, status, heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_beta_redistribute(const FitArgs& a) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads;
+  FastPlan pl = plan_fast((char*)a.ws, H, a.n, a.t, a.d, a.bf16 ? 2 : 4, 0);
+  hipLaunchKernelGGL(redist_prep_kernel, dim3(H), dim3(256), 0, st, a.lse, a.n, pl.shift2h,
+                     pl.zsum);
+  KeyMassArgs km;
+  km.Q = a.Q; km.Ck = a.Ck; km.keypos = a.idx; km.shift2 = pl.shift2h;
+  km.kmax = pl.kmax; km.kmean = pl.kmean;
+  km.heads = H; km.n = a.n; km.t = a.t; km.d = a.d; km.group = a.group; km.causal = a.causal;
+  km.bf16 = a.bf16; km.scale = a.scale; km.stream = st;
+  hipError_t e = launch_key_mass(km);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(redist_beta_kernel, dim3(H), dim3(256), 0, st, pl.kmax, pl.kmean, pl.zsum,
+                     a.n, a.t, a.beta, a.w);
+  if (a.mass_resid && (e = mass_residual(a, a.lse, a.beta, pl, a.mass_resid)) != hipSuccess)
+    return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_values_direct(const FitArgs& a, const void* V, int T) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads;
+  const dim3 g(cdiv((long long)a.t * (a.d / 4), 256), H);
+  if (a.bf16)
+    hipLaunchKernelGGL(gather_f32_kernel<bf16>, g, dim3(256), 0, st, (const bf16*)V, a.idx, a.Cv,
+                       T, a.t, a.d);
+  else
+    hipLaunchKernelGGL(gather_f32_kernel<float>, g, dim3(256), 0, st, (const float*)V, a.idx,
+                       a.Cv, T, a.t, a.d);
+  if (a.out_resid) {
+    FastPlan pl = plan_fast((char*)a.ws, H, a.n, a.t, a.d, a.bf16 ? 2 : 4, 0);
+    const hipError_t e = output_residual(a, a.beta_in, a.Cv, a.O, pl, a.out_resid);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_eval_residuals(const FitArgs& a, const void* K, const void* V, int T,
+                                 float* resid) {
+  const hipStream_t st = a.stream;
+  const int H = a.heads, n = a.n, d = a.d, es = a.bf16 ? 2 : 4;
+  FastPlan pl = plan_fast((char*)a.ws, H, n, a.t, d, es, T);
+  TargetsArgs ta;
+  ta.Q = a.Q; ta.K = K; ta.V = V; ta.Vt = pl.tws;
+  ta.rowstat = (char*)pl.tws + targets_vt_bytes(H, T, d, es);
+  ta.lse = pl.lse; ta.O = pl.O; ta.score = nullptr; ta.mode = 0;
+  ta.heads = H; ta.n = n; ta.T = T; ta.d = d; ta.group = a.group; ta.causal = a.causal;
+  ta.bf16 = a.bf16; ta.scale = a.scale; ta.stream = st;
+  hipError_t e = launch_targets(ta);
+  if (e != hipSuccess) return e;
+  if ((e = mass_residual(a, pl.lse, a.beta_in, pl, resid)) != hipSuccess) return e;
+  return output_residual(a, a.beta_in, a.Cv, pl.O, pl, resid + H);
+}
+
 }  // namespace amc

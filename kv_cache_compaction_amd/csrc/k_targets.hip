@@ -368,16 +368,24 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 // ------------------------------------------------------------------------------------
 // Column-score pass.
 // ------------------------------------------------------------------------------------
-// MODE: 0 = RMS (sum of p^2), 1 = MEAN (sum of p), 2 = MAX (max of p). Only the requested
+// MODE: 0 = RMS (sum of p^2), 1 = MEAN (sum of p), 2 = MAX (max of p), 3 = the log2 of
+// MAX (no final exponentiation, for masses far below the shift). Only the requested
 // statistic is computed: with the row shift u = m + log2 l, RMS exponentiates 2 (x - u)
 // directly (p^2; the doubling is exact) and MAX keeps the max of the exponent and
 // exponentiates once at the end.
 template <typename T, int D> constexpr int colscore_kb() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
 
-template <typename T, int D, int WAVES, bool CAUSAL, int MODE>
+// KPOS: the keys carry original positions keypos[h, Tk] (ascending; compacted keys) for the
+// causal mask instead of their index. head_shift (non-null): one shift per head, in log2
+// units, replaces the per-query row statistics (unnormalized masses on a common scale);
+// key_shift (KPOS only, non-null): a further per-key shift [h, Tk] in log2 units.
+template <typename T, int D, int WAVES, bool CAUSAL, int MODE, bool KPOS>
 __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float2* __restrict__ rowstat,
-    float* __restrict__ score, int n, int Tk, int group, float c2, int heads) {
+    float* __restrict__ score, int n, int Tk, int group, float c2, int heads,
+    const int32_t* __restrict__ keypos, const float* __restrict__ head_shift,
+    const float* __restrict__ key_shift) {
+  constexpr bool MAXM = MODE == 2 || MODE == 3;
   typedef typename V8<T>::type v8;
   constexpr int KB = colscore_kb<T, D>();  // 32-key blocks per wave
   constexpr int NT = WAVES * 64;
@@ -402,13 +410,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   const T* Qh = Q + (size_t)head * n * D;
   const T* Kh = K + (size_t)head * Tk * D;
   const float2* RSh = rowstat + (size_t)head * n;
+  const int32_t* KPh = KPOS ? keypos + (size_t)head * Tk : nullptr;
+  auto kpos = [&](int k) { return KPOS ? KPh[min(k, Tk - 1)] : k; };
 
   const int wk0 = k0 + wave * 32 * KB;
   v8 bk[KB][KC];
-  int key[KB];
+  int key[KB], kp[KB];
+  float ksh[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     key[kb] = wk0 + kb * 32 + r;
+    kp[kb] = kpos(key[kb]);
+    ksh[kb] = (KPOS && key_shift) ? key_shift[(size_t)head * Tk + min(key[kb], Tk - 1)] : 0.f;
     const int krow = min(key[kb], Tk - 1);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   }
 
   int qbeg = 0;
-  if (CAUSAL) qbeg = (min(n, k0 * group) / kBQ) * kBQ;
+  if (CAUSAL) qbeg = (min(n, kpos(k0) * group) / kBQ) * kBQ;
   const int ntiles = (n - qbeg + kBQ - 1) / kBQ;
 
   u32x4 qreg[QPT];
@@ -430,8 +443,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
       qreg[i] = *(const u32x4*)(Qh + (size_t)min(qt0 + row, n - 1) * D + col);
     }
     if (tid < kBQ) {
-      const float2 st = RSh[min(qt0 + tid, n - 1)];
-      rreg = f * (st.x + st.y);
+      if (head_shift) {
+        rreg = f * head_shift[head];
+      } else {
+        const float2 st = RSh[min(qt0 + tid, n - 1)];
+        rreg = f * (st.x + st.y);
+      }
     }
   };
   auto sstore = [&](int buf) {
@@ -484,18 +501,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        float part = MODE == 2 ? -INFINITY : 0.f;
+        float part = MAXM ? -INFINITY : 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           float e = __builtin_fmaf(s[kb][j], fc2, -sh[j]);
+          if (KPOS) e -= ksh[kb];
           if (MASK) {
             const int q = qt0 + qb * 32 + crow(j, hh);
-            e = (q < n && (!CAUSAL || key[kb] <= q / group)) ? e : -INFINITY;
+            e = (q < n && (!CAUSAL || kp[kb] <= q / group)) ? e : -INFINITY;
           }
-          if (MODE == 2) part = vmax(part, e);
+          if (MAXM) part = vmax(part, e);
           else part += ex2(e);
         }
-        if (MODE == 2) amx[kb] = vmax(amx[kb], part);
+        if (MAXM) amx[kb] = vmax(amx[kb], part);
         else acc[kb] += (double)part;
       }
     }
@@ -510,7 +528,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   __syncthreads();
   // leading tiles on the causal diagonal and a ragged last tile need the mask
   int nhead = 0;
-  if (CAUSAL) nhead = min(ntiles, max(0, (group * (wk0 + 32 * KB - 1) - qbeg + kBQ - 1) / kBQ));
+  if (CAUSAL) nhead = min(ntiles, max(0, (group * kpos(wk0 + 32 * KB - 1) - qbeg + kBQ - 1) / kBQ));
   int nbody = ntiles - ((qbeg + ntiles * kBQ > n) ? 1 : 0);
   nbody = max(nbody, nhead);
   for (int it = 0; it < nhead; ++it) tile_step(it, std::true_type{});
@@ -519,9 +537,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     float out;
-    if (MODE == 2) {
+    if (MAXM) {
       const float mx = vmax(amx[kb], shfl_xor32(amx[kb]));
-      out = ex2(mx);
+      out = MODE == 3 ? mx : ex2(mx);
     } else {
       const double tot = acc[kb] + __shfl_xor(acc[kb], 32, 64);
       out = MODE == 0 ? (float)sqrt(tot / (double)n) : (float)(tot / (double)n);
@@ -571,9 +589,10 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   const int BK = kScoreWaves * 32 * colscore_kb<T, D>();
   const dim3 gs(((a.T + BK - 1) / BK) * a.heads), bs(kScoreWaves * 64);
 #define AM_SCORE(C, M)                                                                          \
-  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M>), gs, bs, 0, a.stream,          \
+  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M, false>), gs, bs, 0, a.stream,   \
                      (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.n, a.T, \
-                     a.group, c2, a.heads)
+                     a.group, c2, a.heads, (const int32_t*)nullptr, (const float*)nullptr,     \
+                     (const float*)nullptr)
   if (a.causal) {
     if (a.mode == 0) AM_SCORE(true, 0); else if (a.mode == 1) AM_SCORE(true, 1); else AM_SCORE(true, 2);
   } else {
@@ -581,6 +600,34 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   }
 #undef AM_SCORE
   return hipGetLastError();
+}
+
+// Per-key masses of the compacted keys (original positions for the causal mask) in log
+// form: kmax = max_i (scale q_i.k_j log2 e - shift2_h) over the queries that see key j,
+// then kmean = (1/n) sum_i 2^(that exponent - kmax), so log2 m_j = kmax + log2 kmean holds
+// masses far below the common shift without underflow. Two column passes (MAX, MEAN).
+template <typename T, int D, bool C>
+static void launch_key_mass_c(const KeyMassArgs& a) {
+  const int BK = kScoreWaves * 32 * colscore_kb<T, D>();
+  const dim3 gs(((a.t + BK - 1) / BK) * a.heads), bs(kScoreWaves * 64);
+  const float c2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, 3, true>), gs, bs, 0, a.stream,
+                     (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, a.kmax, a.n, a.t,
+                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)nullptr);
+  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, 1, true>), gs, bs, 0, a.stream,
+                     (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, a.kmean, a.n, a.t,
+                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)a.kmax);
+}
+template <typename T, int D>
+static hipError_t launch_key_mass_t(const KeyMassArgs& a) {
+  if (a.causal) launch_key_mass_c<T, D, true>(a);
+  else launch_key_mass_c<T, D, false>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_mass(const KeyMassArgs& a) {
+  if (a.bf16) return a.d == 128 ? launch_key_mass_t<bf16, 128>(a) : launch_key_mass_t<bf16, 64>(a);
+  return a.d == 128 ? launch_key_mass_t<float, 128>(a) : launch_key_mass_t<float, 64>(a);
 }
 
 hipError_t launch_targets(const TargetsArgs& a) {

@@ -142,3 +142,21 @@ def make_cache_case(seed: int, heads: int, n: int, T: int, t: int, m: int, d: in
     if dtype == "bf16":
         Q, Ck, Kn, Vn = (bf16_bits(x) for x in (Q, Ck, Kn, Vn))
     return Q, Ck, Cv, bias, keypos, nvalid, Kn, Vn
+
+
+def make_heldout_queries(w: Workload, heads=None, K=None, seed: int = 1):
+    """A second query set for the same caches (held-out evaluation): the query recipe above
+    (half of the rows near random keys) from its own seeded stream. K is the batch's key
+    array as generated (bf16 bits or float32); returns Q [h, n, d] in the workload dtype."""
+    hs = range(w.heads) if heads is None else list(heads)
+    Kf = as_f64(K, w.dtype).astype(np.float32)
+    out = np.empty((len(hs), w.n, w.d), np.float32)
+    for i, h in enumerate(hs):
+        rng = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence([SEED0, 8, workload_index(w), h, seed])))
+        Q = rng.standard_normal((w.n, w.d), dtype=np.float32)
+        kd = rng.permutation(w.n)[: w.n // 2]
+        src = rng.integers(0, w.T, size=kd.size)
+        Q[kd] = Kf[i][src] + np.float32(0.5) * rng.standard_normal((kd.size, w.d), dtype=np.float32)
+        out[i] = Q
+    return bf16_bits(out) if w.dtype == "bf16" else out

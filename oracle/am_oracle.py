@@ -433,7 +433,9 @@ def redistribute_beta(Q, Ck, idx, lse, scale, causal=False, group=1):
         vis = visible(np.arange(a, b), np.asarray(idx), causal, group)
         e[a:b] = np.where(vis, np.exp(np.where(vis, s, 0.0) - c), 0.0)
     m = e.sum(axis=0) / n
-    delta = (np.exp(lse - c).sum() - e.sum()) / n
+    # Delta is a mass (the compacted keys are a subset of the reference set): a negative
+    # value can only be rounding, and is taken as 0
+    delta = max((np.exp(lse - c).sum() - e.sum()) / n, 0.0)
     return np.log((m + delta / t) / m)
 
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert amc.lib().am_abi_version() == 1
+    assert amc.lib().am_abi_version() == amc.ABI_VERSION == 2
     assert amc.status_str(0) == "ok"
     assert amc.status_str(-3) == "workspace too small"
     assert amc.status_str(7) == "unknown status"
@@ -40,6 +40,7 @@ def test_default_options():
     amc.lib().am_default_options(ctypes.byref(o))
     assert o.score == 0 and o.mass == 0 and o.w_lo == 0 and math.isinf(o.w_hi)
     assert o.nnls_max_iter == 500 and o.ridge_lambda == pytest.approx(1e-3)
+    assert o.beta == 0 and o.values == 0
 
 
 def test_workspace_sizes():
@@ -123,3 +124,56 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 64)
     with pytest.raises(TypeError):
         amc.targets(q, q, q)
+
+
+def test_new_calls_validation():
+    L = amc.lib()
+    p = P()
+    ws = amc.workspace_bytes(p, 16, amc.CALL_CACHE_ATTENTION)
+    assert ws > 0
+    assert amc.workspace_bytes(p, 16, amc.CALL_BETA_REDIST) > 0
+    assert amc.workspace_bytes(p, 16, amc.CALL_EVAL) > amc.workspace_bytes(p, 16, amc.CALL_BETA_REDIST)
+    # cache attention: m < 0, bad new_causal, missing keypos under causal, small workspace
+    args = dict(Q=FAKE, Ck=FAKE, Cv=FAKE, bias=FAKE, keypos=None, nvalid=None, m=4, Kn=FAKE,
+                Vn=FAKE, nc=1, out=FAKE, lse=FAKE, lz=None, ws=FAKE, nb=1 << 40)
+
+    def ca(pp, **kw):
+        a = dict(args, **kw)
+        return L.am_cache_attention(ctypes.byref(pp), a["Q"], a["Ck"], a["Cv"], a["bias"],
+                                    a["keypos"], a["nvalid"], a["m"], a["Kn"], a["Vn"], a["nc"],
+                                    a["out"], a["lse"], a["lz"], a["ws"], a["nb"], None)
+    assert ca(p, m=-1) == amc.AM_ERR_INVALID_ARG
+    assert ca(p, nc=2) == amc.AM_ERR_INVALID_ARG
+    assert ca(P(causal=1), keypos=None) == amc.AM_ERR_INVALID_ARG
+    assert ca(p, Kn=None) == amc.AM_ERR_INVALID_ARG
+    assert ca(p, nb=16) == amc.AM_ERR_WORKSPACE
+    assert ca(p, Q=FAKE + 4) == amc.AM_ERR_INVALID_ARG
+    assert ca(P(d=96)) == amc.AM_ERR_UNSUPPORTED
+    # merge: d must be a positive multiple of 4
+    assert L.am_attention_merge(10, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == amc.AM_ERR_INVALID_ARG
+    assert L.am_attention_merge(10, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == amc.AM_ERR_INVALID_ARG
+    assert L.am_attention_merge(0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == amc.AM_OK
+    # redistribution and evaluation: t range, workspace
+    assert L.am_beta_redistribute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None,
+                                  FAKE, 1 << 40, None) == amc.AM_ERR_INVALID_ARG
+    assert L.am_beta_redistribute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 16, FAKE, None, None,
+                                  FAKE, 16, None) == amc.AM_ERR_WORKSPACE
+    assert L.am_eval_residuals(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 129,
+                               FAKE, FAKE, 1 << 40, None) == amc.AM_ERR_INVALID_ARG
+    assert L.am_eval_residuals(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16,
+                               FAKE, FAKE, 1 << 40, None) == amc.AM_ERR_INVALID_ARG
+
+
+def test_option_modes_validated():
+    L = amc.lib()
+    p = P()
+    o = amc.make_options()
+    o.beta = 5
+    assert L.am_compact_head(ctypes.byref(p), FAKE, FAKE, FAKE, 16, ctypes.byref(o), FAKE, FAKE,
+                             FAKE, FAKE, None, None, None, None, None, FAKE, 1 << 40,
+                             None) == amc.AM_ERR_INVALID_ARG
+    o = amc.make_options(values="direct")
+    o.values = -1
+    assert L.am_compact_head(ctypes.byref(p), FAKE, FAKE, FAKE, 16, ctypes.byref(o), FAKE, FAKE,
+                             FAKE, FAKE, None, None, None, None, None, FAKE, 1 << 40,
+                             None) == amc.AM_ERR_INVALID_ARG
