@@ -11,6 +11,9 @@ P V on bf16 MFMA) over its average duration, timed with HIP events on the stream
 library launches on, against the bf16 dense MFMA peak.
 cpu_baseline = the float64 oracle's full-cache statistics on a bounded sample of query
 rows of head 0 (pairs/s), on the host cores.
+next = the adjacent rows, timed on the same inputs: the fast pipeline (redistributed beta,
+direct values), the held-out evaluation, and attention through the compacted cache with
+4096 appended tokens (GQA 4) merged in log space.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -163,6 +166,32 @@ def main():
     ms_values = time_calls(torch, lambda: amc.fit_values_ols(dQ, Ck, idx, beta, Og,
                                                              causal=w.causal, group=w.group,
                                                              ridge_lambda=w.ridge_lambda, T=w.T), 2)
+    # adjacent rows: the fast variants and the compacted cache in use
+    fast_opts = amc.make_options(beta="redistribute", values="direct")
+    ms_fast = time_calls(torch, lambda: amc.compact_head(dQ, dK, dV, w.t, causal=w.causal,
+                                                         group=w.group, options=fast_opts,
+                                                         want_stats=False), 3)
+    ms_redist = time_calls(torch, lambda: amc.beta_redistribute(dQ, Ck, idx, lse, causal=w.causal,
+                                                                group=w.group, T=w.T), 5)
+    full = amc.compact_head(dQ, dK, dV, w.t, causal=w.causal, group=w.group, options=opts,
+                            want_stats=False)
+    Qh = synth.make_heldout_queries(w, None, K, seed=3)
+    dQh = dev(Qh)
+    ms_eval = time_calls(torch, lambda: amc.eval_residuals(dQh, dK, dV, full["idx"], full["Ck"],
+                                                           full["beta"], full["Cv"],
+                                                           causal=w.causal, group=w.group), 2)
+    m_new, g_new = 4096, 4
+    n_new = g_new * m_new
+    Qn = synth.make_heldout_queries(
+        type(w)("appended_queries", w.heads, w.d, m_new, n_new, w.t, w.dtype, True, g_new), None,
+        K[:, :m_new], seed=5)
+    _, _, _, _, _, _, Kn, Vn = synth.make_cache_case(11, w.heads, 1, 64, 1, m_new, w.d, w.dtype,
+                                                     False)
+    dQn, dKn, dVn = dev(Qn), dev(Kn), dev(Vn)
+    cache = lambda: amc.cache_attention(dQn, full["Ck"], full["Cv"], full["beta"], Kn=dKn, Vn=dVn,
+                                        new_causal=True, group=g_new)
+    ms_cache = time_calls(torch, cache, 5)
+    cache_pairs = w.heads * (n_new * w.t + g_new * m_new * (m_new + 1) // 2)
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     achieved = flops_flash / (ms_flash * 1e-3) / 1e12
     score_tflops = flops_scores / (ms_targets * 1e-3) / 1e12
@@ -205,6 +234,18 @@ def main():
                       "fit_beta": ms_beta, "fit_values": ms_values},
         "score_passes": {"pairs_per_s": pairs / (ms_targets * 1e-3),
                          "tflops": score_tflops, "mfma_frac": score_tflops / peak},
+        "next": {
+            "fast_pipeline": {"ms_per_step": ms_fast, "pairs_per_s": pairs / (ms_fast * 1e-3),
+                              "options": "beta=redistribute, values=direct",
+                              "beta_redistribute_ms": ms_redist},
+            "heldout_eval": {"ms": ms_eval, "queries_per_head": w.n,
+                             "pairs_per_s": pairs / (ms_eval * 1e-3)},
+            "cache_attention": {"ms": ms_cache, "slots": w.t, "appended": m_new,
+                                "queries_per_head": n_new, "visible_pairs": cache_pairs,
+                                "tflops": 4 * w.d * cache_pairs / (ms_cache * 1e-3) / 1e12,
+                                "mfma_frac": 4 * w.d * cache_pairs / (ms_cache * 1e-3) / 1e12
+                                / peak},
+        },
     }
     print(json.dumps(out), flush=True)
 

@@ -52,15 +52,18 @@ size_t cmp_tstat_bytes(int64_t heads, int64_t t);
 // Per-key masses m_j = (1/n) sum over queries i that see key j of exp(scale q_i . Ck_j -
 // shift_h), shift2[h] = shift_h log2(e), in log form: log2 m_j = kmax_j + log2 kmean_j
 // (keys carry original positions keypos[h, t])
+constexpr int kKeyMassMaxSplit = 64;   // query chunks per key block (partials [split, h, t])
 struct KeyMassArgs {
   const void* Q; const void* Ck; const int32_t* keypos; const float* shift2;
   float* kmax; float* kmean;
+  float* part;   // workspace of key_mass_part_bytes
   int heads, n, t, d, group;
   bool causal, bf16;
   float scale;
   hipStream_t stream;
 };
 hipError_t launch_key_mass(const KeyMassArgs& a);
+size_t key_mass_part_bytes(int64_t heads, int64_t n, int64_t t);
 
 // Log-space merge of two attention results (rows of d floats, d % 4 == 0); O2 may be null.
 struct MergeArgs {

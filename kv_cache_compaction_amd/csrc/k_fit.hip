@@ -1861,7 +1861,7 @@ __global__ __launch_bounds__(256) void gather_f32_kernel(const T* __restrict__ V
 }
 
 struct FastPlan {
-  float* shift2h; double* zsum; float* kmax; float* kmean;   // redistribution
+  float* shift2h; double* zsum; float* kmax; float* kmean; float* kpart;   // redistribution
   float2* rowstat_cmp; float* shift2; double2* part;     // mass residual
   int2* tstat; void* Vt; float2* rowres;                 // output residual
   float* lse; float* O; void* tws;                       // evaluation: targets on the queries
@@ -1876,6 +1876,7 @@ static FastPlan plan_fast(char* base, int64_t heads, int64_t n, int64_t t, int64
   p.zsum = c.take<double>(heads);
   p.kmax = c.take<float>(heads * t);
   p.kmean = c.take<float>(heads * t);
+  p.kpart = (float*)c.take<char>(key_mass_part_bytes(heads, n, t));
   p.rowstat_cmp = c.take<float2>(heads * n);
   p.shift2 = c.take<float>(heads * n);
   p.part = c.take<double2>(heads * kResBlk);
@@ -1952,7 +1953,7 @@ hipError_t launch_beta_redistribute(const FitArgs& a) {
                      pl.zsum);
   KeyMassArgs km;
   km.Q = a.Q; km.Ck = a.Ck; km.keypos = a.idx; km.shift2 = pl.shift2h;
-  km.kmax = pl.kmax; km.kmean = pl.kmean;
+  km.kmax = pl.kmax; km.kmean = pl.kmean; km.part = pl.kpart;
   km.heads = H; km.n = a.n; km.t = a.t; km.d = a.d; km.group = a.group; km.causal = a.causal;
   km.bf16 = a.bf16; km.scale = a.scale; km.stream = st;
   hipError_t e = launch_key_mass(km);

@@ -379,12 +379,15 @@ template <typename T, int D> constexpr int colscore_kb() { return (sizeof(T) == 
 // causal mask instead of their index. head_shift (non-null): one shift per head, in log2
 // units, replaces the per-query row statistics (unnormalized masses on a common scale);
 // key_shift (KPOS only, non-null): a further per-key shift [h, Tk] in log2 units.
+// Query split: gridDim.y workgroups share a key block, each taking qchunk queries (a
+// multiple of kBQ); with more than one they write partials [split, h, Tk] (the log2 max,
+// or the plain sum) for colscore_reduce_kernel.
 template <typename T, int D, int WAVES, bool CAUSAL, int MODE, bool KPOS>
 __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float2* __restrict__ rowstat,
     float* __restrict__ score, int n, int Tk, int group, float c2, int heads,
     const int32_t* __restrict__ keypos, const float* __restrict__ head_shift,
-    const float* __restrict__ key_shift) {
+    const float* __restrict__ key_shift, int qchunk) {
   constexpr bool MAXM = MODE == 2 || MODE == 3;
   typedef typename V8<T>::type v8;
   constexpr int KB = colscore_kb<T, D>();  // 32-key blocks per wave
@@ -428,9 +431,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
       bk[kb][kc] = *(const v8*)(Kh + (size_t)krow * D + kc * 16 + hh * 8);
   }
 
-  int qbeg = 0;
-  if (CAUSAL) qbeg = (min(n, kpos(k0) * group) / kBQ) * kBQ;
-  const int ntiles = (n - qbeg + kBQ - 1) / kBQ;
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int qlo = split * qchunk, qend = min(n, qlo + qchunk);
+  int qbeg = qlo;
+  if (CAUSAL) qbeg = max(qlo, (min(n, kpos(k0) * group) / kBQ) * kBQ);
+  const int ntiles = qend > qbeg ? (qend - qbeg + kBQ - 1) / kBQ : 0;
 
   u32x4 qreg[QPT];
   float rreg = 0.f;
@@ -508,7 +513,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
           if (KPOS) e -= ksh[kb];
           if (MASK) {
             const int q = qt0 + qb * 32 + crow(j, hh);
-            e = (q < n && (!CAUSAL || kp[kb] <= q / group)) ? e : -INFINITY;
+            e = (q < qend && (!CAUSAL || kp[kb] <= q / group)) ? e : -INFINITY;
           }
           if (MAXM) part = vmax(part, e);
           else part += ex2(e);
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   // leading tiles on the causal diagonal and a ragged last tile need the mask
   int nhead = 0;
   if (CAUSAL) nhead = min(ntiles, max(0, (group * kpos(wk0 + 32 * KB - 1) - qbeg + kBQ - 1) / kBQ));
-  int nbody = ntiles - ((qbeg + ntiles * kBQ > n) ? 1 : 0);
+  int nbody = ntiles - ((qbeg + ntiles * kBQ > qend) ? 1 : 0);
   nbody = max(nbody, nhead);
   for (int it = 0; it < nhead; ++it) tile_step(it, std::true_type{});
   for (int it = nhead; it < nbody; ++it) tile_step(it, std::false_type{});
@@ -539,13 +544,34 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     float out;
     if (MAXM) {
       const float mx = vmax(amx[kb], shfl_xor32(amx[kb]));
-      out = MODE == 3 ? mx : ex2(mx);
+      out = (MODE == 3 || nsplit > 1) ? mx : ex2(mx);
     } else {
       const double tot = acc[kb] + __shfl_xor(acc[kb], 32, 64);
-      out = MODE == 0 ? (float)sqrt(tot / (double)n) : (float)(tot / (double)n);
+      out = nsplit > 1 ? (float)tot
+                       : (MODE == 0 ? (float)sqrt(tot / (double)n) : (float)(tot / (double)n));
     }
-    if (hh == 0 && key[kb] < Tk) score[(size_t)head * Tk + key[kb]] = out;
+    if (hh == 0 && key[kb] < Tk) score[((size_t)split * heads + head) * Tk + key[kb]] = out;
   }
+}
+
+// Combines the query-split partials [nsplit, h, Tk] of the column pass (fixed order).
+__global__ __launch_bounds__(256) void colscore_reduce_kernel(const float* __restrict__ part,
+                                                              float* __restrict__ out, int heads,
+                                                              int Tk, int nsplit, int n, int mode) {
+  const int head = blockIdx.y, key = blockIdx.x * 256 + threadIdx.x;
+  if (key >= Tk) return;
+  const size_t stride = (size_t)heads * Tk, o = (size_t)head * Tk + key;
+  float r;
+  if (mode >= 2) {
+    float mx = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) mx = vmax(mx, part[sp * stride + o]);
+    r = mode == 3 ? mx : ex2(mx);
+  } else {
+    double tot = 0.0;
+    for (int sp = 0; sp < nsplit; ++sp) tot += (double)part[sp * stride + o];
+    r = mode == 0 ? (float)sqrt(tot / (double)n) : (float)(tot / (double)n);
+  }
+  out[o] = r;
 }
 
 // ------------------------------------------------------------------------------------
@@ -592,7 +618,7 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M, false>), gs, bs, 0, a.stream,   \
                      (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.n, a.T, \
                      a.group, c2, a.heads, (const int32_t*)nullptr, (const float*)nullptr,     \
-                     (const float*)nullptr)
+                     (const float*)nullptr, a.n)
   if (a.causal) {
     if (a.mode == 0) AM_SCORE(true, 0); else if (a.mode == 1) AM_SCORE(true, 1); else AM_SCORE(true, 2);
   } else {
@@ -605,18 +631,43 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
 // Per-key masses of the compacted keys (original positions for the causal mask) in log
 // form: kmax = max_i (scale q_i.k_j log2 e - shift2_h) over the queries that see key j,
 // then kmean = (1/n) sum_i 2^(that exponent - kmax), so log2 m_j = kmax + log2 kmean holds
-// masses far below the common shift without underflow. Two column passes (MAX, MEAN).
+// masses far below the common shift without underflow. Two column passes (MAX, MEAN),
+// each split over query chunks so that a few hundred compacted keys still fill the chip.
+static void key_mass_split(int t, int heads, int n, int bk, int& nsplit, int& qchunk) {
+  const int nkb = (t + bk - 1) / bk;
+  int want = (1024 + nkb * heads - 1) / (nkb * heads);
+  const int maxs = (n + kBQ - 1) / kBQ;
+  want = max(1, min(want, min(maxs, kKeyMassMaxSplit)));
+  qchunk = ((n + want - 1) / want + kBQ - 1) / kBQ * kBQ;
+  nsplit = (n + qchunk - 1) / qchunk;
+}
 template <typename T, int D, bool C>
 static void launch_key_mass_c(const KeyMassArgs& a) {
   const int BK = kScoreWaves * 32 * colscore_kb<T, D>();
-  const dim3 gs(((a.t + BK - 1) / BK) * a.heads), bs(kScoreWaves * 64);
+  int nsplit, qchunk;
+  key_mass_split(a.t, a.heads, a.n, BK, nsplit, qchunk);
+  const dim3 gs(((a.t + BK - 1) / BK) * a.heads, nsplit), bs(kScoreWaves * 64);
+  const dim3 gr((a.t + 255) / 256, a.heads);
   const float c2 = a.scale * kLog2e;
+  float* o1 = nsplit > 1 ? a.part : a.kmax;
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, 3, true>), gs, bs, 0, a.stream,
-                     (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, a.kmax, a.n, a.t,
-                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)nullptr);
+                     (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, o1, a.n, a.t,
+                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)nullptr, qchunk);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(colscore_reduce_kernel, gr, dim3(256), 0, a.stream, (const float*)a.part,
+                       a.kmax, a.heads, a.t, nsplit, a.n, 3);
+  float* o2 = nsplit > 1 ? a.part : a.kmean;
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, 1, true>), gs, bs, 0, a.stream,
-                     (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, a.kmean, a.n, a.t,
-                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)a.kmax);
+                     (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, o2, a.n, a.t,
+                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)a.kmax, qchunk);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(colscore_reduce_kernel, gr, dim3(256), 0, a.stream, (const float*)a.part,
+                       a.kmean, a.heads, a.t, nsplit, a.n, 1);
+}
+
+size_t key_mass_part_bytes(int64_t heads, int64_t n, int64_t t) {
+  (void)n;
+  return align_up((size_t)kKeyMassMaxSplit * heads * t * sizeof(float));
 }
 template <typename T, int D>
 static hipError_t launch_key_mass_t(const KeyMassArgs& a) {
