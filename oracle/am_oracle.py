@@ -84,12 +84,14 @@ def _chunks(n: int, T: int, budget: int = 1 << 24):
 # --------------------------------------------------------------------------------------
 # S1 + S2: full-cache statistics
 # --------------------------------------------------------------------------------------
-def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True, rows=None):
+def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True, rows=None,
+                     keypos=None):
     """lse [n], O [n, d] (or None) and per-key (sum p, sum p^2, max p) over queries.
 
     Q [n, d], K and V [T, d], all float64. p_ij = exp(s_ij - lse_i) for visible pairs, 0
     otherwise. Queries are processed in chunks only to bound memory. `rows` gives the
-    query indices (positions) of the rows of Q when Q is a subset of a problem's queries.
+    query indices (positions) of the rows of Q when Q is a subset of a problem's queries;
+    `keypos` the original positions of the rows of K when K is a subset of the keys.
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
@@ -99,15 +101,17 @@ def full_cache_stats(Q, K, V, scale, causal=False, group=1, want_O=True, rows=No
     colsum = np.zeros(T)
     colsq = np.zeros(T)
     colmax = np.zeros(T)
-    keys = np.arange(T)
+    keys = np.arange(T) if keypos is None else np.asarray(keypos)
     rows = np.arange(n) if rows is None else np.asarray(rows)
     for a, b in _chunks(n, T):
         s = scale * (Q[a:b] @ K.T)
         vis = visible(rows[a:b], keys, causal, group)
         s = np.where(vis, s, -np.inf)
         m = s.max(axis=1)
-        lse[a:b] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-        p = np.exp(s - lse[a:b, None])
+        m = np.where(np.isfinite(m), m, 0.0)   # a row that sees no key: lse = -inf, p = 0
+        with np.errstate(divide="ignore"):
+            lse[a:b] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        p = np.where(vis, np.exp(s - np.where(np.isfinite(lse[a:b]), lse[a:b], 0.0)[:, None]), 0.0)
         if want_O:
             O[a:b] = p @ V
         colsum += p.sum(axis=0)
@@ -437,6 +441,27 @@ def redistribute_beta(Q, Ck, idx, lse, scale, causal=False, group=1):
     # value can only be rounding, and is taken as 0
     delta = max((np.exp(lse - c).sum() - e.sum()) / n, 0.0)
     return np.log((m + delta / t) / m)
+
+
+def select_two_pass(Q, K, sub, t, k_mult, scale, causal=False, group=1, mode="rms"):
+    """Two-pass key selection ("Compaction" blog, §Choosing C_k, Attempt #3).
+
+    Pass 1 scores every key against the query subset `sub` (ascending query indices; the
+    statistic's divisor is the subset size) and keeps the k_mult * t best keys as a
+    shortlist (all T if fewer). Pass 2 scores the shortlist against all n queries, with
+    each query's softmax normalized over the shortlist keys it sees, and keeps the t best.
+    Returns (idx [t] ascending original key indices, lse over the shortlist [n]).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    n, T = Q.shape[0], K.shape[0]
+    sub = np.asarray(sub)
+    _, _, st1 = full_cache_stats(Q[sub], K, K, scale, causal, group, want_O=False, rows=sub)
+    short = select_top(key_score(st1, mode, sub.size), min(k_mult * t, T))
+    lse_s, _, st2 = full_cache_stats(Q, K[short], K[short], scale, causal, group, want_O=False,
+                                     keypos=short)
+    loc = select_top(key_score(st2, mode, n), t)
+    return short[loc], lse_s
 
 
 def direct_values(V, idx):

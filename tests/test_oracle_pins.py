@@ -500,3 +500,82 @@ def test_redistribute_beta_full_budget_is_zero():
 def test_direct_values_are_the_selected_rows():
     V = np.arange(24.0).reshape(8, 3)
     np.testing.assert_array_equal(O.direct_values(V, [1, 4, 6]), V[[1, 4, 6]])
+
+
+# --------------------------------------------------------------------------------------
+# two-pass selection ("Compaction" blog, §Choosing C_k, Attempt #3)
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,group", [(False, 1), (True, 2)])
+def test_two_pass_with_full_shortlist_and_all_queries_is_full_selection(causal, group):
+    rng = np.random.default_rng(21)
+    T, d = 48, 8
+    n = group * T
+    Q, K, V = _qkv(n, T, d, rng)
+    lse, _, st = O.full_cache_stats(Q, K, V, 0.5, causal, group)
+    full = O.select_top(O.key_score(st, "rms", n), 10)
+    idx, lse_s = O.select_two_pass(Q, K, np.arange(n), 10, 5, 0.5, causal, group)   # 50 >= T
+    np.testing.assert_array_equal(idx, full)
+    np.testing.assert_allclose(lse_s, lse, atol=1e-12)
+
+
+def _loop_two_pass(Q, K, sub, t, k_mult, scale, causal, group):
+    n, T = Q.shape[0], K.shape[0]
+
+    def stats(rows, keys):
+        sq = np.zeros(len(keys))
+        lse = np.zeros(len(rows))
+        for a, i in enumerate(rows):
+            vis = [b for b, j in enumerate(keys) if not causal or j <= i // group]
+            sc = {b: scale * float(Q[i] @ K[keys[b]]) for b in vis}
+            m = max(sc.values())
+            z = sum(np.exp(v - m) for v in sc.values())
+            lse[a] = m + np.log(z)
+            for b, v in sc.items():
+                sq[b] += float(np.exp(v - lse[a])) ** 2
+        return sq, lse
+
+    sq1, _ = stats(list(sub), list(range(T)))
+    r1 = np.sqrt(sq1 / len(sub))
+    short = sorted(sorted(range(T), key=lambda j: (-r1[j], j))[: min(k_mult * t, T)])
+    sq2, lse2 = stats(list(range(n)), short)
+    r2 = np.sqrt(sq2 / n)
+    loc = sorted(sorted(range(len(short)), key=lambda b: (-r2[b], b))[:t])
+    return np.array([short[b] for b in loc]), lse2
+
+
+@pytest.mark.parametrize("causal,group", [(False, 1), (True, 3)])
+def test_two_pass_bruteforce(causal, group):
+    rng = np.random.default_rng(22)
+    T, d = 30, 6
+    n = group * T
+    Q, K, V = _qkv(n, T, d, rng)
+    sub = np.sort(rng.choice(n, size=12, replace=False))
+    idx, lse_s = O.select_two_pass(Q, K, sub, 4, 2, 0.7, causal, group)
+    ref_idx, ref_lse = _loop_two_pass(Q, K, sub, 4, 2, 0.7, causal, group)
+    np.testing.assert_array_equal(idx, ref_idx)
+    np.testing.assert_allclose(lse_s, ref_lse, atol=1e-12)
+
+
+def test_two_pass_shortlist_mass_is_a_lower_bound():
+    rng = np.random.default_rng(23)
+    Q, K, V = _qkv(80, 80, 8, rng)
+    lse, _, _ = O.full_cache_stats(Q, K, V, 0.5, True, 1)
+    idx, lse_s = O.select_two_pass(Q, K, np.arange(0, 80, 5), 6, 2, 0.5, True, 1)
+    assert np.all(lse_s <= lse + 1e-12)
+    assert np.all(np.diff(idx) > 0) and idx.size == 6
+
+
+def test_rows_that_see_no_key_subset():
+    """With a key subset at later positions, early causal rows see nothing: lse = -inf, a
+    zero output row, and no contribution to any key's statistics."""
+    rng = np.random.default_rng(24)
+    Q, K, V = _qkv(20, 20, 4, rng)
+    keypos = np.array([5, 9, 14])
+    lse, Oo, (cs, cq, cm) = O.full_cache_stats(Q, K[keypos], V[keypos], 0.5, True, 1,
+                                               keypos=keypos)
+    assert np.all(lse[:5] == -np.inf) and np.all(Oo[:5] == 0.0)
+    l2, O2, (s2, q2, m2) = O.full_cache_stats(Q[5:], K[keypos], V[keypos], 0.5, True, 1,
+                                              rows=np.arange(5, 20), keypos=keypos)
+    np.testing.assert_allclose(lse[5:], l2, atol=1e-13)
+    np.testing.assert_allclose(cs, s2, atol=1e-13)
+    np.testing.assert_allclose(cq, q2, atol=1e-13)
