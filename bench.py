@@ -12,8 +12,10 @@ library launches on, against the bf16 dense MFMA peak.
 cpu_baseline = the float64 oracle's full-cache statistics on a bounded sample of query
 rows of head 0 (pairs/s), on the host cores.
 next = the adjacent rows, timed on the same inputs: the fast pipeline (redistributed beta,
-direct values), the held-out evaluation, and attention through the compacted cache with
-4096 appended tokens (GQA 4) merged in log space.
+direct values), the two-pass method (256-query subset, shortlist of 4t keys, then the fast
+fits), the held-out evaluation, and attention through the compacted cache with 4096
+appended tokens (GQA 4) merged in log space. The pairs/s of the pipelines count the
+full workload's visible pairs (the work they stand in for), not the pairs they score.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -180,6 +182,9 @@ def main():
     ms_eval = time_calls(torch, lambda: amc.eval_residuals(dQh, dK, dV, full["idx"], full["Ck"],
                                                            full["beta"], full["Cv"],
                                                            causal=w.causal, group=w.group), 2)
+    sub = torch.from_numpy(synth.query_subset(w, None, 256)).cuda()
+    ms_two = time_calls(torch, lambda: amc.compact_two_pass(dQ, dK, dV, sub, w.t, k_mult=4,
+                                                            causal=w.causal, group=w.group), 3)
     m_new, g_new = 4096, 4
     n_new = g_new * m_new
     Qn = synth.make_heldout_queries(
@@ -238,6 +243,9 @@ def main():
             "fast_pipeline": {"ms_per_step": ms_fast, "pairs_per_s": pairs / (ms_fast * 1e-3),
                               "options": "beta=redistribute, values=direct",
                               "beta_redistribute_ms": ms_redist},
+            "two_pass_pipeline": {"ms_per_step": ms_two, "pairs_per_s": pairs / (ms_two * 1e-3),
+                                  "options": "256 query subset, shortlist 4t, redistributed "
+                                             "beta, direct values"},
             "heldout_eval": {"ms": ms_eval, "queries_per_head": w.n,
                              "pairs_per_s": pairs / (ms_eval * 1e-3)},
             "cache_attention": {"ms": ms_cache, "slots": w.t, "appended": m_new,

@@ -176,6 +176,39 @@ am_status am_beta_redistribute(const am_problem* p, const void* Q, const void* C
                                am_stream_t stream);
 
 /*
+ * am_select_two_pass - key selection without the full n x T score pass ("Compaction"
+ * blog, §Choosing C_k, Attempt #3 "Two-Pass"). Pass 1 scores all T keys against the query
+ * subset sub[h, s] (ascending query indices in [0, n), e.g. a seeded random sample; the
+ * statistic's divisor is s) and keeps the kt = min(k_mult * t, T) best keys as a
+ * shortlist. Pass 2 scores the shortlist against all n queries, each query's softmax
+ * normalized over the shortlist keys it sees, and keeps the t best (ties to the lower
+ * index at both stages). Outputs idx[h, t] (ascending original key indices), Ck[h, t, d],
+ * V_sel (optional) and lse_short[h, n] = log sum over the visible shortlist keys (-inf for
+ * a query that sees none), the Z_i that am_beta_redistribute takes for this method.
+ * Workspace: am_two_pass_workspace_bytes.
+ */
+am_status am_select_two_pass(const am_problem* p, const void* Q, const void* K, const void* V,
+                             const int32_t* sub, int64_t s, int64_t t, int32_t k_mult,
+                             am_score_mode mode, int32_t* idx, void* Ck, void* V_sel,
+                             float* lse_short, void* ws, size_t ws_bytes, am_stream_t stream);
+
+/*
+ * am_compact_two_pass - the blog's fast method end to end ("Compaction", §Results,
+ * "two_pass"): am_select_two_pass, beta by uniform redistribution over the shortlist's
+ * mass (am_beta_redistribute with lse_short), and direct values C_v = V[idx] (f32).
+ * Outputs idx, Ck, beta, Cv; optional resid_out[2, h]: the mass residual against the
+ * shortlist's mass and the output residual is not computed (row 1 is set to -1).
+ */
+am_status am_compact_two_pass(const am_problem* p, const void* Q, const void* K, const void* V,
+                              const int32_t* sub, int64_t s, int64_t t, int32_t k_mult,
+                              am_score_mode mode, int32_t* idx, void* Ck, float* beta, float* Cv,
+                              float* resid_out, void* ws, size_t ws_bytes, am_stream_t stream);
+
+/* Workspace bytes of am_select_two_pass (compact = 0) or am_compact_two_pass (compact = 1). */
+size_t am_two_pass_workspace_bytes(const am_problem* p, int64_t t, int64_t s, int32_t k_mult,
+                                   int32_t compact);
+
+/*
  * am_eval_residuals - quality of a compacted cache on a set of queries (for instance a
  * held-out set; "Compaction" blog, §Choosing beta and §Choosing C_v report errors on
  * held-out queries): the full-cache targets of Q against K, V, then

@@ -74,6 +74,15 @@ _PROTOS = {
                                           _P]),
     "am_beta_redistribute": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P,
                                             ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "am_select_two_pass": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _P, _P, _P,
+                                          _P, _P, ctypes.c_size_t, _P]),
+    "am_compact_two_pass": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _P, _P, _P,
+                                           _P, _P, _P, ctypes.c_size_t, _P]),
+    "am_two_pass_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AmProblem), ctypes.c_int64,
+                                                      ctypes.c_int64, ctypes.c_int32,
+                                                      ctypes.c_int32]),
     "am_eval_residuals": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
 }
@@ -389,3 +398,59 @@ def eval_residuals(Q, K, V, idx, Ck, beta, Cv, *, causal=False, group=1, scale=N
                                    _ptr(beta), _ptr(Cv), t, _ptr(res), _ptr(ws), nb, _stream()),
            "am_eval_residuals")
     return res
+
+
+def _two_pass_setup(Q, K, sub, t, k_mult, causal, group, scale, compact):
+    torch = _torch()
+    _need(Q, "Q"); _need(K, "K")
+    p = make_problem(Q, K, causal=causal, group=group, scale=scale)
+    _need(sub, "sub", dtype=torch.int32)
+    if sub.dim() != 2 or sub.shape[0] != p.heads:
+        raise ValueError("sub must be [h, s]")
+    s = sub.shape[1]
+    nb = int(lib().am_two_pass_workspace_bytes(ctypes.byref(p), t, s, int(k_mult), int(compact)))
+    if nb == 0:
+        raise AmError(AM_ERR_INVALID_ARG, "am_two_pass_workspace_bytes")
+    ws = torch.empty(nb, dtype=torch.uint8, device=Q.device)
+    return p, s, ws, nb
+
+
+def select_two_pass(Q, K, sub, t, *, V=None, k_mult=4, score="rms", causal=False, group=1,
+                    scale=None):
+    """Two-pass selection from the query subset sub [h, s] (ascending int32 indices).
+    Returns idx [h, t], Ck [h, t, d], V_sel (or None) and lse over the shortlist [h, n]."""
+    torch = _torch()
+    p, s, ws, nb = _two_pass_setup(Q, K, sub, t, k_mult, causal, group, scale, 0)
+    h, n, d = p.heads, p.n, p.d
+    idx = torch.empty((h, t), dtype=torch.int32, device=Q.device)
+    Ck = torch.empty((h, t, d), dtype=Q.dtype, device=Q.device)
+    Vs = None
+    if V is not None:
+        _need(V, "V", dtype=K.dtype, shape=K.shape)
+        Vs = torch.empty_like(Ck)
+    lse = torch.empty((h, n), dtype=torch.float32, device=Q.device)
+    _check(lib().am_select_two_pass(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(sub), s, t,
+                                    int(k_mult), SCORE_MODES[score], _ptr(idx), _ptr(Ck), _ptr(Vs),
+                                    _ptr(lse), _ptr(ws), nb, _stream()), "am_select_two_pass")
+    return idx, Ck, Vs, lse
+
+
+def compact_two_pass(Q, K, V, sub, t, *, k_mult=4, score="rms", causal=False, group=1,
+                     scale=None):
+    """The blog's two-pass method: two-pass selection, redistributed beta, direct values.
+    Returns a dict of idx, Ck, beta, Cv and resid [2, h] (row 1 is -1: not computed)."""
+    torch = _torch()
+    _need(V, "V", dtype=K.dtype, shape=K.shape)
+    p, s, ws, nb = _two_pass_setup(Q, K, sub, t, k_mult, causal, group, scale, 1)
+    h, d = p.heads, p.d
+    out = dict(idx=torch.empty((h, t), dtype=torch.int32, device=Q.device),
+               Ck=torch.empty((h, t, d), dtype=Q.dtype, device=Q.device),
+               beta=torch.empty((h, t), dtype=torch.float32, device=Q.device),
+               Cv=torch.empty((h, t, d), dtype=torch.float32, device=Q.device),
+               resid=torch.empty((2, h), dtype=torch.float32, device=Q.device))
+    _check(lib().am_compact_two_pass(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(sub), s, t,
+                                     int(k_mult), SCORE_MODES[score], _ptr(out["idx"]),
+                                     _ptr(out["Ck"]), _ptr(out["beta"]), _ptr(out["Cv"]),
+                                     _ptr(out["resid"]), _ptr(ws), nb, _stream()),
+           "am_compact_two_pass")
+    return out

@@ -347,6 +347,94 @@ am_status am_beta_redistribute(const am_problem* p, const void* Q, const void* C
   return from_hip(launch_beta_redistribute(a));
 }
 
+namespace {
+am_status check_two_pass(const am_problem* p, int64_t s, int64_t t, int32_t k_mult) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if (s < 1 || s > p->n || k_mult < 1) return AM_ERR_INVALID_ARG;
+  return AM_OK;
+}
+int64_t two_pass_kt(const am_problem* p, int64_t t, int32_t k_mult) {
+  const int64_t kt = t * (int64_t)k_mult;
+  return kt < p->T ? kt : p->T;
+}
+size_t ws_two_pass(const am_problem* p, int64_t t, int64_t s, int32_t k_mult) {
+  return two_pass_ws_bytes(p->heads, p->n, p->T, p->d, esize(p), s, two_pass_kt(p, t, k_mult));
+}
+size_t ws_compact_two_pass(const am_problem* p, int64_t t, int64_t s, int32_t k_mult) {
+  size_t stage = ws_two_pass(p, t, s, k_mult);
+  const size_t f = ws_fast(p, t, 0);
+  if (f > stage) stage = f;
+  return align_up((size_t)p->heads * p->n * 4) + stage;   // lse_short, then the stages
+}
+TwoPassArgs two_pass_args(const am_problem* p, const void* Q, const void* K, const void* V,
+                          const int32_t* sub, int64_t s, int64_t t, int32_t k_mult, int mode,
+                          int32_t* idx, void* Ck, void* Vsel, float* lse_short, void* ws,
+                          hipStream_t st) {
+  TwoPassArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.sub = sub; a.idx = idx; a.Ck = Ck; a.Vsel = Vsel;
+  a.lse_short = lse_short;
+  a.heads = (int)p->heads; a.n = (int)p->n; a.T = (int)p->T; a.d = (int)p->d; a.group = p->group;
+  a.s = (int)s; a.t = (int)t; a.kt = (int)two_pass_kt(p, t, k_mult); a.mode = mode;
+  a.causal = p->causal != 0; a.bf16 = p->dtype == AM_BF16; a.scale = p->scale;
+  a.ws = ws; a.stream = st;
+  return a;
+}
+}  // namespace
+
+size_t am_two_pass_workspace_bytes(const am_problem* p, int64_t t, int64_t s, int32_t k_mult,
+                                   int32_t compact) {
+  if (check_two_pass(p, s, t, k_mult) != AM_OK) return 0;
+  return compact ? ws_compact_two_pass(p, t, s, k_mult) : ws_two_pass(p, t, s, k_mult);
+}
+
+am_status am_select_two_pass(const am_problem* p, const void* Q, const void* K, const void* V,
+                             const int32_t* sub, int64_t s, int64_t t, int32_t k_mult,
+                             am_score_mode mode, int32_t* idx, void* Ck, void* V_sel,
+                             float* lse_short, void* ws, size_t ws_bytes, am_stream_t stream) {
+  am_status st = check_two_pass(p, s, t, k_mult);
+  if (st != AM_OK) return st;
+  if (mode < AM_SCORE_RMS || mode > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (!Q || !K || !sub || !idx || !Ck || !lse_short || (V_sel && !V)) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(K) || (V && !al16(V)) || !al16(sub) || !al16(idx) || !al16(Ck) ||
+      (V_sel && !al16(V_sel)) || !al16(lse_short) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_two_pass(p, t, s, k_mult)) return AM_ERR_WORKSPACE;
+  return from_hip(launch_two_pass(two_pass_args(p, Q, K, V_sel ? V : nullptr, sub, s, t, k_mult,
+                                                (int)mode, idx, Ck, V_sel, lse_short, ws,
+                                                (hipStream_t)stream)));
+}
+
+am_status am_compact_two_pass(const am_problem* p, const void* Q, const void* K, const void* V,
+                              const int32_t* sub, int64_t s, int64_t t, int32_t k_mult,
+                              am_score_mode mode, int32_t* idx, void* Ck, float* beta, float* Cv,
+                              float* resid_out, void* ws, size_t ws_bytes, am_stream_t stream) {
+  am_status st = check_two_pass(p, s, t, k_mult);
+  if (st != AM_OK) return st;
+  if (mode < AM_SCORE_RMS || mode > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !sub || !idx || !Ck || !beta || !Cv) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(K) || !al16(V) || !al16(sub) || !al16(idx) || !al16(Ck) ||
+      !al16(beta) || !al16(Cv) || (resid_out && !al16(resid_out)) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_compact_two_pass(p, t, s, k_mult)) return AM_ERR_WORKSPACE;
+  const hipStream_t sm = (hipStream_t)stream;
+  float* lse_short = (float*)ws;
+  char* stage = (char*)ws + align_up((size_t)p->heads * p->n * 4);
+  hipError_t e = launch_two_pass(two_pass_args(p, Q, K, nullptr, sub, s, t, k_mult, (int)mode,
+                                               idx, Ck, nullptr, lse_short, stage, sm));
+  if (e != hipSuccess) return AM_ERR_DEVICE;
+  FitArgs a = fit_args(p, Q, Ck, idx, t, stage, ws_bytes - (size_t)(stage - (char*)ws), sm);
+  a.lse = lse_short; a.beta = beta; a.w = nullptr; a.mass_resid = resid_out;
+  if ((e = launch_beta_redistribute(a)) != hipSuccess) return AM_ERR_DEVICE;
+  a.beta_in = beta; a.Cv = Cv; a.O = nullptr; a.out_resid = nullptr;
+  if ((e = launch_values_direct(a, V, (int)p->T)) != hipSuccess) return AM_ERR_DEVICE;
+  if (resid_out && (e = launch_fill_f32(resid_out + p->heads, (long long)p->heads, -1.f, sm)) !=
+                       hipSuccess)
+    return AM_ERR_DEVICE;
+  return AM_OK;
+}
+
 am_status am_eval_residuals(const am_problem* p, const void* Q, const void* K, const void* V,
                             const int32_t* idx, const void* Ck, const float* beta,
                             const float* Cv, int64_t t, float* resid_out, void* ws,

@@ -26,6 +26,7 @@ struct TargetsArgs {
   bool causal, bf16;
   float scale;
   hipStream_t stream;
+  const int32_t* qpos = nullptr;   // query subset: positions [h, n], ascending per head
 };
 hipError_t launch_targets(const TargetsArgs& a);
 size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize);
@@ -64,6 +65,37 @@ struct KeyMassArgs {
 };
 hipError_t launch_key_mass(const KeyMassArgs& a);
 size_t key_mass_part_bytes(int64_t heads, int64_t n, int64_t t);
+
+// score[h, j] = selection statistic (mode as am_score_mode) over all n queries of the keys
+// Ck [h, t] at original positions keypos, with p = 2^(scale q.k log2 e - (m + log2 l)) from
+// the row statistics (m, log2 l) [h, n] over the same keys
+struct KeyScoreArgs {
+  const void* Q; const void* Ck; const int32_t* keypos; const float2* rowstat;
+  float* score;
+  float* part;   // workspace of key_mass_part_bytes
+  int mode;
+  int heads, n, t, d, group;
+  bool causal, bf16;
+  float scale;
+  hipStream_t stream;
+};
+hipError_t launch_key_score(const KeyScoreArgs& a);
+
+// Two-pass key selection (query subset against all keys, then all queries against a
+// shortlist of k * t keys); workspace two_pass_ws_bytes
+struct TwoPassArgs {
+  const void* Q; const void* K; const void* V; const int32_t* sub;
+  int32_t* idx; void* Ck; void* Vsel; float* lse_short;
+  int heads, n, T, d, group, s, t, kt, mode;
+  bool causal, bf16;
+  float scale;
+  void* ws;
+  hipStream_t stream;
+};
+hipError_t launch_two_pass(const TwoPassArgs& a);
+hipError_t launch_fill_f32(float* p, long long count, float v, hipStream_t st);
+size_t two_pass_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t s,
+                         int64_t kt);
 
 // Log-space merge of two attention results (rows of d floats, d % 4 == 0); O2 may be null.
 struct MergeArgs {

@@ -94,6 +94,7 @@ struct FlashParams {
   const void* Q; const void* K; const void* Vt;
   const float* bias; const int32_t* keypos; const float* Y;
   const int2* tstat;   // biased causal: per key tile (min, max) original position, or null
+  const int32_t* qpos; // query positions [h, n], ascending per head, or null (position i / group)
   float* lse; float2* rowstat; float* O; float2* rowres;
   int n, Tk, Tpad, group, heads, n_qtiles;
   float c2;
@@ -143,7 +144,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 
   const int wq0 = q0 + wave * 32;            // first query of this wave
   const int qi = wq0 + r;                    // this lane's query (column of S^T)
-  const int qpos = qi / group;
+  // a query subset carries its positions (ascending); else query i sits at i / group
+  auto qposf = [&](int q) { return p.qpos ? p.qpos[(size_t)head * n + q] : q / group; };
+  const int qpos = p.qpos ? qposf(min(qi, n - 1)) : qi / group;
   v8 bq[KC];
   {
     const int qrow = min(qi, n - 1);
@@ -152,10 +155,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
   }
 
   int kend = Tk;
-  if (CAUSAL && !BIASED) kend = min(Tk, (min(q0 + BM, n) - 1) / group + 1);
+  if (CAUSAL && !BIASED) kend = min(Tk, qposf(min(q0 + BM, n) - 1) + 1);
   // leading tiles this wave can take without any mask
   int nfull = Tk / BN;
-  if (CAUSAL && !BIASED) nfull = min(nfull, (wq0 / group + 1) / BN);
+  if (CAUSAL && !BIASED)
+    nfull = min(nfull, ((p.qpos ? qposf(min(wq0, n - 1)) : wq0 / group) + 1) / BN);
   if (CAUSAL && BIASED) {
     // compacted keys carry their original positions: tiles past the last one holding a
     // key visible to the workgroup's last query are dropped, and leading tiles whose every
@@ -163,7 +167,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
     int nf = 0, last = -1;
     if (p.tstat) {
       const int2* ts = p.tstat + (size_t)head * ((Tk + BN - 1) / BN);
-      const int qmax = (min(q0 + BM, n) - 1) / group, qmin = wq0 / group;
+      const int qmax = qposf(min(q0 + BM, n) - 1);
+      const int qmin = p.qpos ? qposf(min(wq0, n - 1)) : wq0 / group;
       bool lead = true;
       for (int i = 0; i < (Tk + BN - 1) / BN; ++i) {
         const int2 v = ts[i];
@@ -382,12 +387,13 @@ template <typename T, int D> constexpr int colscore_kb() { return (sizeof(T) == 
 // Query split: gridDim.y workgroups share a key block, each taking qchunk queries (a
 // multiple of kBQ); with more than one they write partials [split, h, Tk] (the log2 max,
 // or the plain sum) for colscore_reduce_kernel.
-template <typename T, int D, int WAVES, bool CAUSAL, int MODE, bool KPOS>
+// QPOS: the queries are a subset with positions qpos[h, n] (every tile takes the mask).
+template <typename T, int D, int WAVES, bool CAUSAL, int MODE, bool KPOS, bool QPOS = false>
 __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float2* __restrict__ rowstat,
     float* __restrict__ score, int n, int Tk, int group, float c2, int heads,
     const int32_t* __restrict__ keypos, const float* __restrict__ head_shift,
-    const float* __restrict__ key_shift, int qchunk) {
+    const float* __restrict__ key_shift, int qchunk, const int32_t* __restrict__ qpos) {
   constexpr bool MAXM = MODE == 2 || MODE == 3;
   typedef typename V8<T>::type v8;
   constexpr int KB = colscore_kb<T, D>();  // 32-key blocks per wave
@@ -404,6 +410,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
 
   __shared__ __align__(16) T qs[2][kBQ * QP];
   __shared__ __align__(16) float rs[2][kBQ];   // f (m + log2 l) per query
+  __shared__ int qps[QPOS ? 2 : 1][QPOS ? kBQ : 1];   // query positions of a subset
 
   const int b = blockIdx.x;
   const int head = b % heads;
@@ -434,11 +441,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int qlo = split * qchunk, qend = min(n, qlo + qchunk);
   int qbeg = qlo;
-  if (CAUSAL) qbeg = max(qlo, (min(n, kpos(k0) * group) / kBQ) * kBQ);
+  if (CAUSAL && !QPOS) qbeg = max(qlo, (min(n, kpos(k0) * group) / kBQ) * kBQ);
   const int ntiles = qend > qbeg ? (qend - qbeg + kBQ - 1) / kBQ : 0;
 
   u32x4 qreg[QPT];
   float rreg = 0.f;
+  int qpreg = 0;
   auto gload = [&](int it) {
     const int qt0 = qbeg + it * kBQ;
 #pragma unroll
@@ -447,6 +455,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
       const int row = c / QCPR, col = (c % QCPR) * E;
       qreg[i] = *(const u32x4*)(Qh + (size_t)min(qt0 + row, n - 1) * D + col);
     }
+    if (QPOS && tid < kBQ) qpreg = qpos[(size_t)head * n + min(qt0 + tid, n - 1)];
     if (tid < kBQ) {
       if (head_shift) {
         rreg = f * head_shift[head];
@@ -463,6 +472,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
       *(u32x4*)(&qs[buf][(c / QCPR) * QP + (c % QCPR) * E]) = qreg[i];
     }
     if (tid < kBQ) rs[buf][tid] = rreg;
+    if (QPOS && tid < kBQ) qps[buf][tid] = qpreg;
   };
 
   double acc[KB];
@@ -513,7 +523,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
           if (KPOS) e -= ksh[kb];
           if (MASK) {
             const int q = qt0 + qb * 32 + crow(j, hh);
-            e = (q < qend && (!CAUSAL || kp[kb] <= q / group)) ? e : -INFINITY;
+            const int qp = QPOS ? qps[buf][qb * 32 + crow(j, hh)] : q / group;
+            e = (q < qend && (!CAUSAL || kp[kb] <= qp)) ? e : -INFINITY;
           }
           if (MAXM) part = vmax(part, e);
           else part += ex2(e);
@@ -534,6 +545,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   // leading tiles on the causal diagonal and a ragged last tile need the mask
   int nhead = 0;
   if (CAUSAL) nhead = min(ntiles, max(0, (group * kpos(wk0 + 32 * KB - 1) - qbeg + kBQ - 1) / kBQ));
+  if (CAUSAL && QPOS) nhead = ntiles;
   int nbody = ntiles - ((qbeg + ntiles * kBQ > qend) ? 1 : 0);
   nbody = max(nbody, nhead);
   for (int it = 0; it < nhead; ++it) tile_step(it, std::true_type{});
@@ -605,7 +617,7 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   }
   FlashParams fp;
   fp.Q = a.Q; fp.K = a.K; fp.Vt = a.Vt;
-  fp.bias = nullptr; fp.keypos = nullptr; fp.Y = nullptr; fp.tstat = nullptr;
+  fp.bias = nullptr; fp.keypos = nullptr; fp.Y = nullptr; fp.tstat = nullptr; fp.qpos = a.qpos;
   fp.lse = a.lse; fp.rowstat = (float2*)a.rowstat; fp.O = a.O; fp.rowres = nullptr;
   fp.n = a.n; fp.Tk = a.T; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
   fp.c2 = c2;
@@ -618,8 +630,16 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M, false>), gs, bs, 0, a.stream,   \
                      (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.n, a.T, \
                      a.group, c2, a.heads, (const int32_t*)nullptr, (const float*)nullptr,     \
-                     (const float*)nullptr, a.n)
-  if (a.causal) {
+                     (const float*)nullptr, a.n, (const int32_t*)nullptr)
+  if (a.causal && a.qpos) {   // a query subset with its positions: every tile masked
+#define AM_SCORE_Q(M)                                                                           \
+  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, true, M, false, true>), gs, bs, 0,     \
+                     a.stream, (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, \
+                     a.n, a.T, a.group, c2, a.heads, (const int32_t*)nullptr,                   \
+                     (const float*)nullptr, (const float*)nullptr, a.n, a.qpos)
+    if (a.mode == 0) AM_SCORE_Q(0); else if (a.mode == 1) AM_SCORE_Q(1); else AM_SCORE_Q(2);
+#undef AM_SCORE_Q
+  } else if (a.causal) {
     if (a.mode == 0) AM_SCORE(true, 0); else if (a.mode == 1) AM_SCORE(true, 1); else AM_SCORE(true, 2);
   } else {
     if (a.mode == 0) AM_SCORE(false, 0); else if (a.mode == 1) AM_SCORE(false, 1); else AM_SCORE(false, 2);
@@ -652,17 +672,55 @@ static void launch_key_mass_c(const KeyMassArgs& a) {
   float* o1 = nsplit > 1 ? a.part : a.kmax;
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, 3, true>), gs, bs, 0, a.stream,
                      (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, o1, a.n, a.t,
-                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)nullptr, qchunk);
+                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)nullptr, qchunk,
+                     (const int32_t*)nullptr);
   if (nsplit > 1)
     hipLaunchKernelGGL(colscore_reduce_kernel, gr, dim3(256), 0, a.stream, (const float*)a.part,
                        a.kmax, a.heads, a.t, nsplit, a.n, 3);
   float* o2 = nsplit > 1 ? a.part : a.kmean;
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, 1, true>), gs, bs, 0, a.stream,
                      (const T*)a.Q, (const T*)a.Ck, (const float2*)nullptr, o2, a.n, a.t,
-                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)a.kmax, qchunk);
+                     a.group, c2, a.heads, a.keypos, a.shift2, (const float*)a.kmax, qchunk,
+                     (const int32_t*)nullptr);
   if (nsplit > 1)
     hipLaunchKernelGGL(colscore_reduce_kernel, gr, dim3(256), 0, a.stream, (const float*)a.part,
                        a.kmean, a.heads, a.t, nsplit, a.n, 1);
+}
+
+// Selection statistic of keys with original positions (a shortlist) against all queries,
+// with the queries' row statistics over the same keys: the column pass with KPOS, split
+// over query chunks, then the fixed-order combination.
+template <typename T, int D, bool C, int M>
+static void launch_key_score_m(const KeyScoreArgs& a) {
+  const int BK = kScoreWaves * 32 * colscore_kb<T, D>();
+  int nsplit, qchunk;
+  key_mass_split(a.t, a.heads, a.n, BK, nsplit, qchunk);
+  const dim3 gs(((a.t + BK - 1) / BK) * a.heads, nsplit), bs(kScoreWaves * 64);
+  const float c2 = a.scale * kLog2e;
+  float* o = nsplit > 1 ? a.part : a.score;
+  hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M, true>), gs, bs, 0, a.stream,
+                     (const T*)a.Q, (const T*)a.Ck, a.rowstat, o, a.n, a.t, a.group, c2, a.heads,
+                     a.keypos, (const float*)nullptr, (const float*)nullptr, qchunk,
+                     (const int32_t*)nullptr);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(colscore_reduce_kernel, dim3((a.t + 255) / 256, a.heads), dim3(256), 0,
+                       a.stream, (const float*)a.part, a.score, a.heads, a.t, nsplit, a.n, M);
+}
+template <typename T, int D>
+static hipError_t launch_key_score_t(const KeyScoreArgs& a) {
+#define AM_KS(C)                                                                   \
+  do {                                                                             \
+    if (a.mode == 0) launch_key_score_m<T, D, C, 0>(a);                            \
+    else if (a.mode == 1) launch_key_score_m<T, D, C, 1>(a);                       \
+    else launch_key_score_m<T, D, C, 2>(a);                                        \
+  } while (0)
+  if (a.causal) AM_KS(true); else AM_KS(false);
+#undef AM_KS
+  return hipGetLastError();
+}
+hipError_t launch_key_score(const KeyScoreArgs& a) {
+  if (a.bf16) return a.d == 128 ? launch_key_score_t<bf16, 128>(a) : launch_key_score_t<bf16, 64>(a);
+  return a.d == 128 ? launch_key_score_t<float, 128>(a) : launch_key_score_t<float, 64>(a);
 }
 
 size_t key_mass_part_bytes(int64_t heads, int64_t n, int64_t t) {
@@ -718,6 +776,7 @@ static hipError_t launch_cmp_t(const CmpAttnArgs& a) {
   FlashParams fp;
   fp.Q = a.Q; fp.K = a.Ck; fp.Vt = a.Vt;
   fp.bias = a.bias; fp.keypos = a.keypos; fp.Y = a.Y; fp.tstat = a.causal ? a.tstat : nullptr;
+  fp.qpos = nullptr;
   fp.lse = a.lse; fp.rowstat = a.rowstat; fp.O = a.O; fp.rowres = a.rowres;
   fp.n = a.n; fp.Tk = a.t; fp.Tpad = Tpad; fp.group = a.group; fp.heads = a.heads;
   fp.c2 = a.scale * kLog2e;

@@ -160,3 +160,15 @@ def make_heldout_queries(w: Workload, heads=None, K=None, seed: int = 1):
         Q[kd] = Kf[i][src] + np.float32(0.5) * rng.standard_normal((kd.size, w.d), dtype=np.float32)
         out[i] = Q
     return bf16_bits(out) if w.dtype == "bf16" else out
+
+
+def query_subset(w: Workload, heads=None, s: int = 256, seed: int = 1):
+    """The two-pass method's random query subset: s distinct query indices per head, drawn
+    uniformly without replacement from its own seeded stream, ascending, int32 [h, s]."""
+    hs = range(w.heads) if heads is None else list(heads)
+    out = np.empty((len(hs), s), np.int32)
+    for i, h in enumerate(hs):
+        rng = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence([SEED0, 9, workload_index(w), h, seed])))
+        out[i] = np.sort(rng.choice(w.n, size=s, replace=False))
+    return out
