@@ -36,6 +36,9 @@ exactly before they arrive here):
       unbiased branch for the new tokens), combined by Eq. 5 in log space.
   F   the fast variants of the "Compaction" blog: beta by uniform redistribution of the
       missing mass (§Choosing beta) and direct values C_v = V[idx] (§Choosing C_v).
+  I   anchor + diversifier initialization (Latent Compaction §3.2): anchors by maximum
+      attention (Eq. 6) plus the first entry, diversifiers by farthest-first traversal
+      (Eq. 7).
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
 masked keys are excluded (exp(-inf) = 0), which equals the pseudocode's finfo.min fill
@@ -462,6 +465,50 @@ def select_two_pass(Q, K, sub, t, k_mult, scale, causal=False, group=1, mode="rm
                                      keypos=short)
     loc = select_top(key_score(st2, mode, n), t)
     return short[loc], lse_s
+
+
+def select_anchors(score, n_anchor):
+    """Anchors (Latent Compaction §3.2 "Budget Allocation"): the first document entry and the
+    n_anchor - 1 highest-scoring remaining entries (ties to the lower index), ascending.
+    `score` is the maximum teacher attention of Eq. 6 (key_score "max")."""
+    score = np.asarray(score, np.float64)
+    if n_anchor <= 1:
+        return np.array([0], dtype=np.int64)[:max(n_anchor, 0)]
+    rest = np.arange(1, score.size)
+    order = rest[np.lexsort((rest, -score[1:]))]
+    return np.sort(np.concatenate([[0], order[: n_anchor - 1]])).astype(np.int64)
+
+
+def farthest_first(K, start, M):
+    """Farthest-first traversal (Latent Compaction §3.2, Eq. 7; Gonzalez 1985): starting from
+    the index set `start`, repeatedly add the key i not yet chosen that maximizes
+    min_{j chosen} ||k_i - k_j||^2 (ties to the lower index) until M keys are chosen.
+    Returns the chosen indices in order (start first, in the given order)."""
+    K = np.asarray(K, np.float64)
+    seq = [int(j) for j in start]
+    chosen = np.zeros(K.shape[0], dtype=bool)
+    chosen[seq] = True
+    dist = np.full(K.shape[0], np.inf)
+    for j in seq:
+        dist = np.minimum(dist, ((K - K[j]) ** 2).sum(axis=1))
+    while len(seq) < min(M, K.shape[0]):
+        cand = np.where(chosen, -np.inf, dist)
+        j = int(np.argmax(cand))       # first index of the maximum
+        seq.append(j)
+        chosen[j] = True
+        dist = np.minimum(dist, ((K - K[j]) ** 2).sum(axis=1))
+    return np.array(seq, dtype=np.int64)
+
+
+def anchor_diverse_init(Q, K, M, scale, causal=False, group=1, n_anchor=None):
+    """Anchor + diversifier initialization of an M-slot budget: M / 4 anchors (at least
+    the first entry) by Eq. 6, the rest by farthest-first traversal (Eq. 7) from them.
+    Returns (order of selection, indices ascending)."""
+    n_anchor = max(1, M // 4) if n_anchor is None else n_anchor
+    _, _, st = full_cache_stats(Q, K, K, scale, causal, group, want_O=False)
+    anchors = select_anchors(key_score(st, "max", np.asarray(Q).shape[0]), n_anchor)
+    seq = farthest_first(K, anchors, M)
+    return seq, np.sort(seq)
 
 
 def direct_values(V, idx):

@@ -579,3 +579,59 @@ def test_rows_that_see_no_key_subset():
     np.testing.assert_allclose(lse[5:], l2, atol=1e-13)
     np.testing.assert_allclose(cs, s2, atol=1e-13)
     np.testing.assert_allclose(cq, q2, atol=1e-13)
+
+
+# --------------------------------------------------------------------------------------
+# anchor + diversifier initialization (Latent Compaction §3.2, Eq. 6-7)
+# --------------------------------------------------------------------------------------
+def test_select_anchors_first_entry_and_ties():
+    sc = np.array([0.0, 5.0, 3.0, 5.0, 9.0, 1.0])
+    np.testing.assert_array_equal(O.select_anchors(sc, 3), [0, 1, 4])   # 9, then 5 at 1 (lower)
+    np.testing.assert_array_equal(O.select_anchors(sc, 1), [0])
+    sc[0] = 100.0                                                       # entry 0 never counted twice
+    np.testing.assert_array_equal(O.select_anchors(sc, 2), [0, 4])
+
+
+def test_farthest_first_on_a_line():
+    """Points 0, 1, ..., 10 on a line, starting from {0}: 10 is farthest (100); then 5
+    (25 to both ends); then 2, 3, 7 and 8 tie at 4 and the lower index 2 wins; then 7 and 8
+    tie at 4 and 7 wins (worked by hand below)."""
+    K = np.arange(11.0)[:, None]
+    seq = O.farthest_first(K, [0], 5)
+    # after {0, 10, 5}: mindists 1:1 2:4 3:4 4:1 6:1 7:4 8:4 9:1 -> first max index 2
+    # after {0, 10, 5, 2}: 3:1 7:4 8:4 -> 7
+    np.testing.assert_array_equal(seq, [0, 10, 5, 2, 7])
+
+
+def _loop_fft(K, start, M):
+    seq = list(start)
+    while len(seq) < M:
+        best, bi = -1.0, -1
+        for i in range(len(K)):
+            if i in seq:
+                continue
+            dmin = min(float(((K[i] - K[j]) ** 2).sum()) for j in seq)
+            if dmin > best:
+                best, bi = dmin, i
+        seq.append(bi)
+    return seq
+
+
+def test_farthest_first_bruteforce_and_radius_monotone():
+    rng = np.random.default_rng(31)
+    K = rng.standard_normal((40, 5))
+    seq = O.farthest_first(K, [0, 7], 15)
+    np.testing.assert_array_equal(seq, _loop_fft(K, [0, 7], 15))
+    # the distance of each newly added key to the set never increases (Gonzalez)
+    radii = [min(((K[seq[s]] - K[j]) ** 2).sum() for j in seq[:s]) for s in range(2, 15)]
+    assert all(a >= b - 1e-12 for a, b in zip(radii, radii[1:]))
+
+
+def test_anchor_diverse_init_budget():
+    rng = np.random.default_rng(32)
+    Q, K, V = _qkv(64, 64, 8, rng)
+    seq, idx = O.anchor_diverse_init(Q, K, 16, 0.5, True, 1)
+    assert seq.size == 16 and np.unique(seq).size == 16 and 0 in seq
+    np.testing.assert_array_equal(idx, np.sort(seq))
+    _, _, st = O.full_cache_stats(Q, K, V, 0.5, True, 1, want_O=False)
+    np.testing.assert_array_equal(np.sort(seq[:4]), O.select_anchors(O.key_score(st, "max", 64), 4))
