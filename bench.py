@@ -13,7 +13,8 @@ cpu_baseline = the float64 oracle's full-cache statistics on a bounded sample of
 rows of head 0 (pairs/s), on the host cores.
 next = the adjacent rows, timed on the same inputs: the fast pipeline (redistributed beta,
 direct values), the two-pass method (256-query subset, shortlist of 4t keys, then the fast
-fits), the held-out evaluation, and attention through the compacted cache with 4096
+fits), the anchor + diversifier initialization of a t/4-slot budget, the held-out
+evaluation, and attention through the compacted cache with 4096
 appended tokens (GQA 4) merged in log space. The pairs/s of the pipelines count the
 full workload's visible pairs (the work they stand in for), not the pairs they score.
 
@@ -185,6 +186,9 @@ def main():
     sub = torch.from_numpy(synth.query_subset(w, None, 256)).cuda()
     ms_two = time_calls(torch, lambda: amc.compact_two_pass(dQ, dK, dV, sub, w.t, k_mult=4,
                                                             causal=w.causal, group=w.group), 3)
+    M_init = w.t // 4   # the anchor + diversifier share of a t-slot budget
+    ms_init = time_calls(torch, lambda: amc.init_anchor_diverse(dQ, dK, M_init, causal=w.causal,
+                                                                group=w.group), 2)
     m_new, g_new = 4096, 4
     n_new = g_new * m_new
     Qn = synth.make_heldout_queries(
@@ -246,6 +250,9 @@ def main():
             "two_pass_pipeline": {"ms_per_step": ms_two, "pairs_per_s": pairs / (ms_two * 1e-3),
                                   "options": "256 query subset, shortlist 4t, redistributed "
                                              "beta, direct values"},
+            "init_anchor_diverse": {"ms": ms_init, "M": M_init, "anchors": max(1, M_init // 4),
+                                    "note": "maximum-attention pass over all pairs + "
+                                            "farthest-first traversal"},
             "heldout_eval": {"ms": ms_eval, "queries_per_head": w.n,
                              "pairs_per_s": pairs / (ms_eval * 1e-3)},
             "cache_attention": {"ms": ms_cache, "slots": w.t, "appended": m_new,

@@ -71,7 +71,9 @@ enum {
   AM_HEAD_OK = 0,
   AM_HEAD_NNLS_NOT_CONVERGED = 1, /* KKT tolerance not reached within nnls_max_iter */
   AM_HEAD_CHOL_PIVOT = 2,         /* non-positive pivot in the ridge Cholesky */
-  AM_HEAD_NONFINITE = 4           /* a non-finite value reached a fit */
+  AM_HEAD_NONFINITE = 4,          /* a non-finite value reached a fit */
+  AM_HEAD_TIMEOUT = 8             /* workgroups of a multi-workgroup step did not meet in
+                                     time (the head's outputs are then incomplete) */
 };
 
 typedef struct {
@@ -209,6 +211,26 @@ size_t am_two_pass_workspace_bytes(const am_problem* p, int64_t t, int64_t s, in
                                    int32_t compact);
 
 /*
+ * am_init_anchor_diverse - anchor + diversifier initialization of an M-slot budget
+ * (Latent Compaction §3.2, "Budget Allocation"): n_anchor anchors are the first entry and
+ * the n_anchor - 1 other entries of highest maximum attention a_i = max_q softmax(s K q)_i
+ * over the n reference queries (Eq. 6, causal masks as for am_targets); the other
+ * M - n_anchor entries are added by farthest-first traversal (Eq. 7): each step adds the
+ * key, not yet chosen, whose smallest squared Euclidean distance to the chosen keys is
+ * largest (ties to the lower index; distances in fp32 from the input dtype).
+ * idx[h, M] receives the chosen entries in ascending order; order[h, M] (optional) the
+ * selection order (anchors ascending, then the traversal). Requires 1 <= n_anchor <= M
+ * <= min(T, 8192) and at most 16384 keys per workgroup of the traversal
+ * (AM_ERR_UNSUPPORTED otherwise). head_status (optional) gets AM_HEAD_TIMEOUT if the
+ * traversal's workgroups could not meet. Workspace: am_workspace_bytes(p, M,
+ * AM_CALL_INIT) (sized for n_anchor = M).
+ */
+am_status am_init_anchor_diverse(const am_problem* p, const void* Q, const void* K, int64_t M,
+                                 int64_t n_anchor, int32_t* idx, int32_t* order,
+                                 int32_t* head_status, void* ws, size_t ws_bytes,
+                                 am_stream_t stream);
+
+/*
  * am_eval_residuals - quality of a compacted cache on a set of queries (for instance a
  * held-out set; "Compaction" blog, §Choosing beta and §Choosing C_v report errors on
  * held-out queries): the full-cache targets of Q against K, V, then
@@ -288,7 +310,8 @@ typedef enum {
   AM_CALL_COMPACT = 4,
   AM_CALL_CACHE_ATTENTION = 5, /* the budget argument of am_workspace_bytes is m */
   AM_CALL_BETA_REDIST = 6,
-  AM_CALL_EVAL = 7
+  AM_CALL_EVAL = 7,
+  AM_CALL_INIT = 8             /* the budget argument is M */
 } am_call;
 
 /* Workspace bytes a call needs for problem p and budget t (0 if the problem is invalid). */

@@ -21,11 +21,11 @@ AM_F32, AM_BF16 = 0, 1
 SCORE_MODES = {"rms": 0, "mean": 1, "max": 2}
 MASS_MODES = {"relative": 0, "absolute": 1}
 (CALL_TARGETS, CALL_SELECT, CALL_FIT_BETA, CALL_FIT_VALUES, CALL_COMPACT, CALL_CACHE_ATTENTION,
- CALL_BETA_REDIST, CALL_EVAL) = range(8)
+ CALL_BETA_REDIST, CALL_EVAL, CALL_INIT) = range(9)
 BETA_MODES = {"nnls": 0, "redistribute": 1}
 VALUE_MODES = {"fit": 0, "direct": 1}
 ABI_VERSION = 2
-HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE = 1, 2, 4
+HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE, HEAD_TIMEOUT = 1, 2, 4, 8
 
 
 class AmProblem(ctypes.Structure):
@@ -83,6 +83,9 @@ _PROTOS = {
     "am_two_pass_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AmProblem), ctypes.c_int64,
                                                       ctypes.c_int64, ctypes.c_int32,
                                                       ctypes.c_int32]),
+    "am_init_anchor_diverse": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, ctypes.c_int64,
+                                              ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t,
+                                              _P]),
     "am_eval_residuals": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
 }
@@ -454,3 +457,21 @@ def compact_two_pass(Q, K, V, sub, t, *, k_mult=4, score="rms", causal=False, gr
                                      _ptr(out["resid"]), _ptr(ws), nb, _stream()),
            "am_compact_two_pass")
     return out
+
+
+def init_anchor_diverse(Q, K, M, *, n_anchor=None, causal=False, group=1, scale=None):
+    """Anchor + diversifier initialization of an M-slot budget (n_anchor defaults to M // 4,
+    at least 1). Returns idx [h, M] ascending, the selection order [h, M] and status [h]."""
+    torch = _torch()
+    _need(Q, "Q"); _need(K, "K")
+    p = make_problem(Q, K, causal=causal, group=group, scale=scale)
+    na = max(1, M // 4) if n_anchor is None else int(n_anchor)
+    dev = Q.device
+    idx = torch.empty((p.heads, M), dtype=torch.int32, device=dev)
+    order = torch.empty((p.heads, M), dtype=torch.int32, device=dev)
+    status = torch.empty((p.heads,), dtype=torch.int32, device=dev)
+    ws, nb = _workspace(p, M, CALL_INIT, dev)
+    _check(lib().am_init_anchor_diverse(ctypes.byref(p), _ptr(Q), _ptr(K), M, na, _ptr(idx),
+                                        _ptr(order), _ptr(status), _ptr(ws), nb, _stream()),
+           "am_init_anchor_diverse")
+    return idx, order, status

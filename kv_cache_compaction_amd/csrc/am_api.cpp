@@ -186,6 +186,8 @@ size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
     case AM_CALL_BETA_REDIST: return ws_fast(p, t, 0);
     case AM_CALL_EVAL: return ws_fast(p, t, p->T);
     case AM_CALL_CACHE_ATTENTION: return 0;
+    case AM_CALL_INIT:
+      return t > kInitMaxM ? 0 : init_ws_bytes(p->heads, p->n, p->T, p->d, esize(p), t, t);
   }
   return 0;
 }
@@ -433,6 +435,31 @@ am_status am_compact_two_pass(const am_problem* p, const void* Q, const void* K,
                        hipSuccess)
     return AM_ERR_DEVICE;
   return AM_OK;
+}
+
+am_status am_init_anchor_diverse(const am_problem* p, const void* Q, const void* K, int64_t M,
+                                 int64_t n_anchor, int32_t* idx, int32_t* order,
+                                 int32_t* head_status, void* ws, size_t ws_bytes,
+                                 am_stream_t stream) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, M)) != AM_OK) return st;
+  if (n_anchor < 1 || n_anchor > M) return AM_ERR_INVALID_ARG;
+  if (M > kInitMaxM || init_max_chunk((int)p->heads, (int)p->T) > kInitMaxChunk)
+    return AM_ERR_UNSUPPORTED;
+  if (!Q || !K || !idx) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(K) || !al16(idx) || (order && !al16(order)) ||
+      (head_status && !al16(head_status)) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < init_ws_bytes(p->heads, p->n, p->T, p->d, esize(p), M, M))
+    return AM_ERR_WORKSPACE;
+  InitArgs a;
+  a.Q = Q; a.K = K; a.idx = idx; a.order = order; a.head_status = head_status;
+  a.heads = (int)p->heads; a.n = (int)p->n; a.T = (int)p->T; a.d = (int)p->d;
+  a.group = p->group; a.M = (int)M; a.na = (int)n_anchor;
+  a.causal = p->causal != 0; a.bf16 = p->dtype == AM_BF16; a.scale = p->scale;
+  a.ws = ws; a.stream = (hipStream_t)stream;
+  return from_hip(launch_init_anchor_diverse(a));
 }
 
 am_status am_eval_residuals(const am_problem* p, const void* Q, const void* K, const void* V,

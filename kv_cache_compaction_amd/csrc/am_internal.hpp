@@ -12,6 +12,7 @@ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int AM_HEAD_NNLS_BIT = 1;
 constexpr int AM_HEAD_CHOL_BIT = 2;
 constexpr int AM_HEAD_NONFINITE_BIT = 4;
+constexpr int AM_HEAD_TIMEOUT_BIT = 8;
 // largest compacted size the fits support (the NNLS keeps a t-vector in LDS)
 constexpr int kMaxFitT = 8192;
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -94,6 +95,25 @@ struct TwoPassArgs {
 };
 hipError_t launch_two_pass(const TwoPassArgs& a);
 hipError_t launch_fill_f32(float* p, long long count, float v, hipStream_t st);
+
+// Anchor + diversifier initialization of an M-slot budget (na anchors, the first entry
+// among them); idx [h, M] ascending, order [h, M] the selection order (may be null);
+// workspace init_ws_bytes
+struct InitArgs {
+  const void* Q; const void* K;
+  int32_t* idx; int32_t* order; int32_t* head_status;
+  int heads, n, T, d, group, M, na;
+  bool causal, bf16;
+  float scale;
+  void* ws;
+  hipStream_t stream;
+};
+hipError_t launch_init_anchor_diverse(const InitArgs& a);
+size_t init_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t M,
+                     int64_t na);
+int init_max_chunk(int heads, int T);   // keys per workgroup of the traversal (LDS floats)
+constexpr int kInitMaxChunk = 16384;
+constexpr int kInitMaxM = 8192;
 size_t two_pass_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t s,
                          int64_t kt);
 
