@@ -39,6 +39,9 @@ exactly before they arrive here):
   I   anchor + diversifier initialization (Latent Compaction §3.2): anchors by maximum
       attention (Eq. 6) plus the first entry, diversifiers by farthest-first traversal
       (Eq. 7).
+  G   stage-1 attention fitting (Latent Compaction §3.3, Eq. 8; App. A.2 sampling and
+      AdamW): the compacted keys, values and biases move by AdamW on the standardized
+      output and log-normalizer errors of sampled query positions.
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
 masked keys are excluded (exp(-inf) = 0), which equals the pseudocode's finfo.min fill
@@ -509,6 +512,100 @@ def anchor_diverse_init(Q, K, M, scale, causal=False, group=1, n_anchor=None):
     anchors = select_anchors(key_score(st, "max", np.asarray(Q).shape[0]), n_anchor)
     seq = farthest_first(K, anchors, M)
     return seq, np.sort(seq)
+
+
+def teacher_scales(O_full, lse_full, group):
+    """Per query head g (rows i with i % group == g): the population standard deviation of
+    the full-cache outputs over positions and channels, and of the log-normalizers over
+    positions, each floored at 1e-4 (Latent Compaction §3.3: fixed teacher statistics).
+    The means cancel in Eq. 8's differences and are not needed."""
+    O_full = np.asarray(O_full, np.float64)
+    lse_full = np.asarray(lse_full, np.float64)
+    g = np.arange(O_full.shape[0]) % group
+    sa = np.array([max(O_full[g == q].std(), 1e-4) for q in range(group)])
+    sz = np.array([max(lse_full[g == q].std(), 1e-4) for q in range(group)])
+    return sa, sz
+
+
+def stage1_rows(positions, group):
+    """The query rows of sampled positions: every query head of each position."""
+    positions = np.asarray(positions, dtype=np.int64)
+    return (positions[:, None] * group + np.arange(group)[None, :]).ravel()
+
+
+def stage1_loss_grad(Q, rows, Ck, Cv, b, keypos, O_full, lse_full, sa, sz, scale, causal=False,
+                     group=1):
+    """Eq. 8 on the query rows `rows` and its gradient with respect to (Ck, Cv, b).
+
+    A = softmax(l) Cv and log Z = logsumexp(l) with l = scale Ck q + b over the visible
+    slots (Eq. 2-4); L = mean over rows and channels of ((A - A_full) / sa_g)^2 + mean over
+    rows of ((log Z - log Z_full) / sz_g)^2, g the row's query head. Rows that see no slot
+    are left out of both means. Returns (L, dCk, dCv, db)."""
+    Q = np.asarray(Q, np.float64)[rows]
+    Ck = np.asarray(Ck, np.float64)
+    Cv = np.asarray(Cv, np.float64)
+    b = np.asarray(b, np.float64)
+    Y = np.asarray(O_full, np.float64)[rows]
+    lz_t = np.asarray(lse_full, np.float64)[rows]
+    g = np.asarray(rows) % group
+    vis = visible(np.asarray(rows), np.asarray(keypos), causal, group)
+    keep = vis.any(axis=1)
+    Q, Y, lz_t, g, vis = Q[keep], Y[keep], lz_t[keep], g[keep], vis[keep]
+    N, d = Q.shape[0], Cv.shape[1]
+    s = np.where(vis, scale * Q @ Ck.T + b[None, :], -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    P = e / z
+    lz = (m + np.log(z))[:, 0]
+    A = P @ Cv
+    wa = 1.0 / sa[g] ** 2
+    wz = 1.0 / sz[g] ** 2
+    L = float((wa[:, None] * (A - Y) ** 2).sum() / (N * d) + (wz * (lz - lz_t) ** 2).sum() / N)
+    dA = 2.0 * wa[:, None] * (A - Y) / (N * d)
+    dlz = 2.0 * wz * (lz - lz_t) / N
+    dCv = P.T @ dA
+    dP = dA @ Cv.T
+    dS = P * (dP - (dA * A).sum(axis=1, keepdims=True) + dlz[:, None])
+    db = dS.sum(axis=0)
+    dCk = scale * dS.T @ Q
+    return L, dCk, dCv, db
+
+
+def adamw_step(theta, grad, m, v, step, lr, wd, beta1=0.9, beta2=0.999, eps=1e-8):
+    """One AdamW update (decoupled weight decay first), step counted from 1. Returns the new
+    (theta, m, v)."""
+    m = beta1 * m + (1.0 - beta1) * grad
+    v = beta2 * v + (1.0 - beta2) * grad * grad
+    mh = m / (1.0 - beta1 ** step)
+    vh = v / (1.0 - beta2 ** step)
+    theta = theta * (1.0 - lr * wd) - lr * mh / (np.sqrt(vh) + eps)
+    return theta, m, v
+
+
+def stage1_fit(Q, Ck, Cv, b, keypos, O_full, lse_full, samples, scale, causal=False, group=1,
+               lr=3e-3, wd=1e-2, trainable=None):
+    """Stage-1 attention fitting: for each row of `samples` (sampled positions of one update),
+    Eq. 8's gradient on those positions' query rows and one AdamW update of the trainable
+    slots' keys, values and biases (frozen slots keep theirs). Returns (Ck, Cv, b, losses)."""
+    sa, sz = teacher_scales(O_full, lse_full, group)
+    params = [np.asarray(x, np.float64).copy() for x in (Ck, Cv, b)]
+    mom = [np.zeros_like(x) for x in params]
+    vel = [np.zeros_like(x) for x in params]
+    t = params[0].shape[0]
+    mask = np.ones(t, dtype=bool) if trainable is None else np.asarray(trainable, dtype=bool)
+    losses = []
+    for k, pos in enumerate(samples, start=1):
+        L, *grads = stage1_loss_grad(Q, stage1_rows(pos, group), *params, keypos, O_full,
+                                     lse_full, sa, sz, scale, causal, group)
+        losses.append(L)
+        for i in range(3):
+            th, mm, vv = adamw_step(params[i], grads[i], mom[i], vel[i], k, lr, wd)
+            sel = mask if params[i].ndim == 1 else mask[:, None]
+            params[i] = np.where(sel, th, params[i])
+            mom[i] = np.where(sel, mm, mom[i])
+            vel[i] = np.where(sel, vv, vel[i])
+    return params[0], params[1], params[2], np.array(losses)
 
 
 def direct_values(V, idx):

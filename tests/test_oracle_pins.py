@@ -635,3 +635,82 @@ def test_anchor_diverse_init_budget():
     np.testing.assert_array_equal(idx, np.sort(seq))
     _, _, st = O.full_cache_stats(Q, K, V, 0.5, True, 1, want_O=False)
     np.testing.assert_array_equal(np.sort(seq[:4]), O.select_anchors(O.key_score(st, "max", 64), 4))
+
+
+# --------------------------------------------------------------------------------------
+# stage-1 attention fitting (Latent Compaction §3.3 Eq. 8, AdamW)
+# --------------------------------------------------------------------------------------
+def _stage1_case(rng, causal=True, group=2):
+    T, d, t = 40, 6, 9
+    n = group * T
+    Q, K, V = _qkv(n, T, d, rng)
+    lse, Of, _ = O.full_cache_stats(Q, K, V, 0.5, causal, group)
+    keypos = np.sort(np.concatenate([[0], rng.choice(np.arange(1, T), t - 1, replace=False)]))
+    return Q, K, V, lse, Of, keypos
+
+
+@pytest.mark.parametrize("causal,group", [(True, 2), (False, 1)])
+def test_stage1_gradient_matches_finite_differences(causal, group):
+    rng = np.random.default_rng(41)
+    Q, K, V, lse, Of, kp = _stage1_case(rng, causal, group)
+    Ck = K[kp] + 0.1 * rng.standard_normal(K[kp].shape)
+    Cv = V[kp] + 0.1 * rng.standard_normal(V[kp].shape)
+    b = 0.3 * rng.standard_normal(kp.size)
+    sa, sz = O.teacher_scales(Of, lse, group)
+    rows = O.stage1_rows(rng.integers(0, Q.shape[0] // group, size=7), group)
+    L, dCk, dCv, db = O.stage1_loss_grad(Q, rows, Ck, Cv, b, kp, Of, lse, sa, sz, 0.5, causal, group)
+    h = 1e-6
+    for X, dX in ((Ck, dCk), (Cv, dCv), (b, db)):
+        for idx in [tuple(rng.integers(0, s) for s in X.shape) for _ in range(6)]:
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args = [Ck, Cv, b]
+            which = [Ck is X, Cv is X, b is X].index(True)
+            args_p, args_m = list(args), list(args)
+            args_p[which], args_m[which] = Xp, Xm
+            Lp = O.stage1_loss_grad(Q, rows, *args_p, kp, Of, lse, sa, sz, 0.5, causal, group)[0]
+            Lm = O.stage1_loss_grad(Q, rows, *args_m, kp, Of, lse, sa, sz, 0.5, causal, group)[0]
+            assert abs((Lp - Lm) / (2 * h) - dX[idx]) <= 1e-6 * (1 + abs(dX[idx]))
+
+
+def test_stage1_loss_is_zero_on_the_full_cache():
+    """With every key as a slot, the original values and zero biases, the compacted branch
+    is the full cache: Eq. 8 is zero and so is its gradient."""
+    rng = np.random.default_rng(42)
+    Q, K, V, lse, Of, _ = _stage1_case(rng)
+    kp = np.arange(K.shape[0])
+    sa, sz = O.teacher_scales(Of, lse, 2)
+    L, dCk, dCv, db = O.stage1_loss_grad(Q, np.arange(Q.shape[0]), K, V, np.zeros(kp.size), kp,
+                                         Of, lse, sa, sz, 0.5, True, 2)
+    assert L < 1e-24 and np.abs(dCk).max() < 1e-12 and np.abs(dCv).max() < 1e-12
+
+
+def test_adamw_first_step_closed_form():
+    """From zero moments the bias-corrected ratio is g / (|g| + eps): each coordinate moves
+    by lr times its gradient's sign (after the decoupled decay)."""
+    th = np.array([1.0, -2.0, 0.5])
+    g = np.array([3.0, -1e-3, 0.0])
+    new, m, v = O.adamw_step(th, g, np.zeros(3), np.zeros(3), 1, 1e-2, 0.1)
+    ref = th * (1 - 1e-3) - 1e-2 * g / (np.abs(g) + 1e-8)
+    np.testing.assert_allclose(new, ref, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(m, 0.1 * g)
+    np.testing.assert_allclose(v, 0.001 * g * g)
+
+
+def test_stage1_fit_lowers_the_loss_and_freezes():
+    rng = np.random.default_rng(43)
+    Q, K, V, lse, Of, kp = _stage1_case(rng)
+    samples = rng.integers(0, Q.shape[0] // 2, size=(60, 16))
+    frozen = np.zeros(kp.size, dtype=bool)
+    frozen[[0, 3]] = True
+    Ck, Cv, b, losses = O.stage1_fit(Q, K[kp], V[kp], np.zeros(kp.size), kp, Of, lse, samples,
+                                     0.5, True, 2, lr=1e-2, trainable=~frozen)
+    sa, sz = O.teacher_scales(Of, lse, 2)
+    rows = np.arange(Q.shape[0])
+    before = O.stage1_loss_grad(Q, rows, K[kp], V[kp], np.zeros(kp.size), kp, Of, lse, sa, sz,
+                                0.5, True, 2)[0]
+    after = O.stage1_loss_grad(Q, rows, Ck, Cv, b, kp, Of, lse, sa, sz, 0.5, True, 2)[0]
+    assert after < 0.8 * before
+    np.testing.assert_array_equal(Ck[frozen], K[kp][frozen])
+    np.testing.assert_array_equal(b[frozen], 0.0)
