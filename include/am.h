@@ -301,6 +301,52 @@ am_status am_attention_merge(int64_t rows, int64_t d, const float* O1, const flo
                              const float* O2, const float* lse2, float* out, float* lse_out,
                              am_stream_t stream);
 
+/*
+ * Stage-1 attention fitting (Latent Compaction §3.3, Eq. 8; App. A.2): the compacted keys,
+ * values and biases of a cache become trainable f32 parameters, fitted so that the
+ * compacted attention (Eq. 2-4) reproduces the full cache's outputs and log-normalizers on
+ * sampled query positions. Here p->T is the slot count t, p->n the reference queries per
+ * head (a multiple of group; row i sits at position i / group), p->dtype the dtype of Q;
+ * p->causal masks slot j from row i unless keypos[h, j] <= i / group.
+ * Inputs: Q [h, n, d]; O_full [h, n, d] f32 and lse_full [h, n] f32, the full cache's
+ * attention output and log-normalizer of every row (am_targets computes both);
+ * samples [S] (one evaluation) or [steps, S] (fit) int32 positions in [0, n / group)
+ * (values outside are clamped); each update uses every query head of its S positions
+ * (N = S * group rows).
+ * The loss of one update, per head: with g the row's query head and sa_g, sz_g the
+ * population standard deviations of O_full over that query head's rows and channels and of
+ * lse_full over its rows (both floored at 1e-4, computed once per call),
+ *   L = mean over rows and channels of ((A - O_full) / sa_g)^2
+ *     + mean over rows of ((log Z - lse_full) / sz_g)^2,
+ * where A = softmax(l) Cv, log Z = logsumexp(l), l = scale Ck q + bias over visible slots.
+ * Rows that see no slot are left out of both means (L = 0 if none is left).
+ * Parameters: Ck, Cv [h, t, d] f32 and bias [h, t] f32.
+ */
+
+/* One evaluation at samples [S]: loss_out [h] (optional) and the gradients
+ * gCk, gCv [h, t, d] and gbias [h, t] of L with respect to Ck, Cv and bias. */
+am_status am_stage1_loss_grad(const am_problem* p, const void* Q, const float* O_full,
+                              const float* lse_full, const int32_t* keypos,
+                              const int32_t* samples, int64_t S, const float* Ck,
+                              const float* Cv, const float* bias, float* loss_out, float* gCk,
+                              float* gCv, float* gbias, void* ws, size_t ws_bytes,
+                              am_stream_t stream);
+
+/* `steps` AdamW updates (beta1 0.9, beta2 0.999, eps 1e-8, bias-corrected moments, decoupled
+ * weight decay theta <- theta (1 - lr wd) before the Adam step, constant lr; moments start
+ * at zero) of Ck, Cv and bias IN PLACE, update k on the positions samples[k, :].
+ * trainable [h, t] uint8 (optional, NULL trains every slot): slots with 0 keep their key,
+ * value and bias. loss_out [steps, h] (optional) receives each update's loss, evaluated
+ * before that update. */
+am_status am_fit_stage1(const am_problem* p, const void* Q, const float* O_full,
+                        const float* lse_full, const int32_t* keypos, const int32_t* samples,
+                        int64_t S, int64_t steps, const uint8_t* trainable, float lr, float wd,
+                        float* Ck, float* Cv, float* bias, float* loss_out, void* ws,
+                        size_t ws_bytes, am_stream_t stream);
+
+/* Workspace bytes of am_stage1_loss_grad and am_fit_stage1 for S positions per update. */
+size_t am_stage1_workspace_bytes(const am_problem* p, int64_t S);
+
 /* Which call a workspace size is for. */
 typedef enum {
   AM_CALL_TARGETS = 0,

@@ -24,7 +24,7 @@ MASS_MODES = {"relative": 0, "absolute": 1}
  CALL_BETA_REDIST, CALL_EVAL, CALL_INIT) = range(9)
 BETA_MODES = {"nnls": 0, "redistribute": 1}
 VALUE_MODES = {"fit": 0, "direct": 1}
-ABI_VERSION = 2
+ABI_VERSION = 3
 HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE, HEAD_TIMEOUT = 1, 2, 4, 8
 
 
@@ -88,6 +88,13 @@ _PROTOS = {
                                               _P]),
     "am_eval_residuals": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
+    "am_stage1_loss_grad": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P,
+                                           ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]),
+    "am_fit_stage1": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, ctypes.c_int64,
+                                     ctypes.c_int64, _P, ctypes.c_float, ctypes.c_float, _P, _P,
+                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "am_stage1_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AmProblem), ctypes.c_int64]),
 }
 
 
@@ -475,3 +482,73 @@ def init_anchor_diverse(Q, K, M, *, n_anchor=None, causal=False, group=1, scale=
                                         _ptr(order), _ptr(status), _ptr(ws), nb, _stream()),
            "am_init_anchor_diverse")
     return idx, order, status
+
+
+def _stage1_setup(Q, O_full, lse_full, keypos, Ck, Cv, bias, samples, causal, group, scale):
+    torch = _torch()
+    _need(Q, "Q")
+    h, n, d = Q.shape
+    _need(O_full, "O_full", dtype=torch.float32, shape=(h, n, d))
+    _need(lse_full, "lse_full", dtype=torch.float32, shape=(h, n))
+    _need(Ck, "Ck", dtype=torch.float32)
+    t = Ck.shape[1]
+    if Ck.dim() != 3 or Ck.shape[0] != h or Ck.shape[2] != d:
+        raise ValueError("Ck must be [h, t, d]")
+    _need(Cv, "Cv", dtype=torch.float32, shape=(h, t, d))
+    _need(bias, "bias", dtype=torch.float32, shape=(h, t))
+    if keypos is not None:
+        _need(keypos, "keypos", dtype=torch.int32, shape=(h, t))
+    _need(samples, "samples", dtype=torch.int32)
+    S = samples.shape[-1]
+    p = AmProblem(h, n, t, d, int(bool(causal)), int(group),
+                  float(1.0 / math.sqrt(d) if scale is None else scale), _dtype_code(Q))
+    nb = int(lib().am_stage1_workspace_bytes(ctypes.byref(p), S))
+    if nb == 0:
+        raise AmError(AM_ERR_INVALID_ARG, "am_stage1_workspace_bytes")
+    ws = torch.empty(nb, dtype=torch.uint8, device=Q.device)
+    return p, S, ws, nb
+
+
+def stage1_loss_grad(Q, O_full, lse_full, samples, Ck, Cv, bias, *, keypos=None, causal=False,
+                     group=1, scale=None):
+    """Stage-1 loss [h] and its gradients (dCk, dCv, dbias) at the positions samples [S]
+    (int32), for f32 parameters Ck, Cv [h, t, d] and bias [h, t]."""
+    torch = _torch()
+    p, S, ws, nb = _stage1_setup(Q, O_full, lse_full, keypos, Ck, Cv, bias, samples, causal,
+                                 group, scale)
+    if samples.dim() != 1:
+        raise ValueError("samples must be [S]")
+    loss = torch.empty((p.heads,), dtype=torch.float32, device=Q.device)
+    gCk, gCv, gb = torch.empty_like(Ck), torch.empty_like(Cv), torch.empty_like(bias)
+    _check(lib().am_stage1_loss_grad(ctypes.byref(p), _ptr(Q), _ptr(O_full), _ptr(lse_full),
+                                     _ptr(keypos), _ptr(samples), S, _ptr(Ck), _ptr(Cv),
+                                     _ptr(bias), _ptr(loss), _ptr(gCk), _ptr(gCv), _ptr(gb),
+                                     _ptr(ws), nb, _stream()), "am_stage1_loss_grad")
+    return loss, gCk, gCv, gb
+
+
+def fit_stage1(Q, O_full, lse_full, samples, Ck, Cv, bias, *, keypos=None, trainable=None,
+               lr=3e-3, wd=1e-2, causal=False, group=1, scale=None):
+    """Stage-1 fitting: one AdamW update per row of samples [steps, S] (int32 positions).
+    Ck, Cv, bias are copied to f32 and returned fitted with the per-update losses
+    [steps, h]; trainable [h, t] (bool or uint8) freezes the slots where it is 0."""
+    torch = _torch()
+    Ck = Ck.to(torch.float32).contiguous().clone()
+    Cv = Cv.to(torch.float32).contiguous().clone()
+    bias = bias.to(torch.float32).contiguous().clone()
+    p, S, ws, nb = _stage1_setup(Q, O_full, lse_full, keypos, Ck, Cv, bias, samples, causal,
+                                 group, scale)
+    if samples.dim() != 2:
+        raise ValueError("samples must be [steps, S]")
+    steps = samples.shape[0]
+    tr = None
+    if trainable is not None:
+        tr = trainable.to(torch.uint8).contiguous()
+        if tuple(tr.shape) != (p.heads, p.T):
+            raise ValueError("trainable must be [h, t]")
+    loss = torch.empty((steps, p.heads), dtype=torch.float32, device=Q.device)
+    _check(lib().am_fit_stage1(ctypes.byref(p), _ptr(Q), _ptr(O_full), _ptr(lse_full),
+                               _ptr(keypos), _ptr(samples), S, steps, _ptr(tr), float(lr),
+                               float(wd), _ptr(Ck), _ptr(Cv), _ptr(bias), _ptr(loss), _ptr(ws),
+                               nb, _stream()), "am_fit_stage1")
+    return Ck, Cv, bias, loss

@@ -11,7 +11,7 @@ using namespace amc;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -550,6 +550,85 @@ am_status am_attention_merge(int64_t rows, int64_t d, const float* O1, const flo
   ma.O1 = O1; ma.lse1 = lse1; ma.O2 = O2; ma.lse2 = lse2; ma.out = out; ma.lse = lse_out;
   ma.rows = (long long)rows; ma.d = (int)d; ma.stream = (hipStream_t)stream;
   return from_hip(launch_attention_merge(ma));
+}
+
+namespace {
+// Stage-1 fitting: p->T is the slot count t; query row i sits at position i / group
+am_status check_stage1(const am_problem* p, const void* Q, const float* O_full,
+                       const float* lse_full, const int32_t* keypos, const int32_t* samples,
+                       int64_t S, const void* ws) {
+  am_status st = check_cache_problem(p);
+  if (st != AM_OK) return st;
+  if (p->n % p->group != 0 || S < 1 || S * p->group > ((int64_t)1 << 24)) return AM_ERR_INVALID_ARG;
+  if (!Q || !O_full || !lse_full || !samples || (p->causal && !keypos)) return AM_ERR_INVALID_ARG;
+  if (!al16(Q) || !al16(O_full) || !al16(lse_full) || !al16(samples) ||
+      (keypos && !al16(keypos)) || (ws && !al16(ws)))
+    return AM_ERR_INVALID_ARG;
+  return AM_OK;
+}
+
+Stage1Args stage1_args(const am_problem* p, const void* Q, const float* O_full,
+                       const float* lse_full, const int32_t* keypos, const int32_t* samples,
+                       int64_t S, void* ws, am_stream_t stream) {
+  Stage1Args a;
+  memset(&a, 0, sizeof a);
+  a.Q = Q; a.O_full = O_full; a.lse_full = lse_full; a.keypos = p->causal ? keypos : nullptr;
+  a.samples = samples;
+  a.heads = (int)p->heads; a.n = (int)p->n; a.d = (int)p->d; a.group = p->group;
+  a.t = (int)p->T; a.S = (int)S;
+  a.causal = p->causal != 0; a.bf16 = p->dtype == AM_BF16; a.scale = p->scale;
+  a.ws = ws; a.stream = (hipStream_t)stream;
+  return a;
+}
+}  // namespace
+
+size_t am_stage1_workspace_bytes(const am_problem* p, int64_t S) {
+  if (check_cache_problem(p) != AM_OK || S < 1 || p->n % p->group != 0 ||
+      S * p->group > ((int64_t)1 << 24))
+    return 0;
+  return stage1_ws_bytes(p->heads, p->T, p->d, S, p->group);
+}
+
+am_status am_stage1_loss_grad(const am_problem* p, const void* Q, const float* O_full,
+                              const float* lse_full, const int32_t* keypos,
+                              const int32_t* samples, int64_t S, const float* Ck,
+                              const float* Cv, const float* bias, float* loss_out, float* gCk,
+                              float* gCv, float* gbias, void* ws, size_t ws_bytes,
+                              am_stream_t stream) {
+  am_status st = check_stage1(p, Q, O_full, lse_full, keypos, samples, S, ws);
+  if (st != AM_OK) return st;
+  if (!Ck || !Cv || !bias || !gCk || !gCv || !gbias) return AM_ERR_INVALID_ARG;
+  if (!al16(Ck) || !al16(Cv) || !al16(bias) || !al16(gCk) || !al16(gCv) || !al16(gbias) ||
+      (loss_out && !al16(loss_out)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < stage1_ws_bytes(p->heads, p->T, p->d, S, p->group))
+    return AM_ERR_WORKSPACE;
+  Stage1Args a = stage1_args(p, Q, O_full, lse_full, keypos, samples, S, ws, stream);
+  a.Ck = (float*)Ck; a.Cv = (float*)Cv; a.b = (float*)bias; a.loss = loss_out;
+  a.gCk = gCk; a.gCv = gCv; a.gb = gbias; a.steps = 0;
+  return from_hip(launch_stage1(a));
+}
+
+am_status am_fit_stage1(const am_problem* p, const void* Q, const float* O_full,
+                        const float* lse_full, const int32_t* keypos, const int32_t* samples,
+                        int64_t S, int64_t steps, const uint8_t* trainable, float lr, float wd,
+                        float* Ck, float* Cv, float* bias, float* loss_out, void* ws,
+                        size_t ws_bytes, am_stream_t stream) {
+  am_status st = check_stage1(p, Q, O_full, lse_full, keypos, samples, S, ws);
+  if (st != AM_OK) return st;
+  if (steps < 1 || steps > (1 << 20) || !(lr >= 0.f) || !isfinite(lr) || !(wd >= 0.f) ||
+      !isfinite(wd))
+    return AM_ERR_INVALID_ARG;
+  if (!Ck || !Cv || !bias) return AM_ERR_INVALID_ARG;
+  if (!al16(Ck) || !al16(Cv) || !al16(bias) || (trainable && !al16(trainable)) ||
+      (loss_out && !al16(loss_out)))
+    return AM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < stage1_ws_bytes(p->heads, p->T, p->d, S, p->group))
+    return AM_ERR_WORKSPACE;
+  Stage1Args a = stage1_args(p, Q, O_full, lse_full, keypos, samples, S, ws, stream);
+  a.Ck = Ck; a.Cv = Cv; a.b = bias; a.loss = loss_out; a.trainable = trainable;
+  a.steps = (int)steps; a.lr = lr; a.wd = wd;
+  return from_hip(launch_stage1(a));
 }
 
 }  // extern "C"

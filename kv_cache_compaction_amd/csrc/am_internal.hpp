@@ -112,6 +112,23 @@ hipError_t launch_init_anchor_diverse(const InitArgs& a);
 size_t init_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t M,
                      int64_t na);
 int init_max_chunk(int heads, int T);   // keys per workgroup of the traversal (LDS floats)
+
+// Stage-1 attention fitting: steps AdamW updates of Ck, Cv, b (f32, updated in place) on
+// the sampled positions samples [steps, S]; with steps == 0 one evaluation of the loss and
+// its gradients (gCk, gCv, gb) at samples [S]
+struct Stage1Args {
+  const void* Q; const float* O_full; const float* lse_full; const int32_t* keypos;
+  const uint8_t* trainable; const int32_t* samples;
+  float* Ck; float* Cv; float* b; float* loss;
+  float* gCk; float* gCv; float* gb;
+  int heads, n, d, group, t, S, steps;
+  bool causal, bf16;
+  float scale, lr, wd;
+  void* ws;
+  hipStream_t stream;
+};
+hipError_t launch_stage1(const Stage1Args& a);
+size_t stage1_ws_bytes(int64_t heads, int64_t t, int64_t d, int64_t S, int64_t group);
 constexpr int kInitMaxChunk = 16384;
 constexpr int kInitMaxM = 8192;
 size_t two_pass_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t s,

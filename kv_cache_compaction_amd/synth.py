@@ -172,3 +172,13 @@ def query_subset(w: Workload, heads=None, s: int = 256, seed: int = 1):
             np.random.SeedSequence([SEED0, 9, workload_index(w), h, seed])))
         out[i] = np.sort(rng.choice(w.n, size=s, replace=False))
     return out
+
+
+def stage1_samples(n_pos: int, steps: int, S: int = 128, pool: int = 4096, seed: int = 1):
+    """Positions of the stage-1 updates (Latent Compaction App. A.2): a pool of at most
+    `pool` evenly spaced positions (floor(k * n_pos / pool)) out of n_pos, then S positions
+    per update drawn uniformly with replacement from it, from their own seeded stream,
+    shared by every head. Returns int32 [steps, S]."""
+    base = np.arange(n_pos) if n_pos <= pool else (np.arange(pool) * n_pos) // pool
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED0, 10, n_pos, seed])))
+    return base[rng.integers(0, base.size, size=(steps, S))].astype(np.int32)

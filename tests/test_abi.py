@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert amc.lib().am_abi_version() == amc.ABI_VERSION == 2
+    assert amc.lib().am_abi_version() == amc.ABI_VERSION == 3
     assert amc.status_str(0) == "ok"
     assert amc.status_str(-3) == "workspace too small"
     assert amc.status_str(7) == "unknown status"
@@ -177,3 +177,31 @@ def test_option_modes_validated():
     assert L.am_compact_head(ctypes.byref(p), FAKE, FAKE, FAKE, 16, ctypes.byref(o), FAKE, FAKE,
                              FAKE, FAKE, None, None, None, None, None, FAKE, 1 << 40,
                              None) == amc.AM_ERR_INVALID_ARG
+
+
+def test_stage1_validation():
+    L = amc.lib()
+    p = P(n=256, T=32, group=2, causal=1)
+    assert L.am_stage1_workspace_bytes(ctypes.byref(p), 16) > 0
+    assert L.am_stage1_workspace_bytes(ctypes.byref(p), 0) == 0
+    assert L.am_stage1_workspace_bytes(ctypes.byref(P(n=255, T=32, group=2)), 16) == 0
+    big = 1 << 40
+
+    def fit(pp, S=16, steps=4, lr=3e-3, wd=1e-2, keypos=FAKE, Ck=FAKE, nb=big, samples=FAKE):
+        return L.am_fit_stage1(ctypes.byref(pp), FAKE, FAKE, FAKE, keypos, samples, S, steps,
+                               None, lr, wd, Ck, FAKE, FAKE, None, FAKE, nb, None)
+    assert fit(p, steps=0) == amc.AM_ERR_INVALID_ARG
+    assert fit(p, S=0) == amc.AM_ERR_INVALID_ARG
+    assert fit(p, lr=-1.0) == amc.AM_ERR_INVALID_ARG
+    assert fit(p, wd=float("nan")) == amc.AM_ERR_INVALID_ARG
+    assert fit(p, keypos=None) == amc.AM_ERR_INVALID_ARG       # causal needs positions
+    assert fit(p, Ck=None) == amc.AM_ERR_INVALID_ARG
+    assert fit(p, samples=FAKE + 4) == amc.AM_ERR_INVALID_ARG  # misaligned
+    assert fit(p, nb=64) == amc.AM_ERR_WORKSPACE
+    assert fit(P(n=256, T=32, group=2, d=96)) == amc.AM_ERR_UNSUPPORTED
+    assert L.am_stage1_loss_grad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                 FAKE, None, FAKE, None, FAKE, FAKE, big,
+                                 None) == amc.AM_ERR_INVALID_ARG   # gCv missing
+    assert L.am_stage1_loss_grad(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                 FAKE, None, FAKE, FAKE, FAKE, FAKE, 8,
+                                 None) == amc.AM_ERR_WORKSPACE
