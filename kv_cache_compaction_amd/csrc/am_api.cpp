@@ -560,6 +560,7 @@ am_status check_stage1(const am_problem* p, const void* Q, const float* O_full,
   am_status st = check_cache_problem(p);
   if (st != AM_OK) return st;
   if (p->n % p->group != 0 || S < 1 || S * p->group > ((int64_t)1 << 24)) return AM_ERR_INVALID_ARG;
+  if (p->group > 65535) return AM_ERR_UNSUPPORTED;   // a grid dimension of the statistics pass
   if (!Q || !O_full || !lse_full || !samples || (p->causal && !keypos)) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(O_full) || !al16(lse_full) || !al16(samples) ||
       (keypos && !al16(keypos)) || (ws && !al16(ws)))
@@ -584,9 +585,9 @@ Stage1Args stage1_args(const am_problem* p, const void* Q, const float* O_full,
 
 size_t am_stage1_workspace_bytes(const am_problem* p, int64_t S) {
   if (check_cache_problem(p) != AM_OK || S < 1 || p->n % p->group != 0 ||
-      S * p->group > ((int64_t)1 << 24))
+      S * p->group > ((int64_t)1 << 24) || p->group > 65535)
     return 0;
-  return stage1_ws_bytes(p->heads, p->T, p->d, S, p->group);
+  return stage1_ws_bytes(p->heads, p->n, p->T, p->d, S, p->group);
 }
 
 am_status am_stage1_loss_grad(const am_problem* p, const void* Q, const float* O_full,
@@ -601,7 +602,7 @@ am_status am_stage1_loss_grad(const am_problem* p, const void* Q, const float* O
   if (!al16(Ck) || !al16(Cv) || !al16(bias) || !al16(gCk) || !al16(gCv) || !al16(gbias) ||
       (loss_out && !al16(loss_out)))
     return AM_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < stage1_ws_bytes(p->heads, p->T, p->d, S, p->group))
+  if (!ws || ws_bytes < stage1_ws_bytes(p->heads, p->n, p->T, p->d, S, p->group))
     return AM_ERR_WORKSPACE;
   Stage1Args a = stage1_args(p, Q, O_full, lse_full, keypos, samples, S, ws, stream);
   a.Ck = (float*)Ck; a.Cv = (float*)Cv; a.b = (float*)bias; a.loss = loss_out;
@@ -623,7 +624,7 @@ am_status am_fit_stage1(const am_problem* p, const void* Q, const float* O_full,
   if (!al16(Ck) || !al16(Cv) || !al16(bias) || (trainable && !al16(trainable)) ||
       (loss_out && !al16(loss_out)))
     return AM_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < stage1_ws_bytes(p->heads, p->T, p->d, S, p->group))
+  if (!ws || ws_bytes < stage1_ws_bytes(p->heads, p->n, p->T, p->d, S, p->group))
     return AM_ERR_WORKSPACE;
   Stage1Args a = stage1_args(p, Q, O_full, lse_full, keypos, samples, S, ws, stream);
   a.Ck = Ck; a.Cv = Cv; a.b = bias; a.loss = loss_out; a.trainable = trainable;

@@ -128,7 +128,8 @@ struct Stage1Args {
   hipStream_t stream;
 };
 hipError_t launch_stage1(const Stage1Args& a);
-size_t stage1_ws_bytes(int64_t heads, int64_t t, int64_t d, int64_t S, int64_t group);
+size_t stage1_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d, int64_t S,
+                       int64_t group);
 constexpr int kInitMaxChunk = 16384;
 constexpr int kInitMaxM = 8192;
 size_t two_pass_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t s,

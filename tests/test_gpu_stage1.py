@@ -145,3 +145,45 @@ def test_stage1_fit_matches_oracle(case):
         after = O.stage1_loss_grad(Qf[h], every, got[0][h], got[1][h], got[2][h], keypos[h],
                                    Ofull[h], lfull[h], sa, sz, scale, causal, group)[0]
         assert after < before, (before, after)
+
+
+def test_stage1_loss_grad_full_size():
+    """The timed configuration: 8 heads of 131072 queries (GQA 4, causal, 32768 positions),
+    1024 slots, 128 positions per update. The targets are synthetic arrays of the right
+    shape (the fit only reads them), so the oracle evaluates each head exactly."""
+    import torch
+    heads, d, T, t, group, S = 8, 128, 32768, 1024, 4, 128
+    n = T * group
+    rng = np.random.default_rng(77)
+    Qb = synth.bf16_bits(rng.standard_normal((heads, n, d), dtype=np.float32))
+    Ofull = (0.3 * rng.standard_normal((heads, n, d), dtype=np.float32)).astype(np.float32)
+    lfull = (8.0 + 2.0 * rng.standard_normal((heads, n))).astype(np.float32)
+    Ck = rng.standard_normal((heads, t, d)).astype(np.float32)
+    Cv = rng.standard_normal((heads, t, d)).astype(np.float32)
+    bias = (0.5 * rng.standard_normal((heads, t))).astype(np.float32)
+    keypos = np.stack([np.sort(rng.choice(T, t, replace=False)) for _ in range(heads)])
+    keypos[:, 0] = 0
+    keypos = keypos.astype(np.int32)
+    samples = synth.stage1_samples(T, 1, S)[0]
+    scale = 1.0 / np.sqrt(d)
+    dQ = to_dev(Qb, "bf16")
+    L, gCk, gCv, gb = amc.stage1_loss_grad(
+        dQ, torch.from_numpy(Ofull).cuda(), torch.from_numpy(lfull).cuda(),
+        torch.from_numpy(samples).cuda(), torch.from_numpy(Ck).cuda(),
+        torch.from_numpy(Cv).cuda(), torch.from_numpy(bias).cuda(),
+        keypos=torch.from_numpy(keypos).cuda(), causal=True, group=group, scale=scale)
+    L, gCk, gCv, gb = (x.cpu().numpy().astype(np.float64) for x in (L, gCk, gCv, gb))
+    del dQ
+    rows = O.stage1_rows(samples, group)
+    Qf = synth.bf16_to_f32(Qb[:, rows]).astype(np.float64)   # only the sampled rows
+    full_rows = np.zeros((n, d))   # the oracle indexes queries by row; only `rows` are read
+    for h in range(heads):
+        sa, sz = O.teacher_scales(Ofull[h], lfull[h], group)
+        full_rows[rows] = Qf[h]
+        ref = O.stage1_loss_grad(full_rows, rows, Ck[h].astype(np.float64),
+                                 Cv[h].astype(np.float64), bias[h].astype(np.float64),
+                                 keypos[h], Ofull[h], lfull[h], sa, sz, scale, True, group)
+        assert abs(L[h] - ref[0]) <= 1e-4 * abs(ref[0]), (h, L[h], ref[0])
+        for got, want, nm in zip((gCk[h], gCv[h], gb[h]), ref[1:], ("dCk", "dCv", "db")):
+            err = np.abs(got - want).max()
+            assert err <= 1e-3 * np.abs(want).max(), f"head {h} {nm}: max err {err}"
