@@ -63,9 +63,12 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_calls(torch, fn, reps):
-    """Average ms of fn() over reps calls, bracketed by events on the current stream."""
+def time_calls(torch, fn, reps, warm=True):
+    """Average ms of fn() over reps calls, bracketed by events on the current stream; with
+    warm, after one untimed call (first-launch costs of the call's kernels stay out)."""
     e0, e1 = _events(torch)
+    if warm:
+        fn()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
@@ -146,7 +149,7 @@ def main():
         step()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ms = time_calls(torch, step, args.steps)
+    ms = time_calls(torch, step, args.steps, warm=False)   # the warmup steps ran above
     wall = (time.perf_counter() - t_wall) / args.steps * 1e3
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events), {wall:.3f} ms/step (wall)",
           file=sys.stderr, flush=True)
