@@ -19,9 +19,9 @@
 //
 // Gram kernel. part[h, chunk, tile] = X_a X_b^T over one chunk of queries, for the 256 x 256
 // row-block pairs a >= b (lower triangle; for the value fit the pair of the Y^T block with
-// itself is skipped). Four waves, one per SIMD, each own a 128 x 128 quarter (16 MFMA
-// accumulators); 64-query steps are staged through registers into two LDS buffers (one
-// barrier per step). Under the causal mask a key block has no entry before the first
+// itself is skipped). Eight waves, two per SIMD, each own a 128 x 64 block (8 MFMA
+// accumulators), so one wave's LDS reads and barrier wait overlap the other's products;
+// 32-query stages are staged by direct global-to-LDS loads (one barrier per stage). Under the causal mask a key block has no entry before the first
 // query that sees its first key, so each tile starts its chunk there.
 //
 // Reductions sum the chunk partials in a fixed order: no floating-point atomics.
@@ -220,7 +220,8 @@ struct SyrkParams {
 // the buffer read in the previous step is refilled right after it.
 constexpr int kSyS = 4;                  // LDS stages
 constexpr int kSyRow = kSyK;             // bf16 per staged row (64 bytes)
-constexpr int kSyLoads = kSyT / 16 / 4;  // loads per wave per operand per stage (4)
+constexpr int kSyWaves = 8;              // two waves per SIMD, each a 128 x 64 block
+constexpr int kSyLoads = kSyT / 16 / kSyWaves;  // loads per wave per operand per stage (2)
 
 __device__ __forceinline__ void sy_wait_stages(int pending, bool diag) {
   // vmcnt <= pending stages' loads of this wave, lgkmcnt 0, expcnt untouched (7)
@@ -228,16 +229,17 @@ __device__ __forceinline__ void sy_wait_stages(int pending, bool diag) {
   const int per = diag ? kSyLoads : 2 * kSyLoads;
   switch (pending * per) {
     case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (0 << 8)); break;
     case 4: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (0 << 8)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (0 << 8)); break;
     case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (0 << 8)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (1 << 14)); break;
     default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8)); break;
   }
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__global__ __launch_bounds__(256) void syrk_kernel(const SyrkParams p) {
+__global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p) {
   static_assert(kSyK == 32 && kSyS == 4, "staging layout assumes 32-query stages");
   __shared__ __align__(16) bf16 xs[kSyS][2][kSyT * kSyRow];
   const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(256) void syrk_kernel(const SyrkParams p) {
   sy_tri(tile, ra, rb);
   const bool diag = ra == rb;   // (wave-uniform)
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wy = wave >> 1, wx = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wy = wave >> 2, wx = wave & 3;
   // first query with an entry in a block: that of its first key (keys ascend by position)
   auto kfirst = [&](int blk) -> int {
     if (!p.causal || blk >= p.nkb) return 0;
@@ -260,23 +262,23 @@ __global__ __launch_bounds__(256) void syrk_kernel(const SyrkParams p) {
   const bf16* Xa = p.X + ((size_t)head * p.xrows + (size_t)ra * kSyT) * p.npad;
   const bf16* Xb = p.X + ((size_t)head * p.xrows + (size_t)rb * kSyT) * p.npad;
 
-  // this lane's source of load i: row R = 16 (4 wave + i) + l / 4, logical chunk
+  // this lane's source of load i: row R = 16 (kSyLoads wave + i) + l / 4, logical chunk
   // (l % 4) ^ ((R >> 2) & 3)
   size_t soff[kSyLoads];
 #pragma unroll
   for (int i = 0; i < kSyLoads; ++i) {
-    const int R = 16 * (4 * wave + i) + (lane >> 2);
+    const int R = 16 * (kSyLoads * wave + i) + (lane >> 2);
     const int c = (lane & 3) ^ ((R >> 2) & 3);
     soff[i] = (size_t)R * p.npad + kbeg + c * 8;
   }
   // fragment reads: row base + 32 i + r, logical chunk 2 kk + hh
   const int swz = (r >> 2) & 3;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(256) void syrk_kernel(const SyrkParams p) {
       const int buf = st % kSyS, k = st * kSyK;
 #pragma unroll
       for (int i = 0; i < kSyLoads; ++i) {
-        const int R0 = 16 * (4 * wave + i);
+        const int R0 = 16 * (kSyLoads * wave + i);
         __builtin_amdgcn_global_load_lds((const void*)(Xa + soff[i] + k),
                                          (lds_ptr_t)&xs[buf][0][R0 * kSyRow], 16, 0, 0);
         if (!DIAG)
@@ -304,33 +306,31 @@ __global__ __launch_bounds__(256) void syrk_kernel(const SyrkParams p) {
       if (st + kSyS - 1 < nsteps) issue(st + kSyS - 1);
       const int buf = st % kSyS;
       const bf16* A = &xs[buf][0][(wy * 128 + r) * kSyRow];
-      const bf16* B = &xs[buf][DIAG ? 0 : 1][(wx * 128 + r) * kSyRow];
-      bf16x8 af[2][4], bfr[2][4];
+      const bf16* B = &xs[buf][DIAG ? 0 : 1][(wx * 64 + r) * kSyRow];
+      bf16x8 af[2][4], bfr[2][2];
       auto frag = [&](int kk, int slot) {
         const int off = ((2 * kk + hh) ^ swz) * 8;
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[slot][i] = *(const bf16x8*)(A + i * 32 * kSyRow + off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[slot][j] = *(const bf16x8*)(B + j * 32 * kSyRow + off);
+        for (int j = 0; j < 2; ++j) bfr[slot][j] = *(const bf16x8*)(B + j * 32 * kSyRow + off);
       };
-      // sub-step 0's eight reads, its first four MFMAs, then sub-step 1's reads: at most
-      // eight reads are pending at any wait (the LDS counter saturates at 15, past which
-      // the compiler can only wait for all of them)
+      // sub-step 0's six reads, its first two MFMAs, then sub-step 1's reads
       frag(0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mma16(acc[0][j], af[0][0], bfr[0][j]);
+      for (int j = 0; j < 2; ++j) mma16(acc[0][j], af[0][0], bfr[0][j]);
       __builtin_amdgcn_sched_barrier(0);
       frag(1, 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 1; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma16(acc[i][j], af[0][i], bfr[0][j]);
+        for (int j = 0; j < 2; ++j) mma16(acc[i][j], af[0][i], bfr[0][j]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma16(acc[i][j], af[1][i], bfr[1][j]);
+        for (int j = 0; j < 2; ++j) mma16(acc[i][j], af[1][i], bfr[1][j]);
     }
   };
   if (diag) run(std::true_type{});
@@ -340,10 +340,10 @@ __global__ __launch_bounds__(256) void syrk_kernel(const SyrkParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        P[(size_t)(wy * 128 + i * 32 + crow(e, hh)) * kSyT + wx * 128 + j * 32 + r] = acc[i][j][e];
+        P[(size_t)(wy * 128 + i * 32 + crow(e, hh)) * kSyT + wx * 64 + j * 32 + r] = acc[i][j][e];
 }
 
 // Symmetric Gram of the key rows, chunk partials summed in order, into an ld x ld matrix
@@ -512,7 +512,8 @@ hipError_t launch_syrk_gram(const SyrkGramArgs& a) {
   sp.ntiles = s.ntiles; sp.nch = s.nch; sp.chunk = s.chunk; sp.t = t; sp.group = a.group;
   sp.causal = a.causal; sp.nhead = H;
   const int ngrp = s.nch * H;
-  hipLaunchKernelGGL(syrk_kernel, dim3(8 * s.ntiles * ((ngrp + 7) / 8)), dim3(256), 0, st, sp);
+  hipLaunchKernelGGL(syrk_kernel, dim3(8 * s.ntiles * ((ngrp + 7) / 8)), dim3(kSyWaves * 64), 0,
+                     st, sp);
   const dim3 gb((a.ld + 63) / 64, (a.ld + 63) / 64, H);
   if (a.value) {
     hipLaunchKernelGGL((syrk_reduce_g_kernel<double>), gb, dim3(256), 0, st,

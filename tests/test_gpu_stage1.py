@@ -26,6 +26,8 @@ CASES = [
     ("causal_g4_d128", 2, 128, 300, 45, 4, True, "bf16", 29),
     ("noncausal_f32_d128", 1, 128, 256, 70, 1, False, "f32", 128),
     ("causal_g3_d64_f32", 1, 64, 200, 17, 3, True, "f32", 5),
+    ("causal_g2_t2100_d64", 1, 64, 4096, 2100, 2, True, "bf16", 40),   # rows beyond registers
+    ("single_slot_f32", 1, 128, 64, 1, 1, False, "f32", 16),
 ]
 
 
