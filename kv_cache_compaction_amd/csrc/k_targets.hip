@@ -101,9 +101,10 @@ struct FlashParams {
 };
 
 // Launch shape (measured on MI355X at the long causal workload): 8 waves of 32 queries
-// each, two waves per SIMD so one wave's softmax overlaps the other's MFMAs; 64-key tiles
-// (32 for fp32 operands at d = 128, for LDS) in a ring of three LDS buffers with one
-// barrier per tile; the running max is rescaled lazily.
+// each, two waves per SIMD (waves w and w + 4) running their tile phases half a tile apart,
+// so one wave's softmax meets the other's MFMAs; 64-key tiles (32 for fp32 operands at
+// d = 128, for LDS) in a ring of four LDS buffers with one barrier per tile; the running
+// max is rescaled lazily.
 constexpr int kFlashWaves = 8;
 template <typename T, int D> constexpr int flash_bn() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
 constexpr float kLazyTau = 8.f;  // rescale only when the row max grows by more than 2^8
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
   constexpr int NKB = BN / 32;                // 32-key blocks per tile
   constexpr int NT = WAVES * 64;
   constexpr int BM = WAVES * 32;
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   constexpr int E = epc<T>();
   constexpr int KCPR = D / E;                 // 16-byte chunks per K row
   constexpr int VCPR = BN / E;                // 16-byte chunks per Vt row
@@ -238,15 +239,17 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // One tile: S^T = K Q^T, lazy online softmax, O^T += V^T P^T. MASK is a compile-time
-  // choice so unmasked tiles carry no per-element visibility code.
-  auto tile_step = [&](int kt, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    if (kt + 2 < ntiles) gload(kt + 2);
-    const int buf = kt % NBUF;
-    const int k0 = kt * BN;
-    const T* Ks = lds + buf * L::BUF + kperm(r) * L::KP + hh * 8;
-    f32x16 s[NKB];
+  // One tile in three phases: X, S^T = K Q^T (MFMA); Y, the lazy online softmax (vector
+  // ALU); Z, O^T += V^T P^T (MFMA). MASK is a compile-time choice so unmasked tiles carry
+  // no per-element visibility code. The two waves that share a SIMD (wave w and w + 4) run
+  // the phases half a tile apart: the first group does X(k) Y(k) Z(k) between barriers k
+  // and k + 1, the second Y(k-1) Z(k-1) X(k), so one wave's softmax meets the other's
+  // products. A four-buffer LDS ring keeps tile k - 1 readable while tile k + 2 is stored.
+  const bool lag = wave >= WAVES / 2;   // (wave-uniform)
+  f32x16 s[NKB];
+  float x[NKB * 16];
+  auto phase_x = [&](int kt) {
+    const T* Ks = lds + (kt % NBUF) * L::BUF + kperm(r) * L::KP + hh * 8;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -256,8 +259,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         mma16(s[kb], *(const v8*)(Ks + kb * 32 * L::KP + kc * 16), bq[kc]);
-
-    float x[NKB * 16];
+  };
+  auto phase_y = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int buf = kt % NBUF;
+    const int k0 = kt * BN;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -298,8 +304,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
       psum += x[i];
     }
     l += psum;
+  };
+  auto phase_z = [&](int kt) {
     if constexpr (WITH_O) {
-      const T* Vs = lds + buf * L::BUF + L::K_ELEMS + r * L::VP + hh * 8;
+      const T* Vs = lds + (kt % NBUF) * L::BUF + L::K_ELEMS + r * L::VP + hh * 8;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -310,10 +318,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
             mma16(oacc[db], *(const v8*)(Vs + db * 32 * L::VP + kb * 32 + kk * 16), pb);
         }
     }
-    if (kt + 2 < ntiles) sstore((kt + 2) % NBUF);
-    __syncthreads();
   };
-
   if (ntiles > 0) {
     gload(0);
     sstore(0);
@@ -323,9 +328,50 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
     }
   }
   __syncthreads();
-  // every wave runs ntiles iterations with one barrier each; only the split differs
-  for (int kt = 0; kt < nfull; ++kt) tile_step(kt, std::false_type{});
-  for (int kt = nfull; kt < ntiles; ++kt) tile_step(kt, std::true_type{});
+  // every wave runs ntiles intervals with one barrier each; only the phase order differs
+  auto interval_end = [&](int kt) {
+    if (kt + 2 < ntiles) sstore((kt + 2) % NBUF);
+    __syncthreads();
+  };
+  if (!lag) {
+    for (int kt = 0; kt < nfull; ++kt) {
+      if (kt + 2 < ntiles) gload(kt + 2);
+      phase_x(kt);
+      phase_y(kt, std::false_type{});
+      phase_z(kt);
+      interval_end(kt);
+    }
+    for (int kt = nfull; kt < ntiles; ++kt) {
+      if (kt + 2 < ntiles) gload(kt + 2);
+      phase_x(kt);
+      phase_y(kt, std::true_type{});
+      phase_z(kt);
+      interval_end(kt);
+    }
+  } else if (ntiles > 0) {
+    if (2 < ntiles) gload(2);
+    phase_x(0);
+    interval_end(0);
+    const int kmid = min(nfull, ntiles - 1);
+    for (int kt = 1; kt <= kmid; ++kt) {   // tile kt - 1 < nfull: no mask
+      if (kt + 2 < ntiles) gload(kt + 2);
+      phase_y(kt - 1, std::false_type{});
+      phase_z(kt - 1);
+      phase_x(kt);
+      interval_end(kt);
+    }
+    for (int kt = max(kmid + 1, 1); kt < ntiles; ++kt) {
+      if (kt + 2 < ntiles) gload(kt + 2);
+      phase_y(kt - 1, std::true_type{});
+      phase_z(kt - 1);
+      phase_x(kt);
+      interval_end(kt);
+    }
+    // the last tile's buffer is no longer refilled
+    if (ntiles - 1 < nfull) phase_y(ntiles - 1, std::false_type{});
+    else phase_y(ntiles - 1, std::true_type{});
+    phase_z(ntiles - 1);
+  }
 
   const float ltot = l + shfl_xor32(l);
   if constexpr (WITH_O) {
