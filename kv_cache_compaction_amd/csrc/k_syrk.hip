@@ -70,6 +70,18 @@ __global__ __launch_bounds__(256) void design_kernel(const DesignParams p) {
   const int n = p.n, t = p.t, q0 = qb * kDsQ;
   const T* Qh = (const T*)p.Q + (size_t)head * n * D;
   const T* Ch = (const T*)p.Ck + (size_t)head * t * D;
+  // Under the causal mask the Gram product reads this key block only from the first query
+  // that sees its first key (rounded down to its 32-query steps); earlier query tiles hold
+  // zeros nobody reads, so they are neither computed nor written (M^T b partials: 0).
+  if (p.causal) {
+    const int first = p.keypos[(size_t)head * t + min(kblk * kDsK, t - 1)] * p.group;
+    if (q0 + kDsQ <= (first / kSyK) * kSyK) {
+      if (!VALUE)
+        for (int k = tid; k < kDsK; k += 256)
+          p.hpart[((size_t)head * p.tpad + kblk * kDsK + k) * gridDim.x + qb] = 0.f;
+      return;
+    }
+  }
 
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
