@@ -254,10 +254,15 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p) {
   static_assert(kSyK == 32 && kSyS == 4, "staging layout assumes 32-query stages");
   __shared__ __align__(16) bf16 xs[kSyS][2][kSyT * kSyRow];
+  // Groups (head, chunk) in decreasing expected work (later chunks hold more causally
+  // visible pairs; heads alike) are dealt to the XCDs in snake order: XCD x takes groups
+  // 8k + x for even k and 8k + 7 - x for odd k, so the XCDs get equal shares and each
+  // starts with its largest groups.
   const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
-  const int grp = xcd + 8 * (slot / p.ntiles), tile = slot % p.ntiles;
-  if (grp >= p.nch * p.nhead) return;
-  const int ch = grp % p.nch, head = grp / p.nch;
+  const int k = slot / p.ntiles, tile = slot % p.ntiles;
+  const int sgrp = 8 * k + ((k & 1) ? 7 - xcd : xcd);
+  if (sgrp >= p.nch * p.nhead) return;
+  const int ch = p.nch - 1 - sgrp / p.nhead, head = sgrp % p.nhead;
   int ra, rb;
   sy_tri(tile, ra, rb);
   const bool diag = ra == rb;   // (wave-uniform)
