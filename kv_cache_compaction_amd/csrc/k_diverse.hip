@@ -8,7 +8,9 @@
 // streams the range once (a group of lanes per key row, 16 bytes per lane, so a wave reads
 // contiguous rows), lowers the distances by the new key's, and finds the range's best
 // candidate; the P candidates meet through a per-head barrier and every workgroup reduces
-// them in the same way, so all agree on the next key without another round trip.
+// them in the same way, so all agree on the next key without another round trip. For bf16
+// keys whose ranges fit, fft_reg_kernel keeps each range in registers instead, so a step
+// reads only the chosen key.
 #include <climits>
 
 #include "am_common.hpp"
@@ -193,6 +195,170 @@ __global__ __launch_bounds__(256) void fft_kernel(const FftParams p) {
   if (tout && tid == 0 && p.status) atomicOr(&p.status[head], AM_HEAD_TIMEOUT_BIT);
 }
 
+// The same traversal with the keys of each workgroup held in registers (bf16 inputs, a
+// workgroup of 512 threads keeping kFftRegKeys(D) rows per thread): a step reads only the
+// chosen key, so its cost is the distance arithmetic and the per-head barrier.
+template <int D> constexpr int fft_reg_keys() { return D == 128 ? 2 : 4; }
+typedef const __attribute__((address_space(4))) uint32_t* cu32_ptr;
+constexpr int kFftRegThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kFftRegThreads) void fft_reg_kernel(const FftParams p) {
+  constexpr int RK = fft_reg_keys<D>();   // key rows per thread
+  constexpr int W = D / 2;                // bf16 pairs per row
+  constexpr int NW = kFftRegThreads / 64;
+  __shared__ float rv[NW];
+  __shared__ int ri[NW], jsh, tout;
+  const int head = blockIdx.x % p.heads, part = blockIdx.x / p.heads;
+  const int b0 = part * p.chunk, b1 = min(p.T, b0 + p.chunk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16* Kh = (const bf16*)p.K + (size_t)head * p.T * D;
+  uint32_t kx[RK][W];
+  float dist[RK];
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int i = b0 + tid + kFftRegThreads * k;
+    const uint4* src = (const uint4*)(Kh + (size_t)min(i, p.T - 1) * D);
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const uint4 v = src[q];
+      kx[k][4 * q + 0] = v.x;
+      kx[k][4 * q + 1] = v.y;
+      kx[k][4 * q + 2] = v.z;
+      kx[k][4 * q + 3] = v.w;
+    }
+    dist[k] = i < b1 ? INFINITY : -INFINITY;   // rows past the range never win
+  }
+  if (tid == 0) tout = 0;
+  __syncthreads();
+  int j = 0, nbar = 0;
+  for (int step = 0; step < p.M; ++step) {
+    if (step < p.na) j = p.anchors[(size_t)head * p.na + step];
+    if (part == 0 && tid == 0) p.order[(size_t)head * p.M + step] = j;
+    j = __builtin_amdgcn_readfirstlane(j);
+    // the new key's row through the scalar cache (a uniform read-only address), so its
+    // values reach the vector instructions as scalar operands
+    const cu32_ptr crow = (cu32_ptr)(uintptr_t)(Kh + (size_t)j * D);
+    // the rows' bf16 words are re-expanded every step: an empty asm marks them as rewritten,
+    // so the compiler keeps them packed instead of hoisting RK * D floats out of the loop
+#pragma unroll
+    for (int k = 0; k < RK; ++k)
+#pragma unroll
+      for (int q = 0; q < W; ++q) asm volatile("" : "+v"(kx[k][q]));
+    // squared distances to the new key, four partial sums per row
+    float acc[RK][4];
+#pragma unroll
+    for (int k = 0; k < RK; ++k)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[k][u] = 0.f;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) {
+      const uint32_t c0 = crow[2 * q], c1 = crow[2 * q + 1];
+      const float cx = __uint_as_float(c0 << 16), cy = __uint_as_float(c0 & 0xffff0000u);
+      const float cz = __uint_as_float(c1 << 16), cw = __uint_as_float(c1 & 0xffff0000u);
+#pragma unroll
+      for (int k = 0; k < RK; ++k) {
+        const uint32_t w0 = kx[k][2 * q], w1 = kx[k][2 * q + 1];
+        const float d0 = __uint_as_float(w0 << 16) - cx;
+        const float d1 = __uint_as_float(w0 & 0xffff0000u) - cy;
+        const float d2 = __uint_as_float(w1 << 16) - cz;
+        const float d3 = __uint_as_float(w1 & 0xffff0000u) - cw;
+        acc[k][0] = __builtin_fmaf(d0, d0, acc[k][0]);
+        acc[k][1] = __builtin_fmaf(d1, d1, acc[k][1]);
+        acc[k][2] = __builtin_fmaf(d2, d2, acc[k][2]);
+        acc[k][3] = __builtin_fmaf(d3, d3, acc[k][3]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const int i = b0 + tid + kFftRegThreads * k;
+      const float dd = (acc[k][0] + acc[k][1]) + (acc[k][2] + acc[k][3]);
+      if (i < b1) dist[k] = i == j ? -1.f : fminf(dist[k], dd);   // chosen keys stay at -1
+    }
+    if (step + 1 >= p.M) break;
+    if (step + 1 < p.na) continue;   // the next key is an anchor: nothing to search
+    // this workgroup's best candidate
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const int i = b0 + tid + kFftRegThreads * k;
+      if (fft_better(dist[k], i, bv, bi)) {
+        bv = dist[k];
+        bi = i;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
+      const int i2 = __shfl_xor(bi, o, 64);
+      if (fft_better(v2, i2, bv, bi)) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    if (lane == 0) {
+      rv[wave] = bv;
+      ri[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NW; ++w)
+        if (fft_better(rv[w], ri[w], bv, bi)) {
+          bv = rv[w];
+          bi = ri[w];
+        }
+      jsh = min(max(bi, 0), p.T - 1);
+    }
+    __syncthreads();
+    if (p.P == 1) {
+      j = jsh;
+      continue;
+    }
+    // the head's P candidates: publish, meet, and reduce them identically everywhere
+    int2* slot = p.part + ((size_t)head * 2 + (step & 1)) * p.P;
+    if (tid == 0) slot[part] = make_int2(__float_as_int(bv), jsh);   // thread 0 holds the best
+    fft_barrier(&p.bar[head], ++nbar * p.P, &tout);
+    if (tout) break;
+    bv = -INFINITY;
+    bi = INT_MAX;
+    for (int q = tid; q < p.P; q += kFftRegThreads) {
+      const float v = __int_as_float(ld_dev_i(&slot[q].x));
+      const int ix = ld_dev_i(&slot[q].y);
+      if (fft_better(v, ix, bv, bi)) {
+        bv = v;
+        bi = ix;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
+      const int i2 = __shfl_xor(bi, o, 64);
+      if (fft_better(v2, i2, bv, bi)) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      rv[wave] = bv;
+      ri[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NW; ++w)
+        if (fft_better(rv[w], ri[w], bv, bi)) {
+          bv = rv[w];
+          bi = ri[w];
+        }
+      jsh = min(max(bi, 0), p.T - 1);
+    }
+    __syncthreads();
+    j = jsh;
+  }
+  if (tout && tid == 0 && p.status) atomicOr(&p.status[head], AM_HEAD_TIMEOUT_BIT);
+}
+
 // idx = the M chosen keys in ascending order (bitonic sort in LDS, M <= 8192)
 __global__ __launch_bounds__(1024) void sort_order_kernel(const int32_t* __restrict__ order,
                                                           int32_t* __restrict__ idx, int M) {
@@ -274,6 +440,16 @@ hipError_t launch_fft(FftParams fp, size_t shmem, hipStream_t st) {
   void* args[] = {&fp};
   return hipLaunchCooperativeKernel((const void*)fft_kernel<Tt, D>, g, b, args, (unsigned)shmem, st);
 }
+template <int D>
+hipError_t launch_fft_reg(FftParams fp, hipStream_t st) {
+  const dim3 g(fp.heads * fp.P), b(kFftRegThreads);
+  if (fp.P == 1) {
+    hipLaunchKernelGGL((fft_reg_kernel<D>), g, b, 0, st, fp);
+    return hipGetLastError();
+  }
+  void* args[] = {&fp};
+  return hipLaunchCooperativeKernel((const void*)fft_reg_kernel<D>, g, b, args, 0u, st);
+}
 }  // namespace
 
 size_t init_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize, int64_t M,
@@ -317,7 +493,9 @@ hipError_t launch_init_anchor_diverse(const InitArgs& a) {
   fp.bar = pl.bar; fp.status = status;
   fp.heads = H; fp.T = a.T; fp.M = a.M; fp.na = a.na; fp.P = P; fp.chunk = (a.T + P - 1) / P;
   const size_t shmem = (size_t)fp.chunk * sizeof(float);
-  if (a.bf16)
+  if (a.bf16 && fp.chunk <= kFftRegThreads * (a.d == 128 ? fft_reg_keys<128>() : fft_reg_keys<64>()))
+    e = a.d == 128 ? launch_fft_reg<128>(fp, st) : launch_fft_reg<64>(fp, st);
+  else if (a.bf16)
     e = a.d == 128 ? launch_fft<bf16, 128>(fp, shmem, st) : launch_fft<bf16, 64>(fp, shmem, st);
   else
     e = a.d == 128 ? launch_fft<float, 128>(fp, shmem, st) : launch_fft<float, 64>(fp, shmem, st);
