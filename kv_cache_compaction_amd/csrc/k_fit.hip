@@ -1774,23 +1774,33 @@ hipError_t launch_fit_values(const FitArgs& a) {
 // mass far below the scale still get a finite bias. Delta, a mass by definition, is
 // clamped at 0 (a negative value is rounding).
 
-// per head: shift2 = C log2(e) and zsum = sum_i exp(lse_i - C)
-__global__ __launch_bounds__(256) void redist_prep_kernel(const float* __restrict__ lse, int n,
-                                                          float* __restrict__ shift2,
-                                                          double* __restrict__ zsum) {
-  __shared__ float red[4];
-  __shared__ double dred[256];
+// per head: shift2 = C log2(e) and zsum = sum_i exp(lse_i - C); one workgroup of 1024
+// threads per head, each thread streaming every 1024th row with four independent loads in
+// flight (the reduction order is fixed)
+__global__ __launch_bounds__(1024) void redist_prep_kernel(const float* __restrict__ lse, int n,
+                                                           float* __restrict__ shift2,
+                                                           double* __restrict__ zsum) {
+  __shared__ float red[16];
+  __shared__ double dred[1024];
   const int head = blockIdx.x, tid = threadIdx.x;
   const float* l = lse + (size_t)head * n;
-  float mx = -INFINITY;
-  for (int i = tid; i < n; i += 256) mx = fmaxf(mx, l[i]);
-  mx = block_max(mx, red);
+  float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int i = tid; i < n; i += 4096) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + 1024 * u < n) m4[u] = fmaxf(m4[u], l[i + 1024 * u]);
+  }
+  const float mx = block_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), red);
   const float c2 = mx == -INFINITY ? 0.f : mx * kLog2e;
-  double acc = 0.0;
-  for (int i = tid; i < n; i += 256) acc += (double)ex2(__builtin_fmaf(l[i], kLog2e, -c2));
-  dred[tid] = acc;
+  double a4[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int i = tid; i < n; i += 4096) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + 1024 * u < n) a4[u] += (double)ex2(__builtin_fmaf(l[i + 1024 * u], kLog2e, -c2));
+  }
+  dred[tid] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
   __syncthreads();
-  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+  for (int s2 = 512; s2 > 0; s2 >>= 1) {
     if (tid < s2) dred[tid] += dred[tid + s2];
     __syncthreads();
   }
@@ -1949,7 +1959,7 @@ hipError_t launch_beta_redistribute(const FitArgs& a) {
   const hipStream_t st = a.stream;
   const int H = a.heads;
   FastPlan pl = plan_fast((char*)a.ws, H, a.n, a.t, a.d, a.bf16 ? 2 : 4, 0);
-  hipLaunchKernelGGL(redist_prep_kernel, dim3(H), dim3(256), 0, st, a.lse, a.n, pl.shift2h,
+  hipLaunchKernelGGL(redist_prep_kernel, dim3(H), dim3(1024), 0, st, a.lse, a.n, pl.shift2h,
                      pl.zsum);
   KeyMassArgs km;
   km.Q = a.Q; km.Ck = a.Ck; km.keypos = a.idx; km.shift2 = pl.shift2h;
