@@ -372,30 +372,51 @@ __global__ __launch_bounds__(256) void syrk_reduce_g_kernel(const float* __restr
                                                             OT* __restrict__ G, int t, int ld,
                                                             int ntiles, int nch, float lambda) {
   __shared__ float blk[64][65];
-  const int head = blockIdx.z, bi = blockIdx.y, bj = blockIdx.x, tid = threadIdx.x;
-  const bool up = bi < bj;
-  const int si = up ? bj : bi, sj = up ? bi : bj;   // source block, lower triangle
+  // one workgroup per lower 64 x 64 block (si >= sj): it writes the block and its mirror
+  const int head = blockIdx.z, tid = threadIdx.x;
+  int si, sj;
+  sy_tri(blockIdx.x, si, sj);
   const int a = si * 64 / kSyT, b = sj * 64 / kSyT;
   const int tile = a * (a + 1) / 2 + b;
   const float* src = part + ((size_t)head * nch * ntiles + tile) * kSyT * kSyT +
                      (size_t)(si * 64 % kSyT) * kSyT + sj * 64 % kSyT;
   const size_t cstride = (size_t)ntiles * kSyT * kSyT;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    float acc = 0.f;
-    if (si * 64 + r < t && sj * 64 + c < t)
-      for (int ch = 0; ch < nch; ++ch) acc += src[ch * cstride + (size_t)r * kSyT + c];
-    blk[r][c] = acc;
+  // 16 entries per thread, summed over the chunks in order with all 16 loads of a chunk in
+  // flight together
+  constexpr int PER = 64 * 64 / 256;
+  float acc[PER];
+  bool live[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 256 * u, r = e >> 6, c = e & 63;
+    acc[u] = 0.f;
+    live[u] = si * 64 + r < t && sj * 64 + c < t;
+  }
+  for (int ch = 0; ch < nch; ++ch) {
+    const float* sc = src + ch * cstride;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u, r = e >> 6, c = e & 63;
+      if (live[u]) acc[u] += sc[(size_t)r * kSyT + c];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 256 * u;
+    blk[e >> 6][e & 63] = acc[u];
   }
   __syncthreads();
   OT* dst = G + (size_t)head * ld * ld;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63, i = bi * 64 + r, j = bj * 64 + c;
-    if (i >= ld || j >= ld) continue;
-    double v;
-    if (i < t && j < t) v = (double)(up ? blk[c][r] : blk[r][c]) + (i == j ? (double)lambda : 0.0);
-    else v = (i == j) ? 1.0 : 0.0;
-    dst[(size_t)i * ld + j] = (OT)v;
+  for (int mirror = 0; mirror < (si != sj ? 2 : 1); ++mirror) {
+    const int bi = mirror ? sj : si, bj = mirror ? si : sj;
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63, i = bi * 64 + r, j = bj * 64 + c;
+      if (i >= ld || j >= ld) continue;
+      double v;
+      if (i < t && j < t) v = (double)(mirror ? blk[c][r] : blk[r][c]) + (i == j ? (double)lambda : 0.0);
+      else v = (i == j) ? 1.0 : 0.0;
+      dst[(size_t)i * ld + j] = (OT)v;
+    }
   }
 }
 
@@ -405,9 +426,10 @@ __global__ __launch_bounds__(256) void syrk_reduce_r_kernel(const float* __restr
                                                             double* __restrict__ R, int t, int ld,
                                                             int D, int nkb, int ntiles, int nch) {
   const int head = blockIdx.y;
+  // thread (c, j), j fastest, so a wave reads consecutive floats of one partial row
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   if (e >= (long long)ld * D) return;
-  const int j = (int)(e / D), c = (int)(e % D);
+  const int c = (int)(e / ld), j = (int)(e % ld);
   float acc = 0.f;
   if (j < t) {
     const int tile = nkb * (nkb + 1) / 2 + j / kSyT;
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_r_kernel(const float* __restr
       acc += part[(((size_t)head * nch + ch) * ntiles + tile) * kSyT * kSyT +
                   (size_t)c * kSyT + j % kSyT];
   }
-  R[(size_t)head * ld * D + e] = (double)acc;
+  R[((size_t)head * ld + j) * D + c] = (double)acc;
 }
 
 // M^T b: hv[j] = sum over query blocks of the design kernel's partials (key-major
@@ -531,7 +553,8 @@ hipError_t launch_syrk_gram(const SyrkGramArgs& a) {
   const int ngrp = s.nch * H;
   hipLaunchKernelGGL(syrk_kernel, dim3(8 * s.ntiles * ((ngrp + 7) / 8)), dim3(kSyWaves * 64), 0,
                      st, sp);
-  const dim3 gb((a.ld + 63) / 64, (a.ld + 63) / 64, H);
+  const int nb64 = (a.ld + 63) / 64;
+  const dim3 gb(nb64 * (nb64 + 1) / 2, 1, H);   // lower 64 x 64 blocks
   if (a.value) {
     hipLaunchKernelGGL((syrk_reduce_g_kernel<double>), gb, dim3(256), 0, st,
                        (const float*)a.buf.part, a.Gd, t, a.ld, s.ntiles, s.nch, a.lambda);
