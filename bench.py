@@ -204,16 +204,21 @@ def main():
                                         new_causal=True, group=g_new)
     ms_cache = time_calls(torch, cache, 5)
     cache_pairs = w.heads * (n_new * w.t + g_new * m_new * (m_new + 1) // 2)
-    # stage-1 attention fitting of the compacted cache: 128 positions per update from an
-    # evenly spaced pool of 4096, a quarter of the slots trainable
-    S1, s1_updates = 128, 50
+    # stage-1 attention fitting of the compacted cache. The fitting queries stand in for
+    # teacher queries that follow the document: a pool of 4096 evenly spaced positions (every
+    # query head of each), seeing the whole cache (no mask), with full-cache targets from an
+    # unmasked targets pass over the pool; 128 pool positions per update, a quarter of the
+    # slots trainable
+    S1, s1_updates, pool = 128, 50, 4096
     n_pos = w.n // w.group
-    s1_samples = torch.from_numpy(synth.stage1_samples(n_pos, s1_updates, S1)).cuda()
+    pool_pos = (np.arange(min(pool, n_pos)) * n_pos) // min(pool, n_pos)
+    pool_rows = torch.from_numpy((pool_pos[:, None] * w.group + np.arange(w.group)).ravel()).cuda()
+    Qp = dQ[:, pool_rows].contiguous()
+    lse_p, Op, _ = amc.targets(Qp, dK, dV, causal=False, group=w.group, want_score=False)
+    s1_samples = torch.from_numpy(synth.stage1_samples(pool_pos.size, s1_updates, S1)).cuda()
     s1_train = torch.from_numpy(np.random.default_rng(0).random((w.heads, w.t)) < 0.25).cuda()
-    s1_keypos = full["idx"] if w.causal else None
-    s1 = lambda: amc.fit_stage1(dQ, Og, lse, s1_samples, full["Ck"], full["Cv"], full["beta"],
-                                keypos=s1_keypos, trainable=s1_train, causal=w.causal,
-                                group=w.group)
+    s1 = lambda: amc.fit_stage1(Qp, Op, lse_p, s1_samples, full["Ck"], full["Cv"], full["beta"],
+                                trainable=s1_train, causal=False, group=w.group)
     ms_s1 = time_calls(torch, s1, 2)
     s1_flops = 10 * w.heads * S1 * w.group * w.t * w.d * s1_updates
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -274,8 +279,9 @@ def main():
                            "positions_per_update": S1, "rows_per_update": S1 * w.group,
                            "slots": w.t, "trainable_frac": 0.25,
                            "fp32_tflops": s1_flops / (ms_s1 * 1e-3) / 1e12,
-                           "note": "one call = teacher statistics over all queries + "
-                                   f"{s1_updates} AdamW updates"},
+                           "pool_positions": int(pool_pos.size),
+                           "note": "one call = teacher statistics over the pool + "
+                                   f"{s1_updates} AdamW updates; pool queries see every slot"},
             "cache_attention": {"ms": ms_cache, "slots": w.t, "appended": m_new,
                                 "queries_per_head": n_new, "visible_pairs": cache_pairs,
                                 "tflops": 4 * w.d * cache_pairs / (ms_cache * 1e-3) / 1e12,
