@@ -189,3 +189,29 @@ def test_stage1_loss_grad_full_size():
         for got, want, nm in zip((gCk[h], gCv[h], gb[h]), ref[1:], ("dCk", "dCv", "db")):
             err = np.abs(got - want).max()
             assert err <= 1e-3 * np.abs(want).max(), f"head {h} {nm}: max err {err}"
+
+
+def test_stage1_fit_all_frozen_and_zero_rate():
+    """No trainable slot, or a zero learning rate with zero decay: every parameter keeps its
+    value exactly, while the losses are still evaluated (equal to the oracle's first)."""
+    import torch
+    case = CASES[0]
+    name, heads, d, T, t, group, causal, dtype, S = case
+    Q, Qf, Ckf, Cv, bias, keypos, Ofull, lfull, scale = _case(*case[:8], seed=5)
+    samples = synth.stage1_samples(T, 3, S, seed=4)
+    args = dict(keypos=torch.from_numpy(keypos).cuda(), causal=causal, group=group, scale=scale)
+    Ck0, Cv0, b0 = _dev_params(Ckf, Cv, bias)
+    for kw in (dict(trainable=torch.zeros((heads, t), dtype=torch.bool).cuda()),
+               dict(lr=0.0, wd=0.0)):
+        Ck1, Cv1, b1, losses = amc.fit_stage1(
+            to_dev(Q, dtype), torch.from_numpy(Ofull).cuda(), torch.from_numpy(lfull).cuda(),
+            torch.from_numpy(samples).cuda(), Ck0, Cv0, b0, **args, **kw)
+        assert torch.equal(Ck1, Ck0) and torch.equal(Cv1, Cv0) and torch.equal(b1, b0)
+        for h in range(heads):
+            sa, sz = O.teacher_scales(Ofull[h], lfull[h], group)
+            ref = O.stage1_loss_grad(Qf[h], O.stage1_rows(samples[0], group), Ckf[h], Cv[h],
+                                     bias[h], keypos[h], Ofull[h], lfull[h], sa, sz, scale,
+                                     causal, group)[0]
+            got = losses.cpu().numpy()[:, h]
+            assert np.all(np.isfinite(got))
+            assert abs(got[0] - ref) <= 1e-4 * abs(ref)
