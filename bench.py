@@ -192,7 +192,7 @@ def main():
     M_init = w.t // 4   # the anchor + diversifier share of a t-slot budget
     ms_init = time_calls(torch, lambda: amc.init_anchor_diverse(dQ, dK, M_init, causal=w.causal,
                                                                 group=w.group), 2)
-    m_new, g_new = 4096, 4
+    m_new, g_new = min(4096, w.T), 4
     n_new = g_new * m_new
     Qn = synth.make_heldout_queries(
         type(w)("appended_queries", w.heads, w.d, m_new, n_new, w.t, w.dtype, True, g_new), None,
