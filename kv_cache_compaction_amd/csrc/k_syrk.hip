@@ -19,7 +19,8 @@
 //
 // Gram kernel. part[h, chunk, tile] = X_a X_b^T over one chunk of queries, for the 256 x 256
 // row-block pairs a >= b (lower triangle; for the value fit the pair of the Y^T block with
-// itself is skipped). Eight waves, two per SIMD, each own a 128 x 64 block (8 MFMA
+// itself is skipped, and in its pairs with the key blocks only the half of the Y^T block
+// that holds rows is staged and multiplied). Eight waves, two per SIMD, each own a 128 x 64 block (8 MFMA
 // accumulators), so one wave's LDS reads and barrier wait overlap the other's products;
 // 32-query stages are staged by direct global-to-LDS loads (one barrier per stage). Under the causal mask a key block has no entry before the first
 // query that sees its first key, so each tile starts its chunk there.
@@ -36,6 +37,9 @@ constexpr int kSyT = 256;   // Gram tile side (rows of X per block)
 constexpr int kSyK = 32;    // queries per Gram step (one LDS stage)
 constexpr int kDsQ = 128;   // queries per design workgroup
 constexpr int kDsK = 256;   // keys per design workgroup (4 waves x 64)
+// Rows of the Y^T block that are written and multiplied (d <= 128 of them hold Y^T, the rest
+// of these zeros); its other 128 rows are neither written nor read.
+constexpr int kSyYRows = 128;
 
 __device__ __forceinline__ void sy_tri(int k, int& a, int& b) {
   int x = (int)((sqrtf(8.f * (float)k + 1.f) - 1.f) * 0.5f);
@@ -200,9 +204,10 @@ __global__ __launch_bounds__(256) void design_yt_kernel(const float* __restrict_
     ys[row][col + 3] = v.w;
   }
   __syncthreads();
+  static_assert(D <= kSyYRows, "Y^T rows exceed the part of the block the products read");
   bf16* Xh = X + ((size_t)head * xrows + tpad) * npad + q0;
-  // 256 rows x 64 queries, 8 queries (16 bytes) per store
-  for (int e = tid; e < kSyT * 8; e += 256) {
+  // kSyYRows rows x 64 queries, 8 queries (16 bytes) per store
+  for (int e = tid; e < kSyYRows * 8; e += 256) {
     const int c = e / 8, qq = (e % 8) * 8;
     float v[8];
 #pragma unroll
@@ -268,6 +273,11 @@ __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p)
   const bool diag = ra == rb;   // (wave-uniform)
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wy = wave >> 2, wx = wave & 3;
+  // In a tile of the Y^T block (always operand a) the waves of rows 128..255 hold no output:
+  // they neither stage those rows nor multiply (the products read only the first kSyYRows).
+  static_assert(kSyYRows == 128 && kSyLoads * 16 * (kSyWaves / 2) == 128,
+                "waves 4..7 stage exactly rows 128..255 of operand a");
+  const bool idle_a = ra == p.nkb && wy == 1;   // (wave-uniform)
   // first query with an entry in a block: that of its first key (keys ascend by position)
   auto kfirst = [&](int blk) -> int {
     if (!p.causal || blk >= p.nkb) return 0;
@@ -307,8 +317,9 @@ __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p)
 #pragma unroll
       for (int i = 0; i < kSyLoads; ++i) {
         const int R0 = 16 * (kSyLoads * wave + i);
-        __builtin_amdgcn_global_load_lds((const void*)(Xa + soff[i] + k),
-                                         (lds_ptr_t)&xs[buf][0][R0 * kSyRow], 16, 0, 0);
+        if (!idle_a)
+          __builtin_amdgcn_global_load_lds((const void*)(Xa + soff[i] + k),
+                                           (lds_ptr_t)&xs[buf][0][R0 * kSyRow], 16, 0, 0);
         if (!DIAG)
           __builtin_amdgcn_global_load_lds((const void*)(Xb + soff[i] + k),
                                            (lds_ptr_t)&xs[buf][1][R0 * kSyRow], 16, 0, 0);
@@ -318,9 +329,10 @@ __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p)
     for (int s0 = 0; s0 < kSyS - 1; ++s0)
       if (s0 < nsteps) issue(s0);
     for (int st = 0; st < nsteps; ++st) {
-      sy_wait_stages(min(kSyS - 2, nsteps - 1 - st), DIAG);
+      sy_wait_stages(min(kSyS - 2, nsteps - 1 - st), DIAG || idle_a);
       __builtin_amdgcn_s_barrier();
       if (st + kSyS - 1 < nsteps) issue(st + kSyS - 1);
+      if (idle_a) continue;
       const int buf = st % kSyS;
       const bf16* A = &xs[buf][0][(wy * 128 + r) * kSyRow];
       const bf16* B = &xs[buf][DIAG ? 0 : 1][(wx * 64 + r) * kSyRow];
@@ -353,6 +365,7 @@ __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p)
   if (diag) run(std::true_type{});
   else run(std::false_type{});
 
+  if (idle_a) return;
   float* P = p.part + (((size_t)head * p.nch + ch) * p.ntiles + tile) * kSyT * kSyT;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
