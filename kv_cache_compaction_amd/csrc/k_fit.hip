@@ -1044,18 +1044,65 @@ struct BlockRegs {
 // The 64 x 64 block is split 2 x 2 into 32 x 32 blocks:
 //   L11 = chol(A11), L21 = A21 L11^-T, L22 = chol(A22 - L21 L21^T),
 //   L^-1 = [[L11^-1, 0], [-L22^-1 (L21 L11^-1), L22^-1]].
-// Each 32 x 32 factorization (with its inverse) runs on one wave as symmetric Gaussian
-// elimination without pivoting on [A | I]: lanes 0..31 hold the rows of A, lanes 32..63 the
-// rows of I. Step k subtracts (a_rk / a_kk) times pivot row k from every row r > k, in both
-// halves; the pivot rows go through LDS and are read as broadcasts. By symmetry of the
-// trailing block, a_rk is entry r of the pivot row. Afterwards row k of the A half is
-// u_k = L_kk L^T(k, :) with u_kk = L_kk^2 (the k-th pivot), and the I half holds the unit
-// lower triangle M = (L D^-1)^-1, D = diag(L_kk), so L(:, k) = u_k / sqrt(u_kk) and
-// L^-1(k, :) = M(k, :) / sqrt(u_kk).
-// The loop over k is not unrolled: register indices are all compile-time, only the
-// predicates depend on k.
+// Each 32 x 32 factorization (with its inverse) runs on one wave, as symmetric Gaussian
+// elimination without pivoting. Lanes 0..31 (A half) hold the rows of A; lanes 32..63
+// (X half) hold the columns of I, which become those of L^-1 by forward substitution.
+// Step k: the trailing block stays symmetric, so its column k, which lanes r >= k post as
+// their own a_rk, is also pivot row k: one 8-byte store per lane, read back as broadcasts.
+// With u that column and p = u_k (the k-th pivot, L_kk^2), both halves apply
+//   own_j -= (own_k / p) u_j  for j > k,
+// for the A half on rows r > k only: the elimination of row r, and for the X half the
+// substitution x_j -= L_jk (x_k / L_kk) with L_jk = u_j / sqrt(p), whose division by L_kk
+// is deferred. Afterwards a_rr in row r of the A half is the r-th
+// pivot, and the entries j < r it posted, unchanged since, are L(r, j) sqrt(u_jj); the X
+// half ends with L^-1(j, c) = x_c(j) / sqrt(u_jj).
+// Steps are unrolled (compile-time k) so each touches only the entries j > k that change.
+template <int K>
+__device__ __forceinline__ void chol32_step(double (&a)[32], double* col, int r, int half,
+                                            bool& bad) {
+  // lanes that post nothing write a slot of col[32..63] nobody reads: a store without a
+  // branch around it (a branch per step more than doubles the registers the steps take)
+  col[(!half && r >= K) ? r : 32 + r] = a[K];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // every read of the step is issued before any arithmetic waits on one
+  constexpr int J0 = K & ~1;   // the pair holding entry K
+  double u[32];
+#pragma unroll
+  for (int j = J0; j < 32; j += 2) {
+    const double2 v = *(const double2*)&col[j];
+    u[j] = v.x;
+    u[j + 1] = v.y;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  double p = u[K];
+  if (!(p > 0.0)) {
+    bad = true;
+    p = 1e-300;
+  }
+  // 1 / p from the hardware estimate and two Newton steps (p > 0 here)
+  double ip = __builtin_amdgcn_rcp(p);
+  ip = __builtin_fma(ip, __builtin_fma(-p, ip, 1.0), ip);
+  ip = __builtin_fma(ip, __builtin_fma(-p, ip, 1.0), ip);
+  const double m = (half || r > K) ? a[K] * ip : 0.0;
+#pragma unroll
+  for (int j = K + 1; j < 32; ++j) a[j] -= m * u[j];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int K>
+__device__ __forceinline__ void chol32_steps(double (&a)[32], double* col, int r, int half,
+                                             bool& bad) {
+  if constexpr (K < 32) {
+    chol32_step<K>(a, col, r, half, bad);
+    chol32_steps<K + 1>(a, col, r, half, bad);
+  }
+}
+
+// col: 64 doubles of LDS (the posted column and, above it, the slots of lanes not posting)
 __device__ __forceinline__ void chol32_wave(double (*L)[kNB + 1], double (*Li)[kNB + 1], int o,
-                                            double (*piv)[32], bool& bad) {
+                                            double* col, bool& bad) {
   const int lane = threadIdx.x & 63, r = lane & 31, half = lane >> 5;
   double a[32];
 #pragma unroll
@@ -1063,56 +1110,34 @@ __device__ __forceinline__ void chol32_wave(double (*L)[kNB + 1], double (*Li)[k
     const double v = L[o + (j <= r ? r : j)][o + (j <= r ? j : r)];   // lower triangle
     a[j] = half ? (j == r ? 1.0 : 0.0) : v;
   }
-  for (int k = 0; k < 32; ++k) {
-    if (r == k) {
+  chol32_steps<0>(a, col, r, half, bad);
+  // Lane r of the A half posted a_rj at step j < r and left it unchanged since, and a_rr is
+  // the r-th pivot: L(r, j) = a_rj / sqrt(u_jj) for j <= r. It posts 1 / sqrt(u_rr) (its own
+  // pivot has a run-time register index: select).
+  {
+    double dr = a[0];
 #pragma unroll
-      for (int j = 0; j < 32; j += 2) *(double2*)&piv[half][j] = make_double2(a[j], a[j + 1]);
+    for (int j = 1; j < 32; ++j) dr = j == r ? a[j] : dr;
+    if (!(dr > 0.0)) {
+      if (!half) bad = true;
+      dr = 1e-300;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // every read of the step is issued before any arithmetic waits on one
-    double2 x[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = *(const double2*)&piv[half][2 * j];
-    double p = piv[0][k];
-    const double ark = piv[0][r];
-    __builtin_amdgcn_sched_barrier(0);
-    if (!(p > 0.0)) {
-      bad = true;
-      p = 1e-300;
-    }
-    // 1 / p from the hardware estimate and two Newton steps (p > 0 here)
-    double ip = __builtin_amdgcn_rcp(p);
-    ip = __builtin_fma(ip, __builtin_fma(-p, ip, 1.0), ip);
-    ip = __builtin_fma(ip, __builtin_fma(-p, ip, 1.0), ip);
-    const double m = r > k ? ark * ip : 0.0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      a[2 * j] -= m * x[j].x;
-      a[2 * j + 1] -= m * x[j].y;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    col[r + 32 * half] = 1.0 / sqrt(dr);
   }
-  // u_rr through LDS (lane r's own a[r] has a run-time register index)
-  double dr = a[0];
-#pragma unroll
-  for (int j = 1; j < 32; ++j) dr = j == r ? a[j] : dr;
-  if (half == 0) piv[0][r] = dr;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  double u = piv[0][r];
-  if (!(u > 0.0)) {
-    bad = true;
-    u = 1e-300;
+#pragma unroll
+  for (int j = 0; j < 32; j += 2) {
+    const double2 v = *(const double2*)&col[j];
+    a[j] *= v.x;
+    a[j + 1] *= v.y;
   }
-  const double inv = 1.0 / sqrt(u);
   if (half == 0) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) L[o + j][o + r] = j >= r ? a[j] * inv : 0.0;
+    for (int j = 0; j < 32; ++j) L[o + r][o + j] = j <= r ? a[j] : 0.0;
   } else {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) Li[o + r][o + j] = j <= r ? a[j] * inv : 0.0;
+    for (int j = 0; j < 32; ++j) Li[o + j][o + r] = j >= r ? a[j] : 0.0;
   }
 }
 
@@ -1138,7 +1163,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv,
   __shared__ double L[kNB][kNB + 1];    // the block, then its factor
   __shared__ double Li[kNB][kNB + 1];   // the inverse of the factor
   __shared__ double T[32][kNB + 1];     // L21 L11^-1
-  __shared__ double piv[2][32];         // pivot rows of the wave-level eliminations
+  __shared__ __align__(16) double piv[64];   // pivot columns of the wave-level eliminations
   __shared__ int badf;
   const int head = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
