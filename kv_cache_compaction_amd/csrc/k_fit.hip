@@ -1242,12 +1242,37 @@ __device__ __forceinline__ void mm_rows64(double (&acc)[4][4], const double (*P)
   }
 }
 
-// L_ik = A_ik Linv_kk^T for block rows i > kb: (A_ik Linv^T)[u][v] = sum_k A_ik[u][k] Linv[v][k].
-__global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double* Linv, int ld,
-                                                         int kb, int nb) {
-  __shared__ double x[kNB][kLdp];
-  __shared__ double li[kNB][kLdp];
-  const int head = blockIdx.y, ib = kb + 1 + blockIdx.x, tid = threadIdx.x;
+// out[r][c] = sum_k M[r][k] X[k][c] for a 64 x 32 slice: rows tr, tr + 32 (tr = tid / 8),
+// columns tc + 8 b (tc = tid % 8).
+__device__ __forceinline__ void mm_slice(double (&acc)[2][4], const double (*M)[kLdp],
+                                         const double (*X)[33], int tid) {
+  const int tr = tid >> 3, tc = tid & 7;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+#pragma unroll 4
+  for (int k = 0; k < kNB; ++k) {
+    const double m0 = M[tr][k], m1 = M[tr + 32][k];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const double xv = X[k][tc + 8 * b];
+      acc[0][b] += m0 * xv;
+      acc[1][b] += m1 * xv;
+    }
+  }
+}
+
+// The workgroup bodies below take their LDS from the kernel that runs them, so kernels that
+// combine two kinds of workgroup need only the larger of their footprints: two 64 x 65 tiles.
+typedef double LdsTile[kNB][kLdp];
+__device__ __forceinline__ double (*as_slice(LdsTile& t))[33] { return (double (*)[33])&t[0][0]; }
+
+// L_ik = A_ik Linv_kk^T for block row ib > kb: (A_ik Linv^T)[u][v] = sum_k A_ik[u][k] Linv[v][k].
+__device__ __forceinline__ void chol_panel_body(double* A, const double* Linv, int ld, int kb,
+                                                int nb, int ib, int head, LdsTile& x,
+                                                LdsTile& li) {
+  const int tid = threadIdx.x;
   double* Ai = A + (size_t)head * ld * ld + (size_t)ib * kNB * ld + kb * kNB;
   BlockRegs<kNB> ra, rl;
   ra.load(Ai, ld, tid);
@@ -1264,14 +1289,10 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double
     for (int b = 0; b < 4; ++b) Ai[(size_t)(ti + 16 * a) * ld + tj + 16 * b] = acc[a][b];
 }
 
-// A_ij -= L_ik L_jk^T for kb < j <= i (lower block pairs enumerated by blockIdx.x).
-__global__ __launch_bounds__(256) void chol_update_kernel(double* A, int ld, int kb, int nb) {
-  __shared__ double li[kNB][kLdp];
-  __shared__ double lj[kNB][kLdp];
-  const int head = blockIdx.y, tid = threadIdx.x;
-  int a0, b0;
-  tri_index(blockIdx.x, a0, b0);
-  const int ib = kb + 1 + a0, jb = kb + 1 + b0;
+// A_ij -= L_ik L_jk^T for the lower block pair (ib, jb), kb < jb <= ib.
+__device__ __forceinline__ void chol_update_body(double* A, int ld, int kb, int ib, int jb,
+                                                 int head, LdsTile& li, LdsTile& lj) {
+  const int tid = threadIdx.x;
   double* Ah = A + (size_t)head * ld * ld;
   double* Aij = Ah + (size_t)ib * kNB * ld + jb * kNB;
   BlockRegs<kNB> ri, rj;
@@ -1294,34 +1315,12 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* A, int ld, int
     for (int b = 0; b < 4; ++b) Aij[(size_t)(ti + 16 * a) * ld + tj + 16 * b] = cur[a][b] - acc[a][b];
 }
 
-// out[r][c] = sum_k M[r][k] X[k][c] for a 64 x 32 slice: rows tr, tr + 32 (tr = tid / 8),
-// columns tc + 8 b (tc = tid % 8).
-__device__ __forceinline__ void mm_slice(double (&acc)[2][4], const double (*M)[kLdp],
-                                         const double (*X)[33], int tid) {
-  const int tr = tid >> 3, tc = tid & 7;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-#pragma unroll 4
-  for (int k = 0; k < kNB; ++k) {
-    const double m0 = M[tr][k], m1 = M[tr + 32][k];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const double xv = X[k][tc + 8 * b];
-      acc[0][b] += m0 * xv;
-      acc[1][b] += m1 * xv;
-    }
-  }
-}
-
-// R_kb <- Linv_kk R_kb (forward) or Linv_kk^T R_kb (backward); one workgroup per
-// (head, 32-column slice of R).
-__global__ __launch_bounds__(256) void trsm_diag_kernel(double* R, const double* Linv, int ld,
-                                                        int D, int kb, int nb, int trans) {
-  __shared__ double m[kNB][kLdp];
-  __shared__ double x[kNB][33];
-  const int head = blockIdx.y, c0 = blockIdx.x * 32, tid = threadIdx.x;
+// R_kb <- Linv_kk R_kb (forward) or Linv_kk^T R_kb (backward) for the 32 columns from c0.
+__device__ __forceinline__ void trsm_diag_body(double* R, const double* Linv, int ld, int D,
+                                               int kb, int nb, int trans, int head, int c0,
+                                               LdsTile& m, LdsTile& xt) {
+  const int tid = threadIdx.x;
+  double (*x)[33] = as_slice(xt);
   double* Rh = R + ((size_t)head * ld + (size_t)kb * kNB) * D + c0;
   BlockRegs<kNB> rm;
   BlockRegs<32> rx;
@@ -1340,13 +1339,13 @@ __global__ __launch_bounds__(256) void trsm_diag_kernel(double* R, const double*
     for (int b = 0; b < 4; ++b) Rh[(size_t)(tr + 32 * a) * D + tc + 8 * b] = acc[a][b];
 }
 
-// forward: R_i -= L_{i,kb} R_kb for i > kb;  backward: R_i -= L_{kb,i}^T R_kb for i < kb.
-__global__ __launch_bounds__(256) void trsm_update_kernel(double* R, const double* A, int ld,
-                                                          int D, int kb, int trans) {
-  __shared__ double m[kNB][kLdp];
-  __shared__ double x[kNB][33];
-  const int head = blockIdx.z, c0 = blockIdx.y * 32, tid = threadIdx.x;
-  const int ib = trans ? blockIdx.x : kb + 1 + blockIdx.x;
+// forward: R_ib -= L_{ib,kb} R_kb (ib > kb);  backward: R_ib -= L_{kb,ib}^T R_kb (ib < kb);
+// for the 32 columns from c0.
+__device__ __forceinline__ void trsm_update_body(double* R, const double* A, int ld, int D,
+                                                 int kb, int ib, int trans, int head, int c0,
+                                                 LdsTile& m, LdsTile& xt) {
+  const int tid = threadIdx.x;
+  double (*x)[33] = as_slice(xt);
   const double* Ah = A + (size_t)head * ld * ld;
   double* Rh = R + (size_t)head * ld * D + c0;
   BlockRegs<kNB> rm;
@@ -1371,6 +1370,48 @@ __global__ __launch_bounds__(256) void trsm_update_kernel(double* R, const doubl
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) Ri[(size_t)(tr + 32 * a) * D + tc + 8 * b] = cur[a][b] - acc[a][b];
+}
+
+// Step kb of the factorization, after the diagonal block: workgroups x < m (m = nb - kb - 1)
+// form the panel L_ik, the next D / 32 the forward solve's Z_kb = Linv_kk R_kb, whose inputs
+// (R_kb after the updates of steps < kb, and Linv_kk) are complete at this point.
+__global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double* Linv,
+                                                         double* R, int ld, int D, int kb,
+                                                         int nb) {
+  __shared__ LdsTile s0, s1;
+  const int head = blockIdx.y, m = nb - kb - 1;
+  if ((int)blockIdx.x < m) chol_panel_body(A, Linv, ld, kb, nb, kb + 1 + blockIdx.x, head, s0, s1);
+  else trsm_diag_body(R, Linv, ld, D, kb, nb, 0, head, (blockIdx.x - m) * 32, s0, s1);
+}
+
+// Step kb's trailing update: workgroups x < m (m + 1) / 2 update the lower block pairs
+// A_ij -= L_ik L_jk^T (kb < j <= i), the next m D / 32 the forward solve's R_i -= L_ik Z_kb.
+__global__ __launch_bounds__(256) void chol_update_kernel(double* A, double* R, int ld, int D,
+                                                          int kb, int nb) {
+  __shared__ LdsTile s0, s1;
+  const int head = blockIdx.y, m = nb - kb - 1, ntri = m * (m + 1) / 2;
+  if ((int)blockIdx.x < ntri) {
+    int a0, b0;
+    tri_index(blockIdx.x, a0, b0);
+    chol_update_body(A, ld, kb, kb + 1 + a0, kb + 1 + b0, head, s0, s1);
+  } else {
+    const int e = blockIdx.x - ntri, ns = D / 32;
+    trsm_update_body(R, A, ld, D, kb, kb + 1 + e / ns, 0, head, (e % ns) * 32, s0, s1);
+  }
+}
+
+// The backward solve, L^T C = Z, one block row at a time: R_kb <- Linv_kk^T R_kb ...
+__global__ __launch_bounds__(256) void trsm_back_diag_kernel(double* R, const double* Linv,
+                                                             int ld, int D, int kb, int nb) {
+  __shared__ LdsTile s0, s1;
+  trsm_diag_body(R, Linv, ld, D, kb, nb, 1, blockIdx.y, blockIdx.x * 32, s0, s1);
+}
+
+// ... then R_i -= L_{kb,i}^T R_kb for every block row i < kb.
+__global__ __launch_bounds__(256) void trsm_back_update_kernel(double* R, const double* A, int ld,
+                                                               int D, int kb) {
+  __shared__ LdsTile s0, s1;
+  trsm_update_body(R, A, ld, D, kb, blockIdx.x, 1, blockIdx.z, blockIdx.y * 32, s0, s1);
 }
 
 __global__ __launch_bounds__(256) void store_cv_kernel(const double* R, float* Cv, int t, int ld,
@@ -1746,32 +1787,24 @@ hipError_t launch_fit_values(const FitArgs& a) {
     hipLaunchKernelGGL((vec_reduce_kernel<double>), dim3(cdiv((long long)ld * d, 256), H),
                        dim3(256), 0, st, pl.Rpart, pl.R, t, tpad, ld, d, nch);
   }
-  // Cholesky
+  // Cholesky, with the forward solve L Z = R folded into each step's panel and update
+  // launches; then the backward solve L^T C = Z
   for (int kb = 0; kb < nb; ++kb) {
     hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv, ld, kb, nb,
                        status);
     const int m = nb - kb - 1;
-    if (m > 0) {
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(m, H), dim3(256), 0, st, pl.A,
-                         (const double*)pl.Linv, ld, kb, nb);
-      hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2, H), dim3(256), 0, st, pl.A,
-                         ld, kb, nb);
-    }
-  }
-  // L Z = R, then L^T C = Z
-  for (int kb = 0; kb < nb; ++kb) {
-    hipLaunchKernelGGL(trsm_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
-                       (const double*)pl.Linv, ld, d, kb, nb, 0);
-    if (nb - kb - 1 > 0)
-      hipLaunchKernelGGL(trsm_update_kernel, dim3(nb - kb - 1, d / 32, H), dim3(256), 0, st,
-                         pl.R, (const double*)pl.A, ld, d, kb, 0);
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(m + d / 32, H), dim3(256), 0, st, pl.A,
+                       (const double*)pl.Linv, pl.R, ld, d, kb, nb);
+    if (m > 0)
+      hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2 + m * (d / 32), H), dim3(256),
+                         0, st, pl.A, pl.R, ld, d, kb, nb);
   }
   for (int kb = nb - 1; kb >= 0; --kb) {
-    hipLaunchKernelGGL(trsm_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
-                       (const double*)pl.Linv, ld, d, kb, nb, 1);
+    hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
+                       (const double*)pl.Linv, ld, d, kb, nb);
     if (kb > 0)
-      hipLaunchKernelGGL(trsm_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
-                         (const double*)pl.A, ld, d, kb, 1);
+      hipLaunchKernelGGL(trsm_back_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
+                         (const double*)pl.A, ld, d, kb);
   }
   hipLaunchKernelGGL(store_cv_kernel, dim3(cdiv((long long)t * d, 256), H), dim3(256), 0, st,
                      (const double*)pl.R, a.Cv, t, ld, d, status);
