@@ -1010,6 +1010,10 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
 // its global loads (16-byte, one per register pair) before it writes any of them to LDS, so
 // a block costs one memory latency rather than one per element.
 constexpr int kLdp = kNB + 1;   // LDS row pitch (odd: column reads by 16 rows hit 16 banks)
+// The workgroup bodies below take their LDS from the kernel that runs them, so kernels that
+// combine two kinds of workgroup need only the larger of their footprints: two 64 x 65 tiles
+// (and the 64 pivot slots of the diagonal factorization).
+typedef double LdsTile[kNB][kLdp];
 
 template <int W>
 struct BlockRegs {
@@ -1158,14 +1162,13 @@ __device__ __forceinline__ void mm32(double (&out)[4], const double (*P)[kNB + 1
   }
 }
 
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
-                                                        int nb, int32_t* status) {
-  __shared__ double L[kNB][kNB + 1];    // the block, then its factor
-  __shared__ double Li[kNB][kNB + 1];   // the inverse of the factor
-  __shared__ double T[32][kNB + 1];     // L21 L11^-1
-  __shared__ __align__(16) double piv[64];   // pivot columns of the wave-level eliminations
-  __shared__ int badf;
-  const int head = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+// The diagonal block kb of one head. LDS: L (the block, then its factor), Li (the inverse of
+// the factor; while L22 is factored its upper right quadrant, zero in the result, holds
+// T = L21 L11^-1), piv (the wave-level eliminations' pivot columns), badf.
+__device__ __forceinline__ void chol_diag_body(double* A, double* Linv, int ld, int kb, int nb,
+                                               int32_t* status, int head, LdsTile& L,
+                                               LdsTile& Li, double* piv, int& badf) {
+  const int tid = threadIdx.x, wave = tid >> 6;
   double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
   {
     BlockRegs<kNB> ra;
@@ -1199,12 +1202,12 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv,
       const int ii = e >> 5, jj = e & 31;
       double v = 0.0;
       for (int k = jj; k < 32; ++k) v += L[32 + ii][k] * Li[k][jj];
-      T[ii][jj] = v;
+      Li[ii][32 + jj] = v;   // T
     }
   }
   __syncthreads();
   // Li21 = -L22^-1 T
-  mm32<false>(acc, Li, 32, 32, T, 0, 0, tid);
+  mm32<false>(acc, Li, 32, 32, Li, 0, 32, tid);
 #pragma unroll
   for (int m = 0; m < 4; ++m) Li[32 + i][j0 + 8 * m] = -acc[m];
   if (bad) badf = 1;
@@ -1216,6 +1219,14 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv,
     Lo[e] = c <= r ? Li[r][c] : 0.0;
   }
   if (tid == 0 && badf && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
+}
+
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
+                                                        int nb, int32_t* status) {
+  __shared__ LdsTile s0, s1;
+  __shared__ __align__(16) double piv[64];
+  __shared__ int badf;
+  chol_diag_body(A, Linv, ld, kb, nb, status, blockIdx.x, s0, s1, piv, badf);
 }
 
 
@@ -1263,9 +1274,6 @@ __device__ __forceinline__ void mm_slice(double (&acc)[2][4], const double (*M)[
   }
 }
 
-// The workgroup bodies below take their LDS from the kernel that runs them, so kernels that
-// combine two kinds of workgroup need only the larger of their footprints: two 64 x 65 tiles.
-typedef double LdsTile[kNB][kLdp];
 __device__ __forceinline__ double (*as_slice(LdsTile& t))[33] { return (double (*)[33])&t[0][0]; }
 
 // L_ik = A_ik Linv_kk^T for block row ib > kb: (A_ik Linv^T)[u][v] = sum_k A_ik[u][k] Linv[v][k].
@@ -1386,14 +1394,23 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double
 
 // Step kb's trailing update: workgroups x < m (m + 1) / 2 update the lower block pairs
 // A_ij -= L_ik L_jk^T (kb < j <= i), the next m D / 32 the forward solve's R_i -= L_ik Z_kb.
-__global__ __launch_bounds__(256) void chol_update_kernel(double* A, double* R, int ld, int D,
-                                                          int kb, int nb) {
+// Workgroup 0 takes the pair (kb + 1, kb + 1) and then factors that block, the next step's
+// diagonal block, while the others finish the update (lookahead: no launch of its own).
+__global__ __launch_bounds__(256) void chol_update_kernel(double* A, double* R, double* Linv,
+                                                          int32_t* status, int ld, int D, int kb,
+                                                          int nb) {
   __shared__ LdsTile s0, s1;
+  __shared__ __align__(16) double piv[64];
+  __shared__ int badf;
   const int head = blockIdx.y, m = nb - kb - 1, ntri = m * (m + 1) / 2;
   if ((int)blockIdx.x < ntri) {
     int a0, b0;
     tri_index(blockIdx.x, a0, b0);
     chol_update_body(A, ld, kb, kb + 1 + a0, kb + 1 + b0, head, s0, s1);
+    if (blockIdx.x == 0) {   // a0 = b0 = 0: the block just written (same workgroup)
+      __syncthreads();
+      chol_diag_body(A, Linv, ld, kb + 1, nb, status, head, s0, s1, piv, badf);
+    }
   } else {
     const int e = blockIdx.x - ntri, ns = D / 32;
     trsm_update_body(R, A, ld, D, kb, kb + 1 + e / ns, 0, head, (e % ns) * 32, s0, s1);
@@ -1789,15 +1806,16 @@ hipError_t launch_fit_values(const FitArgs& a) {
   }
   // Cholesky, with the forward solve L Z = R folded into each step's panel and update
   // launches; then the backward solve L^T C = Z
+  // (the diagonal blocks after the first are factored inside the previous step's update)
+  hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv, ld, 0, nb,
+                     status);
   for (int kb = 0; kb < nb; ++kb) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv, ld, kb, nb,
-                       status);
     const int m = nb - kb - 1;
     hipLaunchKernelGGL(chol_panel_kernel, dim3(m + d / 32, H), dim3(256), 0, st, pl.A,
                        (const double*)pl.Linv, pl.R, ld, d, kb, nb);
     if (m > 0)
       hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2 + m * (d / 32), H), dim3(256),
-                         0, st, pl.A, pl.R, ld, d, kb, nb);
+                         0, st, pl.A, pl.R, pl.Linv, status, ld, d, kb, nb);
   }
   for (int kb = nb - 1; kb >= 0; --kb) {
     hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
