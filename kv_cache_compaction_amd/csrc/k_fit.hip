@@ -794,23 +794,34 @@ constexpr int kNnlsCoopMinT = 256;            // smaller systems: one workgroup 
 constexpr size_t kNnlsCoopLds = 144 * 1024;   // dynamic LDS for G rows + the vector
 constexpr int kNnlsSpin = 1 << 22;            // polls before a barrier wait gives up
 
-// Loads of data that decide control flow, at device scope.
+// Device-scope loads and stores: they read and write the device's coherence point, not a
+// copy in a CU's or an XCD's cache, so values that change while the workgroups of a head
+// run go through these.
 __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Barrier among the workgroups of one head: the m-th completes when the head's counter
-// reaches m * P. Every wave first waits until its own stores have reached L2 (vmcnt 0);
-// then one thread per workgroup adds to the counter with release semantics (the L2
-// write-back makes those stores visible device-wide), polls it with device-scope loads and
-// finishes with one acquire fence, which drops stale cache lines before any thread reads
-// what the others wrote. A wait longer than kNnlsSpin polls
-// (seconds) marks the workgroup as timed out, after which it waits no more and stops.
+// reaches m * P. Every wave first waits until its own stores have completed (vmcnt 0);
+// then one thread per workgroup adds to the counter and polls it with device-scope loads.
+// FENCED: the add has release semantics and the wait ends with an acquire fence (an L2
+// write-back before, an invalidate after: about 10 us per barrier), so data written and
+// read with ordinary accesses is seen. Otherwise the counter is relaxed (about 4 us): the
+// data that crosses workgroups must then be written with st_dev and read with ld_dev; the
+// vmcnt wait makes those stores complete before the add, and the readers issue their
+// loads only after the poll has seen the count (the barrier's closing __syncthreads).
+// A wait longer than kNnlsSpin polls (seconds) marks the workgroup as timed out, after
+// which it waits no more and stops.
+template <bool FENCED>
 __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_out) {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0) only
   __syncthreads();
   if (threadIdx.x == 0 && !*timed_out) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (FENCED) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(2);
@@ -819,7 +830,7 @@ __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_ou
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (FENCED) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -837,6 +848,9 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
   if (tid == 0) timed_out = 0;
   float* xs = smem;
   float* Gs = smem + t;
+  // this workgroup's rows of the extrapolated iterate and of the current one, formed with xs
+  float* yr = Gs + (g_lds ? (size_t)(r1 - r0) * t : 0);
+  float* vr = yr + rb;
   const float* G = s.G + (size_t)head * t * t;
   if (g_lds)
     for (int e = tid; e < (r1 - r0) * t; e += 256) Gs[e] = G[(size_t)r0 * t + e];
@@ -846,7 +860,10 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
   const size_t ps = (size_t)s.nblk;   // partial slots per head and parity
   int* bar = s.bar + head;
   int nbar = 0;
-  auto barrier = [&]() { head_barrier(bar, ++nbar * P, &timed_out); };
+  // after the set-up (one fenced barrier) G's diagonal scaling dinv and hs stay fixed and
+  // are read with ordinary loads; the vectors and partials that change per step go through
+  // st_dev / ld_dev, so the steps' barriers need no fences
+  auto barrier = [&]() { head_barrier<false>(bar, ++nbar * P, &timed_out); };
   // the head's P partials (float2) staged once, one load per thread
   auto stage = [&](const float2* src) {
     for (int b = tid; b < P; b += 256) {
@@ -880,7 +897,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
     s.PN[((size_t)head * 2 + 0) * ps + part] = part == 0 ? (float)t : 0.f;
     s.P[((size_t)head * 2 + 0) * ps + part] = make_float2(0.f, INFINITY);
   }
-  barrier();
+  head_barrier<true>(bar, ++nbar * P, &timed_out);
   stage(s.init + (size_t)head * ps);
   float hsmax = 0.f;
   bool bad = false;
@@ -907,7 +924,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
     const float sc = nrm > 0.f ? rsqrtf(nrm) : 0.f;
     const float* xin = s.X + ((size_t)head * 2 + (k & 1)) * t;
     float* xout = s.X + ((size_t)head * 2 + ((k + 1) & 1)) * t;
-    for (int j = tid; j < t; j += 256) xs[j] = xin[j] * sc * dinv[j];
+    for (int j = tid; j < t; j += 256) xs[j] = ld_dev(xin + j) * sc * dinv[j];
     __syncthreads();
     float part2 = 0.f;
     for (int i = r0 + wave; i < r1; i += 4) {
@@ -918,12 +935,12 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
       const float y = acc * dinv[i];
       if (lane == 0) {
-        xout[i] = y;
+        st_dev(xout + i, y);
         part2 += y * y;
       }
     }
     part2 = block_sum(part2, red);
-    if (tid == 0) s.PN[((size_t)head * 2 + ((k + 1) & 1)) * ps + part] = part2;
+    if (tid == 0) st_dev(s.PN + ((size_t)head * 2 + ((k + 1) & 1)) * ps + part, part2);
     barrier();
   }
   const float L = 1.1f * sqrtf(head_norm(kPow & 1)) + 1e-30f;
@@ -948,7 +965,15 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
     const float* vprev = s.V + ((size_t)head * 3 + (k + 2) % 3) * t;
     const float* vcur = s.V + ((size_t)head * 3 + k % 3) * t;
     float* vnext = s.V + ((size_t)head * 3 + (k + 1) % 3) * t;
-    for (int j = tid; j < t; j += 256) xs[j] = (vcur[j] + mom * (vcur[j] - vprev[j])) * dinv[j];
+    for (int j = tid; j < t; j += 256) {
+      const float vc = ld_dev(vcur + j), vp = ld_dev(vprev + j);
+      const float y = vc + mom * (vc - vp);
+      xs[j] = y * dinv[j];
+      if (j >= r0 && j < r1) {
+        yr[j - r0] = y;
+        vr[j - r0] = vc;
+      }
+    }
     __syncthreads();
     float pdot = 0.f, pgm = 0.f;
     for (int i = r0 + wave; i < r1; i += 4) {
@@ -958,7 +983,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
       const float di = dinv[i];
-      const float y = vcur[i] + mom * (vcur[i] - vprev[i]);
+      const float vc = vr[i - r0], y = yr[i - r0];
       const float g = acc * di - hs[i];
       float vn = 0.f;
       if (di > 0.f) {
@@ -967,14 +992,18 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
         vn = fminf(fmaxf(y - g / L, lo), hi);
       }
       if (lane == 0) {
-        vnext[i] = vn;
-        pdot += (vn - vcur[i]) * (y - vn);
+        st_dev(vnext + i, vn);
+        pdot += (vn - vc) * (y - vn);
         pgm = fmaxf(pgm, fabsf(y - vn) * L);
       }
     }
     pdot = block_sum(pdot, red);
     pgm = block_max(pgm, red);
-    if (tid == 0) s.P[((size_t)head * 2 + ((k + 1) & 1)) * ps + part] = make_float2(pdot, pgm);
+    if (tid == 0) {
+      float* q = (float*)(s.P + ((size_t)head * 2 + ((k + 1) & 1)) * ps + part);
+      st_dev(q, pdot);
+      st_dev(q + 1, pgm);
+    }
     tk = tn;
     barrier();
   }
@@ -988,7 +1017,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
   float nbw = 0.f;
   for (int j = r0 + tid; j < r1; j += 256) {
     const float di = dinv[j];
-    float w = di > 0.f ? v[j] * di : s.lo;
+    float w = di > 0.f ? ld_dev(v + j) * di : s.lo;
     w = fminf(fmaxf(w, s.lo), s.hi);
     if (!isfinite(w)) nbw = 1.f;
     if (w_out) w_out[(size_t)head * t + j] = w;
@@ -1707,8 +1736,9 @@ hipError_t launch_fit_beta(const FitArgs& a) {
       if (P > s.nblk) P = s.nblk;
       if (P > 256) P = 256;   // the partials of a head are staged in one pass
       const int rb = (t + P - 1) / P;
-      int g_lds = (size_t)(t + (size_t)rb * t) * sizeof(float) <= kNnlsCoopLds ? 1 : 0;
-      const size_t shmem = (size_t)(t + (g_lds ? (size_t)rb * t : 0)) * sizeof(float);
+      // dynamic LDS: the vector (t), the rows of G when they fit (rb t), two row slices (2 rb)
+      int g_lds = (size_t)(t + (size_t)rb * t + 2 * (size_t)rb) * sizeof(float) <= kNnlsCoopLds ? 1 : 0;
+      const size_t shmem = (size_t)(t + (g_lds ? (size_t)rb * t : 0) + 2 * (size_t)rb) * sizeof(float);
       int max_iter = a.max_iter;
       float* wout = a.w;
       float* beta = a.beta;
