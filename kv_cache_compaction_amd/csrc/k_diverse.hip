@@ -20,19 +20,28 @@ namespace amc {
 
 constexpr int kFftSpin = 1 << 22;   // polls before a barrier wait gives up (seconds)
 
+// Device-scope loads and stores (the device's coherence point, not a CU's or an XCD's
+// cache copy): the only data the workgroups of a head exchange, their candidate slots,
+// goes through these.
 __device__ __forceinline__ int ld_dev_i(const int* q) {
   return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev_i(int* q, int v) {
+  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Barrier among the workgroups of one head (the m-th completes when the counter reaches
-// m * P): stores reach L2 first, one thread adds with release semantics and polls with
-// device-scope loads, one acquire fence drops stale lines. A wait longer than kFftSpin
-// polls marks the workgroup as timed out; it then stops.
+// m * P): every wave waits until its stores have completed (vmcnt 0), then one thread adds
+// to the counter and polls it with device-scope loads; readers load the slots only after
+// the poll has seen the count. No release/acquire fences: they would write back and
+// invalidate the whole L2 (about 10 us a barrier against 4 us), and the slots are written
+// and read at device scope. A wait longer than kFftSpin polls marks the workgroup as timed
+// out; it then stops.
 __device__ __forceinline__ void fft_barrier(int* ctr, int target, int* timed_out) {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0) only
   __syncthreads();
   if (threadIdx.x == 0 && !*timed_out) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(2);
@@ -41,7 +50,6 @@ __device__ __forceinline__ void fft_barrier(int* ctr, int target, int* timed_out
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -153,7 +161,10 @@ __global__ __launch_bounds__(256) void fft_kernel(const FftParams p) {
     }
     // the head's P candidates: publish, meet, and reduce them identically everywhere
     int2* slot = p.part + ((size_t)head * 2 + (step & 1)) * p.P;
-    if (tid == 0) slot[part] = make_int2(__float_as_int(bv), jsh);   // thread 0 holds the best
+    if (tid == 0) {   // thread 0 holds the best
+      st_dev_i(&slot[part].x, __float_as_int(bv));
+      st_dev_i(&slot[part].y, jsh);
+    }
     fft_barrier(&p.bar[head], ++nbar * p.P, &tout);
     if (tout) break;
     bv = -INFINITY;
@@ -317,7 +328,10 @@ __global__ __launch_bounds__(kFftRegThreads) void fft_reg_kernel(const FftParams
     }
     // the head's P candidates: publish, meet, and reduce them identically everywhere
     int2* slot = p.part + ((size_t)head * 2 + (step & 1)) * p.P;
-    if (tid == 0) slot[part] = make_int2(__float_as_int(bv), jsh);   // thread 0 holds the best
+    if (tid == 0) {   // thread 0 holds the best
+      st_dev_i(&slot[part].x, __float_as_int(bv));
+      st_dev_i(&slot[part].y, jsh);
+    }
     fft_barrier(&p.bar[head], ++nbar * p.P, &tout);
     if (tout) break;
     bv = -INFINITY;
