@@ -3,7 +3,8 @@
 // squares (§Choosing C_v), with A_i the biased compacted softmax of "Latent Compaction with
 // Test-Time Training", §3.1 Eq. 2-3.
 //
-// Gram builds. Neither the n x t design M nor A is ever stored. A workgroup owns one
+// Gram builds for t <= 256 (larger t store the design once and multiply it in tiles, see
+// k_syrk.hip). Neither the n x t design M nor A is stored here. A workgroup owns one
 // 128 x 128 tile (ta >= tb) of the t x t Gram and one chunk of queries. For every 32
 // queries, its four waves recompute the needed 32 x 32 score blocks Q C_k^T on bf16 MFMA
 // (query rows loaded in the kperm order), turn them into design entries
@@ -17,15 +18,19 @@
 //
 // NNLS. Accelerated projected gradient with Jacobi scaling (v = sqrt(diag G) * w),
 // step 1/L with L from power iteration, momentum restarted when the step turns back
-// (gradient-mapping test), stopped on the scaled gradient-mapping norm. One launch per
-// iteration; each workgroup owns 16 rows, redundantly reduces the previous launch's
-// per-block partial sums (fixed order) for the momentum scalars, and builds the full
-// extrapolated point in LDS. No grid-wide barrier is needed.
+// (gradient-mapping test), stopped on the scaled gradient-mapping norm. t <= 256: one
+// workgroup per head with G in LDS. Larger t: P co-resident workgroups per head
+// (cooperative launch), each owning a slice of rows (of G too when they fit in LDS), meeting
+// at a per-head barrier once per step; all reduce the same partials in the same fixed order.
+// If the cooperative launch is refused: one launch per step, each workgroup owning 16 rows
+// and redundantly reducing the previous launch's per-block partials.
 //
 // Ridge solve. (G_A + lambda I) C = A^T Y in fp64: right-looking blocked Cholesky with
 // 64 x 64 blocks (diagonal factor and its explicit inverse in one workgroup, panel as a
-// product with that inverse, trailing update per block pair), then blocked forward and
-// backward substitution with the stored diagonal inverses.
+// product with that inverse, trailing update per block pair). The forward substitution
+// runs as extra workgroups of the same launches, and each step's update launch also
+// factors the next diagonal block; then blocked backward substitution with the stored
+// diagonal inverses.
 #include "am_common.hpp"
 #include "am_internal.hpp"
 
