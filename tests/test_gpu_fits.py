@@ -210,3 +210,20 @@ def test_fit_calls_deterministic():
     b = amc.compact_head(dQ, dK, dV, w.t, causal=True, group=4)
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("w", [Workload("coop8", 8, 128, 1024, 4096, 320, "bf16", True, 4),
+                               Workload("coop2", 2, 128, 1536, 6144, 384, "bf16", True, 4)],
+                         ids=["8_heads_t320", "2_heads_t384"])
+def test_coop_nnls_repeats_bit_exactly(w):
+    """t > 256 runs the NNLS on several co-resident workgroups per head meeting at per-head
+    barriers, their vectors exchanged at device scope: three whole runs must agree bit for
+    bit (a value read before its writer's store had landed would change the iterates)."""
+    torch = _torch()
+    Q, K, V = synth.make_batch(w)
+    dQ, dK, dV = (to_dev(x, w.dtype) for x in (Q, K, V))
+    runs = [amc.compact_head(dQ, dK, dV, w.t, causal=w.causal, group=w.group) for _ in range(3)]
+    assert np.all(runs[0]["status"].cpu().numpy() == 0)
+    for r in runs[1:]:
+        for key in runs[0]:
+            assert torch.equal(runs[0][key], r[key]), key

@@ -97,3 +97,17 @@ def test_init_anchor_diverse_headline_size():
             assert not chosen[j] and dist[j] >= best * (1 - 1e-5) - 1e-6
             dist = np.minimum(dist, ((k - k[j]) ** 2).sum(axis=1))
             chosen[j] = True
+
+
+def test_traversal_repeats_bit_exactly():
+    """8192 keys per head span several co-resident workgroups that agree on each next key at
+    a per-head barrier (candidate slots exchanged at device scope): three runs must give the
+    same order."""
+    w = Workload("traversal_4x8k", 4, 128, 8192, 8192, 256, "bf16", False, 1)
+    Q, K, V = synth.make_batch(w)
+    dQ, dK = to_dev(Q, w.dtype), to_dev(K, w.dtype)
+    runs = [amc.init_anchor_diverse(dQ, dK, 128, causal=w.causal, group=w.group) for _ in range(3)]
+    assert np.all(runs[0][2].cpu().numpy() == 0)
+    for r in runs[1:]:
+        np.testing.assert_array_equal(runs[0][1].cpu().numpy(), r[1].cpu().numpy())
+        np.testing.assert_array_equal(runs[0][0].cpu().numpy(), r[0].cpu().numpy())
