@@ -120,7 +120,7 @@ def main():
                          "byte counters of that copy calibrate the HBM traffic of the kernels")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the per-head problems shard across GPUs without communication)", file=sys.stderr)
         sys.exit(2)
 

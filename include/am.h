@@ -48,7 +48,7 @@ typedef struct ihipStream_t* am_stream_t;
 typedef enum {
   AM_OK = 0,
   AM_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, t outside [1, T], ... */
-  AM_ERR_UNSUPPORTED = -2, /* valid request this build does not implement: d not 64/128,
+  AM_ERR_UNSUPPORTED = -2, /* valid request the library does not implement: d not 64/128,
                               n or T above 2^30, or t above 8192 in the fit calls */
   AM_ERR_WORKSPACE = -3,   /* ws_bytes smaller than am_workspace_bytes() */
   AM_ERR_DEVICE = -4       /* a HIP launch or device query failed */
