@@ -9,9 +9,11 @@
 // One workgroup per head. Scores map to order-preserving uint32 keys; a 4-pass, 8-bit
 // radix select (LDS histograms with integer atomics) finds the t-th largest key theta
 // and how many keys equal to theta are still needed. A stable compaction in index order
-// (wave ballots plus a 16-entry LDS scan per 1024 keys) then writes every key above
-// theta and the lowest-index keys equal to theta, already sorted. No sort of the t
-// survivors is needed. The gather copies the selected K (and V) rows bit for bit.
+// then writes every key above theta and the lowest-index keys equal to theta, already
+// sorted: each thread owns a contiguous segment of keys, counts its keys above and equal
+// to theta, and two block-wide scans give it the rank of its first equal key and of its
+// first output. No sort of the t survivors is needed. The gather copies the selected K
+// (and V) rows bit for bit.
 #include "am_common.hpp"
 #include "am_internal.hpp"
 
@@ -25,23 +27,27 @@ __device__ __forceinline__ unsigned order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive count of set flags before this thread (thread order) and the block total.
-__device__ __forceinline__ unsigned block_excl_count(bool f, unsigned* total, unsigned* wsum) {
+// Exclusive sum of one count per thread (thread order) and the block total.
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* total, unsigned* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const unsigned long long bal = __ballot(f);
-  const unsigned in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[w] = __popcll(bal);
+  unsigned x = v;   // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
   unsigned before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
-    const unsigned v = wsum[i];
-    before += (i < w) ? v : 0u;
-    tot += v;
+    const unsigned s = wsum[i];
+    before += (i < w) ? s : 0u;
+    tot += s;
   }
   __syncthreads();
   *total = tot;
-  return before + in_wave;
+  return before + x - v;
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ score,
@@ -64,19 +70,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      unsigned c = 0;
-      int dsel = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        const unsigned hc = hist[dg];
-        if (c + hc >= remaining) {
-          dsel = dg;
-          break;
-        }
-        c += hc;
+    // the digit: the largest dg whose count from the top, sum_{k >= dg} hist[k], reaches
+    // `remaining` (thread i takes digit 255 - i, so a scan in thread order sums from the top)
+    {
+      const int dg = 255 - tid;
+      const unsigned hc = tid < 256 ? hist[dg] : 0u;
+      unsigned total;
+      const unsigned above = block_excl_scan(hc, &total, wsum);   // sum over digits > dg
+      if (tid < 256 && above < remaining && above + hc >= remaining) {
+        sh_prefix = prefix | ((unsigned)dg << shift);
+        sh_remaining = remaining - above;
       }
-      sh_prefix = prefix | ((unsigned)dsel << shift);
-      sh_remaining = remaining - c;
+      if (tid == 0 && total < remaining) {   // cannot happen for t <= Tk; keep a defined state
+        sh_prefix = prefix;
+        sh_remaining = remaining - total;
+      }
     }
     __syncthreads();
     prefix = sh_prefix;
@@ -84,21 +92,29 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     mask |= 255u << shift;
     __syncthreads();
   }
-  // prefix = theta, the t-th largest key; `remaining` keys equal to theta are taken.
-  unsigned base_eq = 0, base_out = 0;
-  for (int c0 = 0; c0 < Tk; c0 += kSelThreads) {
-    const int j = c0 + tid;
-    const bool valid = j < Tk;
-    const unsigned u = valid ? order_key(sc[j]) : 0u;
-    const bool eq = valid && u == prefix;
-    const bool gt = valid && u > prefix;
-    unsigned eq_total, take_total;
-    const unsigned eq_before = block_excl_count(eq, &eq_total, wsum);
-    const bool take = gt || (eq && base_eq + eq_before < remaining);
-    const unsigned pos = block_excl_count(take, &take_total, wsum);
-    if (take && base_out + pos < (unsigned)t) out[base_out + pos] = j;
-    base_eq += eq_total;
-    base_out += take_total;
+  // prefix = theta, the t-th largest key; the `remaining` lowest-index keys equal to theta
+  // are taken. Thread segments in thread order are index order.
+  const int seg = (Tk + kSelThreads - 1) / kSelThreads;
+  const int j0 = min(Tk, tid * seg), j1 = min(Tk, j0 + seg);
+  unsigned n_eq = 0, n_gt = 0;
+  for (int j = j0; j < j1; ++j) {
+    const unsigned u = order_key(sc[j]);
+    n_eq += u == prefix;
+    n_gt += u > prefix;
+  }
+  unsigned eq_total, take_total;
+  const unsigned eq_before = block_excl_scan(n_eq, &eq_total, wsum);
+  const unsigned eq_take = eq_before >= remaining ? 0u : min(n_eq, remaining - eq_before);
+  unsigned pos = block_excl_scan(n_gt + eq_take, &take_total, wsum);
+  unsigned eq_seen = 0;
+  for (int j = j0; j < j1; ++j) {
+    const unsigned u = order_key(sc[j]);
+    bool take = u > prefix;
+    if (u == prefix) take = eq_seen++ < eq_take;
+    if (take) {
+      if (pos < (unsigned)t) out[pos] = j;
+      ++pos;
+    }
   }
 }
 
