@@ -1458,11 +1458,19 @@ __global__ __launch_bounds__(256) void trsm_back_diag_kernel(double* R, const do
   trsm_diag_body(R, Linv, ld, D, kb, nb, 1, blockIdx.y, blockIdx.x * 32, s0, s1);
 }
 
-// ... then R_i -= L_{kb,i}^T R_kb for every block row i < kb.
-__global__ __launch_bounds__(256) void trsm_back_update_kernel(double* R, const double* A, int ld,
-                                                               int D, int kb) {
+// ... then R_i -= L_{kb,i}^T R_kb for every block row i < kb. The workgroup of row kb - 1,
+// the only one that touches it, then forms the next step's R_{kb-1} <- Linv^T R_{kb-1} itself
+// (lookahead: the next diagonal product needs no launch of its own).
+__global__ __launch_bounds__(256) void trsm_back_update_kernel(double* R, const double* A,
+                                                               const double* Linv, int ld, int D,
+                                                               int kb, int nb) {
   __shared__ LdsTile s0, s1;
-  trsm_update_body(R, A, ld, D, kb, blockIdx.x, 1, blockIdx.z, blockIdx.y * 32, s0, s1);
+  const int head = blockIdx.z, c0 = blockIdx.y * 32;
+  trsm_update_body(R, A, ld, D, kb, blockIdx.x, 1, head, c0, s0, s1);
+  if ((int)blockIdx.x == kb - 1) {
+    __syncthreads();   // the rows just written are read back by this workgroup
+    trsm_diag_body(R, Linv, ld, D, kb - 1, nb, 1, head, c0, s0, s1);
+  }
 }
 
 __global__ __launch_bounds__(256) void store_cv_kernel(const double* R, float* Cv, int t, int ld,
@@ -1852,13 +1860,12 @@ hipError_t launch_fit_values(const FitArgs& a) {
       hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2 + m * (d / 32), H), dim3(256),
                          0, st, pl.A, pl.R, pl.Linv, status, ld, d, kb, nb);
   }
-  for (int kb = nb - 1; kb >= 0; --kb) {
-    hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
-                       (const double*)pl.Linv, ld, d, kb, nb);
-    if (kb > 0)
-      hipLaunchKernelGGL(trsm_back_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
-                         (const double*)pl.A, ld, d, kb);
-  }
+  // (each update launch also forms the next block row's diagonal product)
+  hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
+                     (const double*)pl.Linv, ld, d, nb - 1, nb);
+  for (int kb = nb - 1; kb > 0; --kb)
+    hipLaunchKernelGGL(trsm_back_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
+                       (const double*)pl.A, (const double*)pl.Linv, ld, d, kb, nb);
   hipLaunchKernelGGL(store_cv_kernel, dim3(cdiv((long long)t * d, 256), H), dim3(256), 0, st,
                      (const double*)pl.R, a.Cv, t, ld, d, status);
   if (a.out_resid) {
