@@ -394,8 +394,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_g_kernel(const float* __restr
   const float* src = part + ((size_t)head * nch * ntiles + tile) * kSyT * kSyT +
                      (size_t)(si * 64 % kSyT) * kSyT + sj * 64 % kSyT;
   const size_t cstride = (size_t)ntiles * kSyT * kSyT;
-  // 16 entries per thread, summed over the chunks in order with all 16 loads of a chunk in
-  // flight together
+  // 16 entries per thread, summed over the chunks in order
   constexpr int PER = 64 * 64 / 256;
   float acc[PER];
   bool live[PER];
@@ -405,13 +404,32 @@ __global__ __launch_bounds__(256) void syrk_reduce_g_kernel(const float* __restr
     acc[u] = 0.f;
     live[u] = si * 64 + r < t && sj * 64 + c < t;
   }
-  for (int ch = 0; ch < nch; ++ch) {
+  // every address lies in a chunk's 256 x 256 partial tile, so the loads are unconditional
+  // (a branch per load would wait for each one) and the padding is masked by a select; four
+  // chunks' loads are issued before their sums, which still run in chunk order
+  auto load_chunk = [&](int ch, float (&v)[PER]) {
     const float* sc = src + ch * cstride;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + 256 * u, r = e >> 6, c = e & 63;
-      if (live[u]) acc[u] += sc[(size_t)r * kSyT + c];
+      v[u] = sc[(size_t)r * kSyT + c];
     }
+  };
+  int ch = 0;
+  for (; ch + 4 <= nch; ch += 4) {
+    float v[4][PER];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_chunk(ch + q, v[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += live[u] ? v[q][u] : 0.f;
+  }
+  for (; ch < nch; ++ch) {
+    float v[PER];
+    load_chunk(ch, v);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc[u] += live[u] ? v[u] : 0.f;
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -446,6 +464,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_r_kernel(const float* __restr
   float acc = 0.f;
   if (j < t) {
     const int tile = nkb * (nkb + 1) / 2 + j / kSyT;
+#pragma unroll 8   // several chunks' loads in flight; the sum still runs in chunk order
     for (int ch = 0; ch < nch; ++ch)
       acc += part[(((size_t)head * nch + ch) * ntiles + tile) * kSyT * kSyT +
                   (size_t)c * kSyT + j % kSyT];
