@@ -34,6 +34,7 @@
 #include "am_common.hpp"
 #include "am_internal.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace amc {
@@ -840,7 +841,7 @@ __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_ou
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int max_iter, int g_lds,
+__global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int max_iter, int nlds,
                                                         float* w_out, float* beta,
                                                         int32_t* status) {
   extern __shared__ float smem[];
@@ -854,12 +855,12 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
   float* xs = smem;
   float* Gs = smem + t;
   // this workgroup's rows of the extrapolated iterate and of the current one, formed with xs
-  float* yr = Gs + (g_lds ? (size_t)(r1 - r0) * t : 0);
+  float* yr = Gs + (size_t)nlds * t;
   float* vr = yr + rb;
   const float* G = s.G + (size_t)head * t * t;
-  if (g_lds)
-    for (int e = tid; e < (r1 - r0) * t; e += 256) Gs[e] = G[(size_t)r0 * t + e];
-  auto grow = [&](int i) { return g_lds ? Gs + (size_t)(i - r0) * t : G + (size_t)i * t; };
+  // the first nlds of this workgroup's rows of G are held in LDS, the others read each step
+  for (int e = tid; e < min(nlds, r1 - r0) * t; e += 256) Gs[e] = G[(size_t)r0 * t + e];
+  auto grow = [&](int i) { return i - r0 < nlds ? Gs + (size_t)(i - r0) * t : G + (size_t)i * t; };
   float* dinv = s.dinv + (size_t)head * t;
   float* hs = s.hs + (size_t)head * t;
   const size_t ps = (size_t)s.nblk;   // partial slots per head and parity
@@ -1749,14 +1750,16 @@ hipError_t launch_fit_beta(const FitArgs& a) {
       if (P > s.nblk) P = s.nblk;
       if (P > 256) P = 256;   // the partials of a head are staged in one pass
       const int rb = (t + P - 1) / P;
-      // dynamic LDS: the vector (t), the rows of G when they fit (rb t), two row slices (2 rb)
-      int g_lds = (size_t)(t + (size_t)rb * t + 2 * (size_t)rb) * sizeof(float) <= kNnlsCoopLds ? 1 : 0;
-      const size_t shmem = (size_t)(t + (g_lds ? (size_t)rb * t : 0) + 2 * (size_t)rb) * sizeof(float);
+      // dynamic LDS: the vector (t), two row slices (2 rb) and as many of the workgroup's
+      // rows of G as fit (nlds t)
+      const size_t lds_f = kNnlsCoopLds / sizeof(float), fixed = (size_t)t + 2 * (size_t)rb;
+      int nlds = lds_f > fixed ? (int)std::min<size_t>((size_t)rb, (lds_f - fixed) / t) : 0;
+      const size_t shmem = (fixed + (size_t)nlds * t) * sizeof(float);
       int max_iter = a.max_iter;
       float* wout = a.w;
       float* beta = a.beta;
       int32_t* stp = status;
-      void* args[] = {&s, &P, &max_iter, &g_lds, &wout, &beta, &stp};
+      void* args[] = {&s, &P, &max_iter, &nlds, &wout, &beta, &stp};
       hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(H, 256)), dim3(256), 0, st, pl.bar, H);
       (void)hipFuncSetAttribute((const void*)nnls_coop_kernel,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
