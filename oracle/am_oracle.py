@@ -30,10 +30,10 @@ exactly before they arrive here):
   E   the compacted attention itself, to evaluate any (idx, beta, C_v): biased scores
       l(q) = scale K_cmp q + b (Latent Compaction §3.1, Eq. 2), output Eq. 3 and
       normalizer Z_cmp = 1^T exp(l) (Eq. 4), plus the residuals compared in parity.
-  C   attention through a compacted cache followed by ordinary appended entries: each
-      branch gives an output and a log-normalizer (Latent Compaction App. A.2, the
-      normalizer-aware cache attention: biased and slot-masked document branch, causal
-      unbiased branch for the new tokens), combined by Eq. 5 in log space.
+  C   attention through a compacted cache followed by ordinary appended entries (Latent
+      Compaction §3.1 Eq. 2-5; App. A.2, attention over a compacted cache plus new
+      tokens): each entry set gives masked, biased scores (Eq. 2), a log-normalizer
+      (Eq. 4) and an output (Eq. 3), and the two sets are merged by Eq. 5 in log space.
   F   the fast variants of the "Compaction" blog: beta by uniform redistribution of the
       missing mass (§Choosing beta) and direct values C_v = V[idx] (§Choosing C_v).
   I   anchor + diversifier initialization (Latent Compaction §3.2): anchors by maximum
@@ -44,9 +44,9 @@ exactly before they arrive here):
       output and log-normalizer errors of sampled query positions.
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
-masked keys are excluded (exp(-inf) = 0), which equals the pseudocode's finfo.min fill
-whenever a row keeps at least one visible entry (key 0 is visible to every query); the
-RMS divisor is n for every key; w_j = 0 gives beta_j = -inf; a query with no visible
+masked entries are excluded (weight exp(-inf) = 0), and an entry set a row cannot see
+at all has log Z = -inf and takes no weight in Eq. 5 (key 0 is visible to every query of
+the full cache, so its rows always see one); the RMS divisor is n for every key; w_j = 0 gives beta_j = -inf; a query with no visible
 selected key contributes a zero row to A; lambda is absolute on the summed normal
 equations; natural log/exp throughout, with the 1/sqrt(d) scale applied to q.k.
 
@@ -59,6 +59,7 @@ from __future__ import annotations
 import numpy as np
 import scipy.linalg
 import scipy.optimize
+import scipy.special
 
 SCORE_MODES = ("rms", "mean", "max")
 MASS_MODES = ("relative", "absolute")
@@ -349,40 +350,34 @@ def compacted_attention(Q, Ck, idx, beta, Cv, scale, causal=False, group=1):
 # --------------------------------------------------------------------------------------
 # C: cache attention with appended entries, and the log-space combination
 # --------------------------------------------------------------------------------------
-def branch_attention(Q, keys, values, bias, valid, scale):
-    """Output [n, d] and log-normalizer [n] of one attention branch.
-
-    Scores scale * q.k, plus bias[j] when bias is given; entries where valid[i, j] is
-    False are excluded. A row without any valid entry gets log Z = -inf and a zero output:
-    the branch then carries no weight when combined (the pseudocode's finfo.min fill gives
-    the same combined result whenever the other branch has an entry).
-    """
-    Q = np.asarray(Q, np.float64)
-    keys = np.asarray(keys, np.float64)
-    n, d = Q.shape[0], np.asarray(values).shape[1]
-    out = np.zeros((n, d))
-    logz = np.full(n, -np.inf)
-    if keys.shape[0] == 0:
-        return out, logz
-    s = scale * (Q @ keys.T)
+def biased_scores(Q, keys, bias, valid, scale):
+    """Eq. 2 with the entry mask: l_ij = scale * q_i . k_j + bias_j where valid[i, j], and
+    -inf (excluded) elsewhere. bias None means an unbiased set of entries."""
+    l = scale * (np.asarray(Q, np.float64) @ np.asarray(keys, np.float64).T)
     if bias is not None:
-        s = s + np.asarray(bias, np.float64)[None, :]
-    s = np.where(np.broadcast_to(valid, s.shape), s, -np.inf)
-    m = s.max(axis=1)
-    fin = np.isfinite(m)
+        l = l + np.asarray(bias, np.float64)[None, :]
+    return np.where(np.broadcast_to(valid, l.shape), l, -np.inf)
+
+
+def log_normalizer(l):
+    """Eq. 4 in log form: log Z_i = log sum_j exp(l_ij) over the entries that are not
+    -inf; a row with none gets -inf (scipy's logsumexp, which returns -inf there)."""
+    return scipy.special.logsumexp(l, axis=1)
+
+
+def attention_output(l, logz, values):
+    """Eq. 3: A_i = sum_j exp(l_ij - log Z_i) v_j; a row with log Z = -inf is zero."""
+    out = np.zeros((l.shape[0], np.asarray(values).shape[1]))
+    fin = np.isfinite(logz)
     if fin.any():
-        e = np.exp(s[fin] - m[fin, None])
-        z = e.sum(axis=1)
-        logz[fin] = m[fin] + np.log(z)
-        out[fin] = (e / z[:, None]) @ np.asarray(values, np.float64)
-    return out, logz
+        out[fin] = np.exp(l[fin] - logz[fin, None]) @ np.asarray(values, np.float64)
+    return out
 
 
-def combine_attention(out1, logz1, out2, logz2):
-    """Eq. 5 in log space: log Z = logaddexp(log Z1, log Z2); out = the Z-weighted mixture.
-
-    Rows where both branches are empty keep log Z = -inf and a zero output.
-    """
+def merge_log_space(out1, logz1, out2, logz2):
+    """Eq. 5 for two disjoint entry sets, weighted in log space: log Z = log(Z1 + Z2) and
+    A = (Z1 A1 + Z2 A2) / (Z1 + Z2). A set whose log Z is -inf takes no weight; rows where
+    both are -inf keep -inf and a zero output."""
     logz = np.logaddexp(logz1, logz2)
     out = np.zeros_like(np.asarray(out1, np.float64))
     fin = np.isfinite(logz)
@@ -411,13 +406,17 @@ def cache_attention(Q, Ck, Cv, bias, scale, keypos=None, nvalid=None, causal=Fal
         valid &= (slots < nvalid)[None, :]
     if causal:
         valid &= visible(rows, np.asarray(keypos), True, group)
-    out1, lz1 = branch_attention(Q, Ck, Cv, bias, valid, scale)
+    l1 = biased_scores(Q, Ck, bias, valid, scale)           # document slots (Eq. 2)
+    lz1 = log_normalizer(l1)                                 # Eq. 4
+    out1 = attention_output(l1, lz1, Cv)                     # Eq. 3
     if Kn is None or np.asarray(Kn).shape[0] == 0:
         return out1, lz1.copy(), lz1
     m = np.asarray(Kn).shape[0]
     nvis = visible(rows, np.arange(m), bool(new_causal), group)
-    out2, lz2 = branch_attention(Q, Kn, Vn, None, nvis, scale)
-    out, lz = combine_attention(out1, lz1, out2, lz2)
+    l2 = biased_scores(Q, Kn, None, nvis, scale)            # appended entries, no bias
+    lz2 = log_normalizer(l2)
+    out2 = attention_output(l2, lz2, Vn)
+    out, lz = merge_log_space(out1, lz1, out2, lz2)          # Eq. 5
     return out, lz, lz1
 
 
@@ -628,13 +627,43 @@ def mass_residual(M, b, w) -> float:
 
 
 def output_residual(A, Y, Cv) -> float:
+    """||A C_v - Y||_F^2 / ||Y||_F^2."""
     R = A @ Cv - Y
     return float((R * R).sum() / (Y * Y).sum())
+
+
+def value_fit_stats(A, Y):
+    """(A^T Y, ||Y||_F^2): what the output residual of any C_v needs besides A itself, since
+    ||A C - Y||^2 = ||A C||^2 - 2 <C, A^T Y> + ||Y||^2. Lets a large problem's targets Y be
+    summarized once instead of kept."""
+    Y = np.asarray(Y, np.float64)
+    return np.asarray(A, np.float64).T @ Y, float((Y * Y).sum())
+
+
+def output_residual_from_stats(A, Cv, AtY, yy) -> float:
+    """The output residual ||A C_v - Y||_F^2 / ||Y||_F^2 from value_fit_stats(A, Y)."""
+    AC = np.asarray(A, np.float64) @ np.asarray(Cv, np.float64)
+    return float(((AC * AC).sum() - 2.0 * (np.asarray(Cv, np.float64) * AtY).sum() + yy) / yy)
 
 
 # --------------------------------------------------------------------------------------
 # the whole per-head pipeline
 # --------------------------------------------------------------------------------------
+def fit_selected(Q, K, lse, O, idx, scale, causal=False, group=1, mass="relative", w_lo=0.0,
+                 w_hi=np.inf, ridge_lambda=1e-3):
+    """S4..S7 on a given key set: the mass design and beta (NNLS on w), then the value
+    design and C_v (ridge), with both residuals. lse and O are the full-cache targets."""
+    Q = np.asarray(Q, np.float64)
+    idx = np.asarray(idx, np.int64)
+    Ck = np.asarray(K, np.float64)[idx]
+    M, b = mass_design(Q, Ck, idx, lse, scale, causal, group, mass)
+    w, beta = fit_beta(M, b, w_lo, w_hi)
+    A = value_design(M, w)
+    Cv = fit_values(A, O, ridge_lambda)
+    return dict(idx=idx, Ck=Ck, M=M, b=b, w=w, beta=beta, A=A, Cv=Cv,
+                r_mass=mass_residual(M, b, w), r_out=output_residual(A, O, Cv))
+
+
 def compact_head(Q, K, V, t, scale, causal=False, group=1, score="rms", mass="relative",
                  w_lo=0.0, w_hi=np.inf, ridge_lambda=1e-3, idx=None):
     """S1..S7 for one head. Returns a dict with every intermediate the parity tests use.
@@ -649,12 +678,6 @@ def compact_head(Q, K, V, t, scale, causal=False, group=1, score="rms", mass="re
     sc = key_score(stats, score, n)
     if idx is None:
         idx = select_top(sc, t)
-    idx = np.asarray(idx, np.int64)
-    Ck = K[idx]
-    M, b = mass_design(Q, Ck, idx, lse, scale, causal, group, mass)
-    w, beta = fit_beta(M, b, w_lo, w_hi)
-    A = value_design(M, w)
-    Cv = fit_values(A, O, ridge_lambda)
-    return dict(lse=lse, O=O, stats=stats, score=sc, idx=idx, Ck=Ck, M=M, b=b, w=w,
-                beta=beta, A=A, Cv=Cv,
-                r_mass=mass_residual(M, b, w), r_out=output_residual(A, O, Cv))
+    r = fit_selected(Q, K, lse, O, idx, scale, causal, group, mass, w_lo, w_hi, ridge_lambda)
+    r.update(lse=lse, O=O, stats=stats, score=sc)
+    return r

@@ -113,8 +113,8 @@ def test_attention_merge_matches_oracle_and_in_place():
     ref_out = np.zeros((h, n, d))
     ref_l = np.zeros((h, n))
     for i in range(h):
-        ref_out[i], ref_l[i] = O.combine_attention(O1[i].astype(np.float64), l1[i].astype(np.float64),
-                                                   O2[i].astype(np.float64), l2[i].astype(np.float64))
+        ref_out[i], ref_l[i] = O.merge_log_space(O1[i].astype(np.float64), l1[i].astype(np.float64),
+                                                  O2[i].astype(np.float64), l2[i].astype(np.float64))
     lse = lse.cpu().numpy()
     assert np.array_equal(np.isfinite(lse), np.isfinite(ref_l))
     fin = np.isfinite(ref_l)

@@ -401,7 +401,9 @@ def test_cache_attention_empty_branches():
     Q, Ck, Cv, bias, keypos, Kn, Vn = _cache_case(rng)
     # no new entries: the document branch alone
     out, lz, lz1 = O.cache_attention(Q, Ck, Cv, bias, 0.5)
-    d_out, d_lz = O.branch_attention(Q, Ck, Cv, bias, np.ones((Q.shape[0], Ck.shape[0]), bool), 0.5)
+    l = O.biased_scores(Q, Ck, bias, np.ones((Q.shape[0], Ck.shape[0]), bool), 0.5)
+    d_lz = O.log_normalizer(l)
+    d_out = O.attention_output(l, d_lz, Cv)
     np.testing.assert_array_equal(out, d_out)
     np.testing.assert_array_equal(lz, d_lz)
     # no valid slot: the new branch alone (unbiased causal attention over Kn)
@@ -430,13 +432,13 @@ def test_combine_weights_sum_to_one_and_commute():
     l1 = rng.standard_normal(9) * 5
     l2 = rng.standard_normal(9) * 5
     l2[3] = -np.inf
-    a, la = O.combine_attention(o1, l1, o2, l2)
-    b, lb = O.combine_attention(o2, l2, o1, l1)
+    a, la = O.merge_log_space(o1, l1, o2, l2)
+    b, lb = O.merge_log_space(o2, l2, o1, l1)
     np.testing.assert_allclose(a, b, atol=1e-13)
     np.testing.assert_array_equal(la, lb)
     np.testing.assert_allclose(a[3], o1[3], atol=1e-15)
     # equal normalizers: the plain average, and log Z grows by log 2
-    c, lc = O.combine_attention(o1, l1, o2, l1)
+    c, lc = O.merge_log_space(o1, l1, o2, l1)
     np.testing.assert_allclose(c, 0.5 * (o1 + o2), atol=1e-13)
     np.testing.assert_allclose(lc, l1 + np.log(2.0), atol=1e-13)
 
@@ -714,3 +716,82 @@ def test_stage1_fit_lowers_the_loss_and_freezes():
     assert after < 0.8 * before
     np.testing.assert_array_equal(Ck[frozen], K[kp][frozen])
     np.testing.assert_array_equal(b[frozen], 0.0)
+
+
+# --------------------------------------------------------------------------------------
+# hand-worked cases: teacher statistics, Eq. 8's averaging, the KKT checker
+# --------------------------------------------------------------------------------------
+def test_teacher_scales_hand_worked():
+    """Two query heads (group 2, rows alternate heads). Head 0's outputs are the channel
+    values {1, 3, 3, 5}: mean 3, population variance (4 + 0 + 0 + 4) / 4 = 2, std sqrt(2)
+    (ddof = 1 would give sqrt(8/3)); its log-normalizers {0, 4} have population std 2
+    (ddof = 1: 2 sqrt 2). Head 1 is constant in both, so both stds are 0 and the floor of
+    1e-4 applies to the standard deviation itself (a floor on the variance would give
+    1e-2). Pooling the heads would mix {1, 3, 3, 5} with {2, 2, 2, 2}."""
+    O_full = np.array([[1.0, 3.0], [2.0, 2.0], [3.0, 5.0], [2.0, 2.0]])
+    lse = np.array([0.0, 7.0, 4.0, 7.0])
+    sa, sz = O.teacher_scales(O_full, lse, 2)
+    np.testing.assert_allclose(sa, [np.sqrt(2.0), 1e-4], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(sz, [2.0, 1e-4], rtol=1e-15, atol=0)
+
+
+def test_stage1_loss_hand_worked():
+    """Eq. 8 on two rows, d = 2, one slot: with t = 1 the softmax is 1, so A = C_v for every
+    row and log Z = scale k . q + b. Rows q0 = (1, 0), q1 = (0, 1); slot key (2, 0), value
+    (1, 2), bias 0.5, scale 0.5: log Z = (1.5, 0.5). Targets O = ((0, 0), (1, 1)) and
+    lse = (0.5, 0.5), with sa = 2 and sz = 0.5 given.
+      output term: ((1/2)^2 + (2/2)^2 + 0^2 + (1/2)^2) / (N d = 4)  = 1.5 / 4  = 0.375
+      log Z term:  ((1/0.5)^2 + 0^2) / (N = 2)                        = 4 / 2    = 2
+      L = 2.375 (dividing the output term by N alone would give 2.75, summing the log Z
+      term instead of averaging 4.375).
+    Gradients: dL/db = (2 * 1 / 0.25 + 0) / 2 = 4; dL/dC_v = 2 / (sa^2 N d) * sum of the
+    output errors = (1/8) * (1, 3); dL/dC_k = (2 * 1 / (0.25 * 2)) * scale * q0 = (2, 0)."""
+    Q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    Ck = np.array([[2.0, 0.0]])
+    Cv = np.array([[1.0, 2.0]])
+    b = np.array([0.5])
+    O_full = np.array([[0.0, 0.0], [1.0, 1.0]])
+    lse = np.array([0.5, 0.5])
+    L, dCk, dCv, db = O.stage1_loss_grad(Q, np.arange(2), Ck, Cv, b, np.zeros(1, np.int64),
+                                         O_full, lse, np.array([2.0]), np.array([0.5]), 0.5)
+    assert L == pytest.approx(2.375, rel=1e-15)
+    np.testing.assert_allclose(db, [4.0], rtol=1e-15)
+    np.testing.assert_allclose(dCv, [[0.125, 0.375]], rtol=1e-15)
+    np.testing.assert_allclose(dCk, [[2.0, 0.0]], rtol=1e-15, atol=1e-15)
+
+
+def test_kkt_residual_flags_non_optimal_points():
+    """G = diag(2, 1), h = (2, 1): the optimum w = (1, 1) is interior. Hand-computed
+    violations of g = G w - h:
+      interior, w = (0.5, 1): g = (-1, 0), both free -> |g_0| = 1;
+      lower bound, w = (0, 1): g = (-2, 0), w_0 at 0 needs g_0 >= 0 -> 2;
+      lower bound met, h = (-2, 1), w = (0, 1): g = (2, 0) -> 0 (the optimum);
+      upper bound hi = 0.5, w = (0.5, 0.5): g = (-1, -0.5), both at hi need g <= 0 -> 0;
+      upper bound, h = (0.5, 0.2), w = (0.5, 0.5): g = (0.5, 0.3) at hi -> 0.5;
+      infeasible, w = (1.25, 1) with hi = 1.2: outside the box by 0.05."""
+    G = np.diag([2.0, 1.0])
+    h = np.array([2.0, 1.0])
+    assert O.nnls_kkt_residual(G, h, np.array([1.0, 1.0])) == 0.0
+    assert O.nnls_kkt_residual(G, h, np.array([0.5, 1.0])) == pytest.approx(1.0, rel=1e-15)
+    assert O.nnls_kkt_residual(G, h, np.array([0.0, 1.0])) == pytest.approx(2.0, rel=1e-15)
+    assert O.nnls_kkt_residual(G, np.array([-2.0, 1.0]), np.array([0.0, 1.0])) == 0.0
+    assert O.nnls_kkt_residual(G, h, np.array([0.5, 0.5]), 0.0, 0.5) == 0.0
+    assert O.nnls_kkt_residual(G, np.array([0.5, 0.2]), np.array([0.5, 0.5]), 0.0, 0.5) == \
+        pytest.approx(0.5, rel=1e-15)
+    assert O.nnls_kkt_residual(G, np.array([2.5, 1.0]), np.array([1.25, 1.0]), 0.0, 1.2) == \
+        pytest.approx(0.05, rel=1e-12)
+    # a positive lower bound: w_0 sits at lo = 0.25 with g_0 = 0.5 - 2 < 0 -> 1.5
+    assert O.nnls_kkt_residual(G, h, np.array([0.25, 1.0]), 0.25) == pytest.approx(1.5, rel=1e-15)
+
+
+def test_output_residual_from_stats_equals_direct():
+    """The expansion ||A C - Y||^2 = ||A C||^2 - 2 <C, A^T Y> + ||Y||^2 against the direct
+    residual, for the optimum and for an arbitrary C."""
+    rng = np.random.default_rng(71)
+    A = np.abs(rng.standard_normal((300, 12)))
+    A /= A.sum(axis=1, keepdims=True)
+    Y = rng.standard_normal((300, 5))
+    AtY, yy = O.value_fit_stats(A, Y)
+    for C in (O.fit_values(A, Y, 1e-3), rng.standard_normal((12, 5))):
+        assert O.output_residual_from_stats(A, C, AtY, yy) == \
+            pytest.approx(O.output_residual(A, Y, C), rel=1e-10)
