@@ -28,7 +28,7 @@
  *     passed the work. Calls on different streams with disjoint buffers are independent.
  *   - Arguments are validated on the host before any launch. A failed validation returns
  *     an error and launches nothing. Conditions found on the device (NNLS not converged,
- *     non-positive Cholesky pivot, non-finite values) are reported per head through the
+ *     a singular ridge system, non-finite values) are reported per head through the
  *     optional head_status array (AM_HEAD_* bits), never by a return code.
  *   - Results are deterministic: fixed reduction orders and no floating-point atomics.
  */
@@ -70,7 +70,10 @@ typedef enum { AM_MASS_RELATIVE = 0, AM_MASS_ABSOLUTE = 1 } am_mass_mode;
 enum {
   AM_HEAD_OK = 0,
   AM_HEAD_NNLS_NOT_CONVERGED = 1, /* KKT tolerance not reached within nnls_max_iter */
-  AM_HEAD_CHOL_PIVOT = 2,         /* non-positive pivot in the ridge Cholesky */
+  AM_HEAD_CHOL_PIVOT = 2,         /* a ridge Cholesky pivot not above 2^-40 times its
+                                     diagonal entry: A^T A + lambda I is singular at the
+                                     precision of the solve (lambda = 0 with dependent
+                                     columns of A); C_v is then not meaningful */
   AM_HEAD_NONFINITE = 4,          /* a non-finite value reached a fit */
   AM_HEAD_TIMEOUT = 8             /* workgroups of a multi-workgroup step did not meet in
                                      time (the head's outputs are then incomplete) */
@@ -138,15 +141,44 @@ am_status am_select_keys(const am_problem* p, const float* key_score, int64_t t,
  * am_fit_beta_nnls - beta from the mass equations by non-negative least squares on
  * w = exp(beta) (blog, §Choosing beta). With M the mass design of the selected keys
  * (see am_mass_mode), w = argmin_{w_lo <= w <= w_hi} ||M w - b||^2, solved on the device
- * from the Gram form G = M^T M, M^T b by accelerated projected gradient. beta = log w
+ * from the Gram form G = M^T M, h = M^T b by accelerated projected gradient. beta = log w
  * (w = 0 gives -inf). lse[h, n] is the natural-log normalizer from am_targets. idx must
  * be ascending (as am_select_keys returns it); it gives the compacted keys' positions.
- * Optional outputs: w[h, t]; mass_resid[h] = ||M w - b||^2 / n; head_status[h].
+ * Optional outputs (NULL skips each):
+ *   w[h, t];
+ *   mass_resid[h] = ||M w - b||^2 / n;
+ *   kkt_resid[h]  = max_j viol_j / max_j |h_j|, the optimality-condition residual of the
+ *                   returned w on the Gram system the library formed (fp32): with
+ *                   g = G w - h, viol_j = |g_j| where w_lo < w_j < w_hi, max(-g_j, 0) where
+ *                   w_j = w_lo and max(g_j, 0) where w_j = w_hi;
+ *   iters[h]      = projected-gradient steps taken (the solve stops when its scaled
+ *                   gradient-mapping norm is below nnls_tol, or after nnls_max_iter steps);
+ *   head_status[h].
+ * For t > 256 the solve runs on several workgroups per head that wait on each other; it
+ * needs them all resident at once and returns AM_ERR_DEVICE if the device cannot hold them
+ * (am_fit_beta_plan reports the schedule). A head whose workgroups still fail to meet
+ * within about a second gets AM_HEAD_TIMEOUT.
  */
 am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,
                            const int32_t* idx, const float* lse, int64_t t,
                            const am_options* opt, float* beta, float* w, float* mass_resid,
-                           int32_t* head_status, void* ws, size_t ws_bytes, am_stream_t stream);
+                           float* kkt_resid, int32_t* iters, int32_t* head_status, void* ws,
+                           size_t ws_bytes, am_stream_t stream);
+
+/* How am_fit_beta_nnls (and am_compact_head) schedule the NNLS of a problem on the current
+ * device. */
+typedef struct {
+  int32_t workgroups_per_head;    /* 1: one workgroup holds a head's whole system (t <= 256) */
+  int32_t launches;               /* heads are solved in this many batches */
+  int32_t heads_per_launch;       /* heads in each batch but possibly the last */
+  int32_t rows_per_workgroup;     /* rows of G each workgroup of a full batch owns */
+  int32_t lds_rows_per_workgroup; /* of those, the rows held in LDS for the whole solve; the
+                                     others are read from memory at every step */
+} am_nnls_plan;
+
+/* Fills *out for problem p and budget t (host only; AM_ERR_DEVICE if the device cannot be
+ * queried). */
+am_status am_fit_beta_plan(const am_problem* p, int64_t t, am_nnls_plan* out);
 
 /*
  * am_fit_values_ols - C_v from the output equations (blog, §Choosing C_v) by ridge least

@@ -24,7 +24,7 @@ MASS_MODES = {"relative": 0, "absolute": 1}
  CALL_BETA_REDIST, CALL_EVAL, CALL_INIT) = range(9)
 BETA_MODES = {"nnls": 0, "redistribute": 1}
 VALUE_MODES = {"fit": 0, "direct": 1}
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_NNLS_NOT_CONVERGED, HEAD_CHOL_PIVOT, HEAD_NONFINITE, HEAD_TIMEOUT = 1, 2, 4, 8
 
 
@@ -39,6 +39,12 @@ class AmOptions(ctypes.Structure):
                 ("w_hi", ctypes.c_float), ("nnls_max_iter", ctypes.c_int32),
                 ("nnls_tol", ctypes.c_float), ("ridge_lambda", ctypes.c_float),
                 ("beta", ctypes.c_int), ("values", ctypes.c_int)]
+
+
+class AmNnlsPlan(ctypes.Structure):
+    _fields_ = [("workgroups_per_head", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("heads_per_launch", ctypes.c_int32), ("rows_per_workgroup", ctypes.c_int32),
+                ("lds_rows_per_workgroup", ctypes.c_int32)]
 
 
 class AmError(RuntimeError):
@@ -59,8 +65,10 @@ _PROTOS = {
     "am_select_keys": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, ctypes.c_int64, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]),
     "am_fit_beta_nnls": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, ctypes.c_int64,
-                                        ctypes.POINTER(AmOptions), _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(AmOptions), _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
+    "am_fit_beta_plan": (ctypes.c_int, [ctypes.POINTER(AmProblem), ctypes.c_int64,
+                                        ctypes.POINTER(AmNnlsPlan)]),
     "am_fit_values_ols": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P,
                                          ctypes.c_int64, ctypes.c_float, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
@@ -235,8 +243,9 @@ def select_keys(key_score, K, t, V=None, *, want_vsel=False):
 
 
 def fit_beta_nnls(Q, Ck, idx, lse, *, causal=False, group=1, scale=None, options=None,
-                  T=None):
-    """beta [h, t], w [h, t], mass residual [h], head status [h]."""
+                  T=None, diagnostics=False):
+    """beta [h, t], w [h, t], mass residual [h], head status [h]; with diagnostics=True also
+    the relative KKT residual [h] (f32) and the projected-gradient step count [h] (int32)."""
     torch = _torch()
     _need(Q, "Q"); _need(Ck, "Ck", dtype=Q.dtype)
     h, n, d = Q.shape
@@ -252,11 +261,26 @@ def fit_beta_nnls(Q, Ck, idx, lse, *, causal=False, group=1, scale=None, options
     w = torch.empty((h, t), dtype=torch.float32, device=dev)
     res = torch.empty((h,), dtype=torch.float32, device=dev)
     st = torch.empty((h,), dtype=torch.int32, device=dev)
+    kkt = torch.empty((h,), dtype=torch.float32, device=dev) if diagnostics else None
+    its = torch.empty((h,), dtype=torch.int32, device=dev) if diagnostics else None
     ws, nb = _workspace(p, t, CALL_FIT_BETA, dev)
     _check(lib().am_fit_beta_nnls(ctypes.byref(p), _ptr(Q), _ptr(Ck), _ptr(idx), _ptr(lse), t,
-                                  ctypes.byref(o), _ptr(beta), _ptr(w), _ptr(res), _ptr(st),
-                                  _ptr(ws), nb, _stream()), "am_fit_beta_nnls")
+                                  ctypes.byref(o), _ptr(beta), _ptr(w), _ptr(res), _ptr(kkt),
+                                  _ptr(its), _ptr(st), _ptr(ws), nb, _stream()),
+           "am_fit_beta_nnls")
+    if diagnostics:
+        return beta, w, res, st, kkt, its
     return beta, w, res, st
+
+
+def fit_beta_plan(heads, n, T, d, t, *, causal=False, group=1, dtype="bf16"):
+    """How the NNLS of such a problem is scheduled on the current device (a dict of
+    am_nnls_plan's fields)."""
+    p = AmProblem(heads, n, T, d, int(bool(causal)), int(group), float(1.0 / math.sqrt(d)),
+                  AM_BF16 if dtype == "bf16" else AM_F32)
+    out = AmNnlsPlan()
+    _check(lib().am_fit_beta_plan(ctypes.byref(p), t, ctypes.byref(out)), "am_fit_beta_plan")
+    return {f: getattr(out, f) for f, _ in AmNnlsPlan._fields_}
 
 
 def fit_values_ols(Q, Ck, idx, beta, O, *, causal=False, group=1, scale=None, ridge_lambda=1e-3,

@@ -11,7 +11,7 @@ using namespace amc;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -228,8 +228,8 @@ am_status am_select_keys(const am_problem* p, const float* key_score, int64_t t,
 am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,
                            const int32_t* idx, const float* lse, int64_t t,
                            const am_options* opt, float* beta, float* w, float* mass_resid,
-                           int32_t* head_status, void* ws, size_t ws_bytes,
-                           am_stream_t stream) {
+                           float* kkt_resid, int32_t* iters, int32_t* head_status, void* ws,
+                           size_t ws_bytes, am_stream_t stream) {
   am_status st = check_problem(p);
   if (st != AM_OK) return st;
   if ((st = check_t(p, t)) != AM_OK) return st;
@@ -237,15 +237,33 @@ am_status am_fit_beta_nnls(const am_problem* p, const void* Q, const void* Ck,
   if ((st = check_fit_t(t)) != AM_OK) return st;
   if (!Q || !Ck || !idx || !lse || !beta) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(Ck) || !al16(idx) || !al16(lse) || !al16(beta) || (w && !al16(w)) ||
-      (mass_resid && !al16(mass_resid)) || (head_status && !al16(head_status)) ||
-      (ws && !al16(ws)))
+      (mass_resid && !al16(mass_resid)) || (kkt_resid && !al16(kkt_resid)) ||
+      (iters && !al16(iters)) || (head_status && !al16(head_status)) || (ws && !al16(ws)))
     return AM_ERR_INVALID_ARG;
   if (!ws || ws_bytes < ws_fit_beta(p, t)) return AM_ERR_WORKSPACE;
   FitArgs a = fit_args(p, Q, Ck, idx, t, ws, ws_bytes, (hipStream_t)stream);
   a.lse = lse; a.beta = beta; a.w = w; a.mass_resid = mass_resid; a.head_status = head_status;
+  a.kkt = kkt_resid; a.iters = iters;
   a.absolute = opt->mass == AM_MASS_ABSOLUTE;
   a.w_lo = opt->w_lo; a.w_hi = opt->w_hi; a.tol = opt->nnls_tol; a.max_iter = opt->nnls_max_iter;
   return from_hip(launch_fit_beta(a));
+}
+
+am_status am_fit_beta_plan(const am_problem* p, int64_t t, am_nnls_plan* out) {
+  am_status st = check_problem(p);
+  if (st != AM_OK) return st;
+  if ((st = check_t(p, t)) != AM_OK) return st;
+  if ((st = check_fit_t(t)) != AM_OK) return st;
+  if (!out) return AM_ERR_INVALID_ARG;
+  const int ncu = device_cu_count();
+  if (ncu < 1) return AM_ERR_DEVICE;
+  const NnlsSchedule sc = nnls_schedule((int)p->heads, (int)t, ncu);
+  out->workgroups_per_head = sc.first.P;
+  out->launches = sc.launches;
+  out->heads_per_launch = sc.heads_per_launch;
+  out->rows_per_workgroup = sc.first.rb;
+  out->lds_rows_per_workgroup = sc.first.nlds;
+  return AM_OK;
 }
 
 am_status am_fit_values_ols(const am_problem* p, const void* Q, const void* Ck,

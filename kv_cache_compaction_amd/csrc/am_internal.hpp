@@ -161,6 +161,8 @@ struct FitArgs {
   const float* beta_in;  // value fit: beta of the selected keys
   const float* O;        // value fit: targets Y [h, n, d]
   float* beta; float* w; float* mass_resid; float* Cv; float* out_resid;
+  float* kkt;            // beta fit: relative KKT residual per head (optional)
+  int32_t* iters;        // beta fit: projected-gradient steps per head (optional)
   int32_t* head_status;
   int heads, n, t, d, group;
   bool causal, bf16, absolute;
@@ -215,6 +217,17 @@ size_t fast_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d, int esize, 
 hipError_t launch_zero_status(int32_t* status, int heads, hipStream_t st);
 
 hipError_t launch_fit_beta(const FitArgs& a);
+// How the NNLS of a beta fit is scheduled: one workgroup per head (t <= 256; P = 1), or P
+// workgroups per head that meet at per-head barriers, heads_per_launch heads per launch.
+struct NnlsParts { int P, rb, nlds; size_t shmem; };   // rb rows per workgroup, nlds in LDS
+struct NnlsSchedule { int heads_per_launch, launches; NnlsParts first; };
+NnlsParts nnls_parts(int hb, int t, int ncu);
+NnlsSchedule nnls_schedule(int heads, int t, int ncu);
+int device_cu_count();   // of the current device (0 if the query fails)
+// An ordinary launch of a kernel whose workgroups wait on each other: refused with
+// hipErrorCooperativeLaunchTooLarge unless the whole grid can be resident at once.
+hipError_t launch_all_resident(const void* fn, dim3 grid, dim3 block, void** args, size_t shmem,
+                               hipStream_t st);
 hipError_t launch_fit_values(const FitArgs& a);
 size_t fit_beta_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d);
 size_t fit_values_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d);

@@ -3,7 +3,8 @@
 // of highest maximum attention; diversifiers are added by farthest-first traversal, each
 // step taking the key farthest (squared Euclidean distance) from every key chosen so far.
 //
-// The traversal runs on P co-resident workgroups per head (cooperative launch): each owns
+// The traversal runs on P workgroups per head, all resident at once (an ordinary launch
+// that is refused unless the whole grid fits on the device at the same time): each owns
 // a contiguous range of keys and keeps their distances to the chosen set in LDS. A step
 // streams the range once (a group of lanes per key row, 16 bytes per lane, so a wave reads
 // contiguous rows), lowers the distances by the new key's, and finds the range's best
@@ -432,11 +433,7 @@ InitPlan plan_init(char* base, int64_t h, int64_t n, int64_t T, int64_t d, int e
   return q;
 }
 int fft_parts(int heads, int T) {
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    ncu = 0;
-  int P = ncu / heads;
+  int P = device_cu_count() / heads;
   P = min(P, (T + 255) / 256);   // at least 256 keys per workgroup
   return max(1, min(P, 256));
 }
@@ -452,7 +449,7 @@ hipError_t launch_fft(FftParams fp, size_t shmem, hipStream_t st) {
   (void)hipFuncSetAttribute((const void*)fft_kernel<Tt, D>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
   void* args[] = {&fp};
-  return hipLaunchCooperativeKernel((const void*)fft_kernel<Tt, D>, g, b, args, (unsigned)shmem, st);
+  return launch_all_resident((const void*)fft_kernel<Tt, D>, g, b, args, shmem, st);
 }
 template <int D>
 hipError_t launch_fft_reg(FftParams fp, hipStream_t st) {
@@ -462,7 +459,7 @@ hipError_t launch_fft_reg(FftParams fp, hipStream_t st) {
     return hipGetLastError();
   }
   void* args[] = {&fp};
-  return hipLaunchCooperativeKernel((const void*)fft_reg_kernel<D>, g, b, args, 0u, st);
+  return launch_all_resident((const void*)fft_reg_kernel<D>, g, b, args, 0, st);
 }
 }  // namespace
 

@@ -19,11 +19,11 @@
 // NNLS. Accelerated projected gradient with Jacobi scaling (v = sqrt(diag G) * w),
 // step 1/L with L from power iteration, momentum restarted when the step turns back
 // (gradient-mapping test), stopped on the scaled gradient-mapping norm. t <= 256: one
-// workgroup per head with G in LDS. Larger t: P co-resident workgroups per head
-// (cooperative launch), each owning a slice of rows (of G too when they fit in LDS), meeting
-// at a per-head barrier once per step; all reduce the same partials in the same fixed order.
-// If the cooperative launch is refused: one launch per step, each workgroup owning 16 rows
-// and redundantly reducing the previous launch's per-block partials.
+// workgroup per head. Larger t: P workgroups per head, all resident at once (the launch
+// is refused otherwise), each owning a slice of rows (of G too when they fit in LDS),
+// meeting at a per-head barrier once per step; all reduce the same partials in the same
+// fixed order. Heads are batched so that each gets at least four workgroups. Each solve
+// also reports its step count and the KKT residual of the w it returns.
 //
 // Ridge solve. (G_A + lambda I) C = A^T Y in fp64: right-looking blocked Cholesky with
 // 64 x 64 blocks (diagonal factor and its explicit inverse in one workgroup, panel as a
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) void shift_kernel(const float* __restrict__ ls
 }
 
 // ------------------------------------------------------------------------------------
-// NNLS by accelerated projected gradient (one launch per iteration)
+// NNLS by accelerated projected gradient
 // ------------------------------------------------------------------------------------
 struct NnlsState {
   const float* G;   // [h, t, t]
@@ -468,14 +468,17 @@ struct NnlsState {
   float* X;         // [h, 2, t] power-iteration vectors
   float* PN;        // [h, 2, nblk] power-iteration partial squared norms
   float2* P;        // [h, 2, nblk] (restart dot, gradient-mapping max) partials
-  float* TK;        // [h, 2] momentum scalars
-  float* hsmax;     // [h]
-  int* iters;       // [h]
-  int* fin;         // [h] ring slot of the converged iterate, -1 while running
-  float2* init;     // [h, nblk] (max |hs|, non-finite flag) partials (multi-workgroup solver)
-  int* bar;         // [h] barrier counters of the multi-workgroup solver (zero before a launch)
+  float2* init;     // [h, nblk] (max |hs|, non-finite flag) partials
+  float2* kktp;     // [h, nblk] (largest KKT violation, largest |h|) partials, zero-filled
+  int* bar;         // [h] barrier counters (zero before the first launch)
   int t, nblk;
   float lo, hi, tol;
+};
+
+// Outputs of a solve: w (optional), beta, status (optional), the relative KKT residual
+// (optional) and the number of projected-gradient steps taken (optional), all per head.
+struct NnlsOut {
+  float* w; float* beta; int32_t* status; float* kkt; int32_t* iters;
 };
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -501,191 +504,25 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return s;
 }
 
-__global__ __launch_bounds__(256) void nnls_prep_kernel(NnlsState s, int32_t* status) {
-  __shared__ float red[4];
-  const int head = blockIdx.x, t = s.t;
-  const float* G = s.G + (size_t)head * t * t;
-  bool bad = false;
-  float hm = 0.f;
-  for (int j = threadIdx.x; j < t; j += 256) {
-    const float g = G[(size_t)j * t + j];
-    const float h = s.hv[(size_t)head * t + j];
-    bad |= !isfinite(g) || !isfinite(h);
-    const float di = g > 0.f ? rsqrtf(g) : 0.f;
-    s.dinv[(size_t)head * t + j] = di;
-    const float hsj = h * di;
-    s.hs[(size_t)head * t + j] = hsj;
-    hm = fmaxf(hm, fabsf(hsj));
-    const float v0 = di > 0.f ? s.lo / di : 0.f;
-    s.V[((size_t)head * 3 + 0) * t + j] = v0;
-    s.V[((size_t)head * 3 + 2) * t + j] = v0;
-    s.X[((size_t)head * 2 + 0) * t + j] = 1.f;
-  }
-  hm = block_max(hm, red);
-  const float nb = block_max(bad ? 1.f : 0.f, red);
-  for (int b = threadIdx.x; b < s.nblk; b += 256) {
-    s.PN[((size_t)head * 2 + 0) * s.nblk + b] = b == 0 ? (float)t : 0.f;
-    s.P[((size_t)head * 2 + 0) * s.nblk + b] = make_float2(0.f, INFINITY);
-  }
-  if (threadIdx.x == 0) {
-    s.hsmax[head] = hm;
-    s.TK[head * 2 + 0] = 1.f;
-    s.iters[head] = 0;
-    s.fin[head] = -1;
-    if (status) status[head] = nb > 0.f ? AM_HEAD_NONFINITE_BIT : 0;
-  }
+// Violation of the optimality conditions of min 1/2 w^T G w - h^T w over lo <= w <= hi at
+// one coordinate, with g = (G w - h)_j: a free coordinate needs g = 0, one at the lower
+// bound g >= 0, one at the upper bound g <= 0.
+__device__ __forceinline__ float kkt_violation(float g, float w, float lo, float hi) {
+  if (w <= lo) return fmaxf(-g, 0.f);
+  if (w >= hi) return fmaxf(g, 0.f);
+  return fabsf(g);
 }
 
-// rows of this block: y_i = (D^-1 G D^-1 x)_i  with x read from X[k % 2] normalised
-__global__ __launch_bounds__(256) void nnls_power_kernel(NnlsState s, int k) {
-  __shared__ float xs[kMaxFitT];
-  __shared__ float red[4];
-  const int head = blockIdx.y, blk = blockIdx.x, t = s.t;
-  const float* xin = s.X + ((size_t)head * 2 + (k & 1)) * t;
-  float* xout = s.X + ((size_t)head * 2 + ((k + 1) & 1)) * t;
-  const float* pn = s.PN + ((size_t)head * 2 + (k & 1)) * s.nblk;
-  float nrm = 0.f;
-  for (int b = 0; b < s.nblk; ++b) nrm += pn[b];
-  const float sc = nrm > 0.f ? rsqrtf(nrm) : 0.f;
-  const float* di = s.dinv + (size_t)head * t;
-  for (int j = threadIdx.x; j < t; j += 256) xs[j] = xin[j] * sc * di[j];
-  __syncthreads();
-  const float* G = s.G + (size_t)head * t * t;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float part = 0.f;
-  for (int rr = wave; rr < kRB; rr += 4) {
-    const int i = blk * kRB + rr;
-    if (i >= t) break;
-    float acc = 0.f;
-    for (int j = lane; j < t; j += 64) acc += G[(size_t)i * t + j] * xs[j];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    const float y = acc * di[i];
-    if (lane == 0) xout[i] = y;
-    part += (lane == 0) ? y * y : 0.f;
-  }
-  part = block_sum(part, red);
-  if (threadIdx.x == 0) s.PN[((size_t)head * 2 + ((k + 1) & 1)) * s.nblk + blk] = part;
-}
-
-__device__ __forceinline__ float nnls_L(const NnlsState& s, int head) {
-  // ||D^-1 G D^-1 x|| for the last normalised power vector, with a safety margin
-  const float* pn = s.PN + ((size_t)head * 2 + (kPow & 1)) * s.nblk;
-  float nrm = 0.f;
-  for (int b = 0; b < s.nblk; ++b) nrm += pn[b];
-  return 1.1f * sqrtf(nrm) + 1e-30f;
-}
-
-__global__ __launch_bounds__(256) void nnls_step_kernel(NnlsState s, int k) {
-  __shared__ float ys[kMaxFitT];
-  __shared__ float red[4];
-  const int head = blockIdx.y, blk = blockIdx.x, t = s.t;
-  if (s.fin[head] >= 0) return;   // converged in an earlier launch: nothing left to do
-  const float L = nnls_L(s, head);
-  const float2* P = s.P + ((size_t)head * 2 + (k & 1)) * s.nblk;
-  float dot = 0.f, gm = 0.f;
-  for (int b = 0; b < s.nblk; ++b) {
-    const float2 v = P[b];
-    dot += v.x;
-    gm = fmaxf(gm, v.y);
-  }
-  const float thr = s.tol * fmaxf(s.hsmax[head], 1e-30f);
-  const bool done = k > 0 && gm <= thr;
-  const float tk = s.TK[head * 2 + (k & 1)];
-  const bool restart = dot > 0.f;
-  const float tn = restart ? 1.f : 0.5f * (1.f + sqrtf(1.f + 4.f * tk * tk));
-  const float mom = restart ? 0.f : (tk - 1.f) / tn;
-  const float* vprev = s.V + ((size_t)head * 3 + (k + 2) % 3) * t;
-  const float* vcur = s.V + ((size_t)head * 3 + k % 3) * t;
-  float* vnext = s.V + ((size_t)head * 3 + (k + 1) % 3) * t;
-  const float* di = s.dinv + (size_t)head * t;
-  for (int j = threadIdx.x; j < t; j += 256) {
-    const float y = vcur[j] + mom * (vcur[j] - vprev[j]);
-    ys[j] = y;
-  }
-  __syncthreads();
-  const float* G = s.G + (size_t)head * t * t;
-  const float* hs = s.hs + (size_t)head * t;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float pdot = 0.f, pgm = 0.f;
-  for (int rr = wave; rr < kRB; rr += 4) {
-    const int i = blk * kRB + rr;
-    if (i >= t) break;
-    float vn;
-    if (done) {
-      vn = vcur[i];
-    } else {
-      float acc = 0.f;
-      for (int j = lane; j < t; j += 64) acc += G[(size_t)i * t + j] * (ys[j] * di[j]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      const float g = acc * di[i] - hs[i];
-      const float y = ys[i];
-      if (di[i] > 0.f) {
-        const float lo = s.lo / di[i];
-        const float hi = isinf(s.hi) ? INFINITY : s.hi / di[i];
-        vn = fminf(fmaxf(y - g / L, lo), hi);
-      } else {
-        vn = 0.f;
-      }
-      if (lane == 0) {
-        pdot += (vn - vcur[i]) * (y - vn);
-        pgm = fmaxf(pgm, fabsf(y - vn) * L);
-      }
-    }
-    if (lane == 0) vnext[i] = vn;
-  }
-  pdot = block_sum(pdot, red);
-  pgm = block_max(pgm, red);
-  if (threadIdx.x == 0) {
-    s.P[((size_t)head * 2 + ((k + 1) & 1)) * s.nblk + blk] =
-        done ? make_float2(0.f, gm) : make_float2(pdot, pgm);
-    if (blk == 0) {
-      s.TK[head * 2 + ((k + 1) & 1)] = tn;
-      if (!done) s.iters[head] = k + 1;
-      else s.fin[head] = k % 3;   // later launches exit at once
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void nnls_finish_kernel(NnlsState s, int K, float* w_out,
-                                                          float* beta, int32_t* status) {
-  __shared__ float red[4];
-  const int head = blockIdx.x, t = s.t;
-  const int fin = s.fin[head];
-  const float* v = s.V + ((size_t)head * 3 + (fin >= 0 ? fin : K % 3)) * t;
-  // converged heads were stopped on the tolerance; otherwise check the last partials
-  float gm = 0.f;
-  if (fin < 0) {
-    const float2* P = s.P + ((size_t)head * 2 + (K & 1)) * s.nblk;
-    for (int b = 0; b < s.nblk; ++b) gm = fmaxf(gm, P[b].y);
-  }
-  const float thr = s.tol * fmaxf(s.hsmax[head], 1e-30f);
-  bool bad = false;
-  for (int j = threadIdx.x; j < t; j += 256) {
-    const float di = s.dinv[(size_t)head * t + j];
-    float w = di > 0.f ? v[j] * di : s.lo;
-    w = fminf(fmaxf(w, s.lo), s.hi);
-    bad |= !isfinite(w);
-    if (w_out) w_out[(size_t)head * t + j] = w;
-    beta[(size_t)head * t + j] = w > 0.f ? logf(w) : -INFINITY;
-  }
-  const float nb = block_max(bad ? 1.f : 0.f, red);
-  if (threadIdx.x == 0 && status)
-    status[head] |= (gm > thr ? AM_HEAD_NNLS_BIT : 0) | (nb > 0.f ? AM_HEAD_NONFINITE_BIT : 0);
-}
-
-// Persistent solver for t <= kNnlsSingle: one workgroup per head runs the same iteration
-// (Jacobi scaling, step 1/L from power iteration, restarted momentum, stop on the scaled
-// gradient-mapping norm) with all vectors in LDS. Thread i owns row i; by symmetry it
-// forms (G z)_i as sum_j G[j][i] z_j, so every step of j reads one row of G coalesced.
-// G itself is staged in LDS when it fits (t <= 128), otherwise read from L2.
-constexpr int kNnlsSingle = 1024;
+// One workgroup per head for t <= kNnlsSingle (thread i owns row i): Jacobi scaling
+// v = sqrt(diag G) w, step 1/L with L from power iteration, momentum restarted when the
+// step turns back, stop on the scaled gradient-mapping norm; all vectors in LDS. By
+// symmetry thread i forms (G z)_i as sum_j G[j][i] z_j, so every step of j reads one row of
+// G coalesced; G itself is staged in LDS when it fits (t <= 128), otherwise read from L2.
+constexpr int kNnlsSingle = 256;
 constexpr int kNnlsLdsG = 128;
 
 __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, int max_iter,
-                                                                  float* w_out, float* beta,
-                                                                  int32_t* status) {
+                                                                  NnlsOut o) {
   __shared__ float zs[kNnlsSingle];
   __shared__ float Gl[kNnlsLdsG * kNnlsLdsG];
   __shared__ float red[kNnlsSingle / 64], red2[kNnlsSingle / 64];
@@ -700,7 +537,7 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
 
   auto bsum = [&](float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    for (int o2 = 32; o2 > 0; o2 >>= 1) v += __shfl_xor(v, o2, 64);
     __syncthreads();
     if ((i & 63) == 0) red[i >> 6] = v;
     __syncthreads();
@@ -710,7 +547,7 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
   };
   auto bmax2 = [&](float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    for (int o2 = 32; o2 > 0; o2 >>= 1) v = fmaxf(v, __shfl_xor(v, o2, 64));
     __syncthreads();
     if ((i & 63) == 0) red2[i >> 6] = v;
     __syncthreads();
@@ -718,22 +555,23 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
     for (int w = 1; w < kNnlsSingle / 64; ++w) r = fmaxf(r, red2[w]);
     return r;
   };
-  // (D^-1 G D^-1 x)_i with zs = D^-1 x already in LDS
-  auto row = [&](float di) {
+  // sum_j G[j][i] zs[j] times f (zs = D^-1 x: the scaled product (D^-1 G D^-1 x)_i with
+  // f = d_i; zs = w: (G w)_i with f = 1)
+  auto row = [&](float f) {
     float acc = 0.f;
     if (own)
       for (int j = 0; j < t; ++j) acc += Gs[(size_t)j * t + i] * zs[j];
-    return acc * di;
+    return acc * f;
   };
 
-  float di = 0.f, hsi = 0.f, gii = 0.f, hi_ = 0.f;
+  float di = 0.f, hsi = 0.f, gii = 0.f, h_i = 0.f;
   if (own) {
     gii = Gs[(size_t)i * t + i];
-    hi_ = s.hv[(size_t)head * t + i];
+    h_i = s.hv[(size_t)head * t + i];
     di = gii > 0.f ? rsqrtf(gii) : 0.f;
-    hsi = hi_ * di;
+    hsi = h_i * di;
   }
-  const float bad = bmax2((own && (!isfinite(gii) || !isfinite(hi_))) ? 1.f : 0.f);
+  const float bad = bmax2((own && (!isfinite(gii) || !isfinite(h_i))) ? 1.f : 0.f);
   const float hsmax = bmax2(fabsf(hsi));
   const float lo_i = di > 0.f ? s.lo / di : 0.f;
   const float hi_i = di > 0.f ? (isinf(s.hi) ? INFINITY : s.hi / di) : 0.f;
@@ -772,31 +610,42 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
     tk = tn;
   }
   bool badw = false;
+  float wi = 0.f;
   if (own) {
     float w = di > 0.f ? v * di : s.lo;
-    w = fminf(fmaxf(w, s.lo), s.hi);
-    badw = !isfinite(w);
-    if (w_out) w_out[(size_t)head * t + i] = w;
-    beta[(size_t)head * t + i] = w > 0.f ? logf(w) : -INFINITY;
+    wi = fminf(fmaxf(w, s.lo), s.hi);
+    badw = !isfinite(wi);
+    if (o.w) o.w[(size_t)head * t + i] = wi;
+    o.beta[(size_t)head * t + i] = wi > 0.f ? logf(wi) : -INFINITY;
   }
   const float nbw = bmax2(badw ? 1.f : 0.f);
+  if (o.kkt) {   // the KKT residual of the returned w on the system solved
+    __syncthreads();
+    zs[i] = wi;
+    __syncthreads();
+    const float viol = own ? kkt_violation(row(1.f) - h_i, wi, s.lo, s.hi) : 0.f;
+    const float vmx = bmax2(viol);
+    const float hmx = bmax2(fabsf(h_i));
+    if (i == 0) o.kkt[head] = vmx / fmaxf(hmx, 1e-30f);
+  }
   if (i == 0) {
-    s.iters[head] = it;
-    if (status)
-      status[head] = (gm > thr ? AM_HEAD_NNLS_BIT : 0) |
-                     ((bad > 0.f || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0);
+    if (o.iters) o.iters[head] = it;
+    if (o.status)
+      o.status[head] = (gm > thr ? AM_HEAD_NNLS_BIT : 0) |
+                       ((bad > 0.f || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0);
   }
 }
 
-// Multi-workgroup solver for t > kNnlsCoopMinT: the same iteration, with the rows of each
-// head split over P workgroups and a barrier among those P between steps. The grid is
-// launched cooperatively, which guarantees that every workgroup is resident (the barrier
-// waits on the others). A workgroup keeps its rows of G in LDS when they fit, else reads
-// them from L2; the iterate vectors go through global memory. All workgroups of a head
-// reduce the head's per-workgroup partials in the same fixed order, so they take the same
-// decisions (momentum, convergence, exit) and pass the same number of barriers; heads are
-// independent and stop on their own.
-constexpr int kNnlsCoopMinT = 256;            // smaller systems: one workgroup per head
+// Multi-workgroup solver for t > kNnlsSingle: the same iteration, with the rows of each
+// head split over P workgroups and a barrier among those P between steps. The launch
+// checks that every workgroup of the grid can be resident at once (one per CU here), since
+// the barrier waits on the others. A workgroup keeps its rows of G in LDS when they fit,
+// else reads them from L2; the iterate vectors go through global memory. All workgroups
+// of a head reduce the head's per-workgroup partials in the same fixed order, so they take
+// the same decisions (momentum, convergence, exit) and pass the same number of barriers;
+// heads are independent and stop on their own. Heads are solved in batches of at most
+// ncu / 4 per launch (so every head gets at least four workgroups); a launch takes heads
+// h0 .. h0 + Hb - 1.
 constexpr size_t kNnlsCoopLds = 144 * 1024;   // dynamic LDS for G rows + the vector
 constexpr int kNnlsSpin = 1 << 22;            // polls before a barrier wait gives up
 
@@ -841,14 +690,13 @@ __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_ou
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int max_iter, int nlds,
-                                                        float* w_out, float* beta,
-                                                        int32_t* status) {
+__global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int Hb, int P,
+                                                        int max_iter, int nlds, NnlsOut o) {
   extern __shared__ float smem[];
   __shared__ float red[4];
   __shared__ float2 pst[256];   // staged partials of the head's workgroups (P <= 256)
   __shared__ int timed_out;
-  const int H = gridDim.x / P, head = blockIdx.x % H, part = blockIdx.x / H, t = s.t;
+  const int head = h0 + (int)blockIdx.x % Hb, part = (int)blockIdx.x / Hb, t = s.t;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rb = (t + P - 1) / P, r0 = min(t, part * rb), r1 = min(t, r0 + rb);
   if (tid == 0) timed_out = 0;
@@ -898,7 +746,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
   hm = block_max(hm, red);
   nb = block_max(nb, red);
   if (tid == 0) {
-    if (part == 0 && status) status[head] = 0;   // parts OR their flags in at the end
+    if (part == 0 && o.status) o.status[head] = 0;   // parts OR their flags in at the end
     s.init[(size_t)head * ps + part] = make_float2(hm, nb);
     s.PN[((size_t)head * 2 + 0) * ps + part] = part == 0 ? (float)t : 0.f;
     s.P[((size_t)head * 2 + 0) * ps + part] = make_float2(0.f, INFINITY);
@@ -1018,24 +866,66 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
     gm = 0.f;
     for (int b = 0; b < P; ++b) gm = fmaxf(gm, pst[b].y);
   }
-  // the answer is v_k
+  // the answer is v_k, whose rows were all written before the last barrier: every
+  // workgroup forms the whole returned w (for the KKT product) and writes its own rows
   const float* v = s.V + ((size_t)head * 3 + k % 3) * t;
+  for (int j = tid; j < t; j += 256) {
+    const float di = dinv[j];
+    const float w = di > 0.f ? ld_dev(v + j) * di : s.lo;
+    xs[j] = fminf(fmaxf(w, s.lo), s.hi);
+  }
+  __syncthreads();
   float nbw = 0.f;
   for (int j = r0 + tid; j < r1; j += 256) {
-    const float di = dinv[j];
-    float w = di > 0.f ? ld_dev(v + j) * di : s.lo;
-    w = fminf(fmaxf(w, s.lo), s.hi);
+    const float w = xs[j];
     if (!isfinite(w)) nbw = 1.f;
-    if (w_out) w_out[(size_t)head * t + j] = w;
-    beta[(size_t)head * t + j] = w > 0.f ? logf(w) : -INFINITY;
+    if (o.w) o.w[(size_t)head * t + j] = w;
+    o.beta[(size_t)head * t + j] = w > 0.f ? logf(w) : -INFINITY;
   }
   nbw = block_max(nbw, red);
-  if (tid == 0 && part == 0) s.iters[head] = k;
-  if (tid == 0 && status) {
-    const int bits = ((timed_out || k == 0 || !(gm <= thr)) ? AM_HEAD_NNLS_BIT : 0) |
-                     ((bad || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0);
-    if (bits) atomicOr(&status[head], bits);
+  if (o.kkt) {   // KKT residual of the returned w on the system solved, own rows
+    float pv = 0.f, ph = 0.f;
+    for (int i = r0 + wave; i < r1; i += 4) {
+      const float* gr = grow(i);
+      float acc = 0.f;
+      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
+#pragma unroll
+      for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, 64);
+      const float hi = s.hv[(size_t)head * t + i];
+      if (lane == 0) {
+        pv = fmaxf(pv, kkt_violation(acc - hi, xs[i], s.lo, s.hi));
+        ph = fmaxf(ph, fabsf(hi));
+      }
+    }
+    pv = block_max(pv, red);
+    ph = block_max(ph, red);
+    if (tid == 0) s.kktp[(size_t)head * ps + part] = make_float2(pv, ph);
   }
+  if (tid == 0 && part == 0 && o.iters) o.iters[head] = k;
+  if (tid == 0 && o.status) {
+    const int bits = ((timed_out || k == 0 || !(gm <= thr)) ? AM_HEAD_NNLS_BIT : 0) |
+                     ((bad || nbw > 0.f) ? AM_HEAD_NONFINITE_BIT : 0) |
+                     (timed_out ? AM_HEAD_TIMEOUT_BIT : 0);
+    if (bits) atomicOr(&o.status[head], bits);
+  }
+}
+
+// kkt[h] = the largest violation over the head's workgroups / the largest |h_j|
+__global__ __launch_bounds__(64) void nnls_kkt_final_kernel(const float2* __restrict__ kktp,
+                                                            int nblk, float* __restrict__ kkt) {
+  const int head = blockIdx.x;
+  float v = 0.f, hm = 0.f;
+  for (int b = threadIdx.x; b < nblk; b += 64) {
+    const float2 p = kktp[(size_t)head * nblk + b];
+    v = fmaxf(v, p.x);
+    hm = fmaxf(hm, p.y);
+  }
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) {
+    v = fmaxf(v, __shfl_xor(v, o2, 64));
+    hm = fmaxf(hm, __shfl_xor(hm, o2, 64));
+  }
+  if (threadIdx.x == 0) kkt[head] = v / fmaxf(hm, 1e-30f);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1044,6 +934,11 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int P, int 
 // 64-row fp64 blocks staged through LDS for the block kernels. A loader issues all of
 // its global loads (16-byte, one per register pair) before it writes any of them to LDS, so
 // a block costs one memory latency rather than one per element.
+// A pivot below kPivRel times its column's diagonal entry before the factorization (or not
+// positive) marks the system as singular at the precision of the solve: AM_HEAD_CHOL_PIVOT.
+// With the ridge lambda > 0 every pivot is at least lambda, far above this for any
+// diagonal the designs produce (at most n <= 2^30 plus lambda).
+constexpr double kPivRel = 0x1p-40;
 constexpr int kLdp = kNB + 1;   // LDS row pitch (odd: column reads by 16 rows hit 16 banks)
 // The workgroup bodies below take their LDS from the kernel that runs them, so kernels that
 // combine two kinds of workgroup need only the larger of their footprints: two 64 x 65 tiles
@@ -1139,9 +1034,10 @@ __device__ __forceinline__ void chol32_steps(double (&a)[32], double* col, int r
   }
 }
 
-// col: 64 doubles of LDS (the posted column and, above it, the slots of lanes not posting)
+// col: 64 doubles of LDS (the posted column and, above it, the slots of lanes not posting);
+// thr: the smallest pivot lane r accepts for its row (see kPivRel)
 __device__ __forceinline__ void chol32_wave(double (*L)[kNB + 1], double (*Li)[kNB + 1], int o,
-                                            double* col, bool& bad) {
+                                            double* col, bool& bad, double thr) {
   const int lane = threadIdx.x & 63, r = lane & 31, half = lane >> 5;
   double a[32];
 #pragma unroll
@@ -1157,10 +1053,8 @@ __device__ __forceinline__ void chol32_wave(double (*L)[kNB + 1], double (*Li)[k
     double dr = a[0];
 #pragma unroll
     for (int j = 1; j < 32; ++j) dr = j == r ? a[j] : dr;
-    if (!(dr > 0.0)) {
-      if (!half) bad = true;
-      dr = 1e-300;
-    }
+    if (!(dr > thr) && !half) bad = true;
+    if (!(dr > 0.0)) dr = 1e-300;
     col[r + 32 * half] = 1.0 / sqrt(dr);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -1200,10 +1094,14 @@ __device__ __forceinline__ void mm32(double (&out)[4], const double (*P)[kNB + 1
 // The diagonal block kb of one head. LDS: L (the block, then its factor), Li (the inverse of
 // the factor; while L22 is factored its upper right quadrant, zero in the result, holds
 // T = L21 L11^-1), piv (the wave-level eliminations' pivot columns), badf.
-__device__ __forceinline__ void chol_diag_body(double* A, double* Linv, int ld, int kb, int nb,
-                                               int32_t* status, int head, LdsTile& L,
-                                               LdsTile& Li, double* piv, int& badf) {
+__device__ __forceinline__ void chol_diag_body(double* A, double* Linv, const double* Dg, int ld,
+                                               int kb, int nb, int32_t* status, int head,
+                                               LdsTile& L, LdsTile& Li, double* piv, int& badf) {
   const int tid = threadIdx.x, wave = tid >> 6;
+  // pivot thresholds of the rows lane r of wave 0 eliminates (rows r and 32 + r of the block)
+  const double* dgb = Dg + (size_t)head * ld + kb * kNB + (tid & 31);
+  const double thr0 = wave == 0 ? kPivRel * dgb[0] : 0.0;
+  const double thr1 = wave == 0 ? kPivRel * dgb[32] : 0.0;
   double* Ah = A + (size_t)head * ld * ld + (size_t)kb * kNB * ld + kb * kNB;
   {
     BlockRegs<kNB> ra;
@@ -1214,7 +1112,7 @@ __device__ __forceinline__ void chol_diag_body(double* A, double* Linv, int ld, 
   if (tid == 0) badf = 0;
   __syncthreads();
   bool bad = false;
-  if (wave == 0) chol32_wave(L, Li, 0, piv, bad);
+  if (wave == 0) chol32_wave(L, Li, 0, piv, bad, thr0);
   __syncthreads();
   const int i = tid >> 3, j0 = tid & 7;
   double acc[4];
@@ -1231,7 +1129,7 @@ __device__ __forceinline__ void chol_diag_body(double* A, double* Linv, int ld, 
   __syncthreads();
   // wave 0: L22 and its inverse; the other waves meanwhile T = L21 L11^-1
   if (wave == 0) {
-    chol32_wave(L, Li, 32, piv, bad);
+    chol32_wave(L, Li, 32, piv, bad, thr1);
   } else {
     for (int e = tid - 64; e < 32 * 32; e += 192) {
       const int ii = e >> 5, jj = e & 31;
@@ -1256,12 +1154,19 @@ __device__ __forceinline__ void chol_diag_body(double* A, double* Linv, int ld, 
   if (tid == 0 && badf && status) atomicOr(&status[head], AM_HEAD_CHOL_BIT);
 }
 
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, int ld, int kb,
-                                                        int nb, int32_t* status) {
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* A, double* Linv, const double* Dg,
+                                                        int ld, int kb, int nb, int32_t* status) {
   __shared__ LdsTile s0, s1;
   __shared__ __align__(16) double piv[64];
   __shared__ int badf;
-  chol_diag_body(A, Linv, ld, kb, nb, status, blockIdx.x, s0, s1, piv, badf);
+  chol_diag_body(A, Linv, Dg, ld, kb, nb, status, blockIdx.x, s0, s1, piv, badf);
+}
+
+// Dg[h, i] = A[h, i, i] before the factorization (the reference of the pivot test)
+__global__ __launch_bounds__(256) void diag_copy_kernel(const double* __restrict__ A,
+                                                        double* __restrict__ Dg, int ld) {
+  const int head = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (i < ld) Dg[(size_t)head * ld + i] = A[(size_t)head * ld * ld + (size_t)i * ld + i];
 }
 
 
@@ -1432,8 +1337,8 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* A, const double
 // Workgroup 0 takes the pair (kb + 1, kb + 1) and then factors that block, the next step's
 // diagonal block, while the others finish the update (lookahead: no launch of its own).
 __global__ __launch_bounds__(256) void chol_update_kernel(double* A, double* R, double* Linv,
-                                                          int32_t* status, int ld, int D, int kb,
-                                                          int nb) {
+                                                          const double* Dg, int32_t* status,
+                                                          int ld, int D, int kb, int nb) {
   __shared__ LdsTile s0, s1;
   __shared__ __align__(16) double piv[64];
   __shared__ int badf;
@@ -1444,7 +1349,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* A, double* R, 
     chol_update_body(A, ld, kb, kb + 1 + a0, kb + 1 + b0, head, s0, s1);
     if (blockIdx.x == 0) {   // a0 = b0 = 0: the block just written (same workgroup)
       __syncthreads();
-      chol_diag_body(A, Linv, ld, kb + 1, nb, status, head, s0, s1, piv, badf);
+      chol_diag_body(A, Linv, Dg, ld, kb + 1, nb, status, head, s0, s1, piv, badf);
     }
   } else {
     const int e = blockIdx.x - ntri, ns = D / 32;
@@ -1585,8 +1490,8 @@ struct Carve {
 
 struct BetaPlan {
   float* shift2; float* target; float* Gpart; float* hpart; float* G; float* hv;
-  float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float* TK; float* hsmax;
-  int* iters; int* fin; float2* init; int* bar; int2* tstat; float2* rowstat_cmp; double2* part; int32_t* status;
+  float* dinv; float* hs; float* V; float* X; float* PN; float2* P; float2* init; float2* kktp;
+  int* bar; int2* tstat; float2* rowstat_cmp; double2* part; int32_t* status;
   SyrkBuffers sy;
   size_t bytes;
 };
@@ -1619,11 +1524,8 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
   p.X = c.take<float>(heads * 2 * t);
   p.PN = c.take<float>(heads * 2 * nblk);
   p.P = c.take<float2>(heads * 2 * nblk);
-  p.TK = c.take<float>(heads * 2);
-  p.hsmax = c.take<float>(heads);
-  p.iters = c.take<int>(heads);
-  p.fin = c.take<int>(heads);
   p.init = c.take<float2>(heads * nblk);
+  p.kktp = c.take<float2>(heads * nblk);
   p.bar = c.take<int>(heads);
   p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
   p.status = c.take<int32_t>(heads);
@@ -1633,7 +1535,7 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
 
 struct ValuePlan {
   float2* rowstat_cmp; double2* part; float* shift2; float* Gpart; float* Rpart; double* A;
-  double* R; double* Linv; void* Vt; int2* tstat; float2* rowres; int32_t* status;
+  double* R; double* Linv; double* Dg; void* Vt; int2* tstat; float2* rowres; int32_t* status;
   SyrkBuffers sy;
   size_t bytes;
 };
@@ -1661,6 +1563,7 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   p.A = c.take<double>((size_t)heads * ld * ld);
   p.R = c.take<double>((size_t)heads * ld * d);
   p.Linv = c.take<double>((size_t)heads * (ld / kNB) * kNB * kNB);
+  p.Dg = c.take<double>((size_t)heads * ld);
   p.Vt = c.take<char>(cmp_vt_bytes(heads, t, d, esize));
   p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
   p.rowres = c.take<float2>(heads * n);
@@ -1693,6 +1596,54 @@ static void launch_gram_any(const GramParams& gp, int heads, int d, bool bf, boo
 }
 
 static unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+
+int device_cu_count() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return ncu;
+}
+
+hipError_t launch_all_resident(const void* fn, dim3 grid, dim3 block, void** args, size_t shmem,
+                               hipStream_t st) {
+  const int ncu = device_cu_count();
+  int per_cu = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, fn, (int)(block.x * block.y * block.z), shmem);
+  if (e != hipSuccess) return e;
+  if ((long long)per_cu * ncu < (long long)grid.x * grid.y * grid.z)
+    return hipErrorCooperativeLaunchTooLarge;
+  return hipLaunchKernel(fn, grid, block, args, shmem, st);
+}
+
+// A batch of hb heads on the multi-workgroup solver: P workgroups per head (at most one per
+// CU for the batch, at most one per 16 rows, at most 256), rb rows each, of which the
+// first nlds are held in LDS (the vector, two row slices and as many rows of G as fit).
+NnlsParts nnls_parts(int hb, int t, int ncu) {
+  NnlsParts p;
+  p.P = std::max(1, std::min(std::min(ncu / std::max(hb, 1), (t + kRB - 1) / kRB), 256));
+  p.rb = (t + p.P - 1) / p.P;
+  const size_t lds_f = kNnlsCoopLds / sizeof(float), fixed = (size_t)t + 2 * (size_t)p.rb;
+  p.nlds = lds_f > fixed ? (int)std::min<size_t>((size_t)p.rb, (lds_f - fixed) / t) : 0;
+  p.shmem = (fixed + (size_t)p.nlds * t) * sizeof(float);
+  return p;
+}
+
+NnlsSchedule nnls_schedule(int heads, int t, int ncu) {
+  NnlsSchedule sc;
+  if (t <= kNnlsSingle) {
+    sc.heads_per_launch = heads;
+    sc.launches = 1;
+    sc.first = NnlsParts{1, t, t <= kNnlsLdsG ? t : 0, 0};
+    return sc;
+  }
+  // every head of a batch gets at least four workgroups (CUs)
+  sc.heads_per_launch = std::max(1, std::min(heads, ncu / 4));
+  sc.launches = (heads + sc.heads_per_launch - 1) / sc.heads_per_launch;
+  sc.first = nnls_parts(sc.heads_per_launch, t, ncu);
+  return sc;
+}
 
 hipError_t launch_fit_beta(const FitArgs& a) {
   const hipStream_t st = a.stream;
@@ -1733,55 +1684,35 @@ hipError_t launch_fit_beta(const FitArgs& a) {
   // NNLS
   NnlsState s;
   s.G = pl.G; s.hv = pl.hv; s.dinv = pl.dinv; s.hs = pl.hs; s.V = pl.V; s.X = pl.X;
-  s.PN = pl.PN; s.P = pl.P; s.TK = pl.TK; s.hsmax = pl.hsmax; s.iters = pl.iters;
-  s.fin = pl.fin; s.init = pl.init; s.bar = pl.bar;
+  s.PN = pl.PN; s.P = pl.P; s.init = pl.init; s.kktp = pl.kktp; s.bar = pl.bar;
   s.t = t; s.nblk = (t + kRB - 1) / kRB;
   s.lo = a.w_lo; s.hi = a.w_hi; s.tol = a.tol;
-  bool done = false;
-  if (t > kNnlsCoopMinT) {
-    // cooperative solver: P workgroups per head, all co-resident (one per CU)
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        ncu >= 4 * H) {
-      // one workgroup per CU: the rows of G then mostly fit in LDS (G read from L2 every
-      // step costs more than the extra barrier traffic of more workgroups)
-      int P = ncu / H;
-      if (P > s.nblk) P = s.nblk;
-      if (P > 256) P = 256;   // the partials of a head are staged in one pass
-      const int rb = (t + P - 1) / P;
-      // dynamic LDS: the vector (t), two row slices (2 rb) and as many of the workgroup's
-      // rows of G as fit (nlds t)
-      const size_t lds_f = kNnlsCoopLds / sizeof(float), fixed = (size_t)t + 2 * (size_t)rb;
-      int nlds = lds_f > fixed ? (int)std::min<size_t>((size_t)rb, (lds_f - fixed) / t) : 0;
-      const size_t shmem = (fixed + (size_t)nlds * t) * sizeof(float);
-      int max_iter = a.max_iter;
-      float* wout = a.w;
-      float* beta = a.beta;
-      int32_t* stp = status;
-      void* args[] = {&s, &P, &max_iter, &nlds, &wout, &beta, &stp};
-      hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(H, 256)), dim3(256), 0, st, pl.bar, H);
-      (void)hipFuncSetAttribute((const void*)nnls_coop_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-      if (hipLaunchCooperativeKernel((const void*)nnls_coop_kernel, dim3(H * P), dim3(256), args,
-                                     (unsigned)shmem, st) == hipSuccess)
-        done = true;
-      else
-        (void)hipGetLastError();   // refused (e.g. not co-resident): use the kernels below
-    }
-  }
-  if (done) {
-  } else if (t <= kNnlsSingle) {
-    hipLaunchKernelGGL(nnls_single_kernel, dim3(H), dim3(kNnlsSingle), 0, st, s, a.max_iter, a.w,
-                       a.beta, status);
+  NnlsOut o{a.w, a.beta, status, a.kkt, a.iters};
+  if (t <= kNnlsSingle) {
+    hipLaunchKernelGGL(nnls_single_kernel, dim3(H), dim3(kNnlsSingle), 0, st, s, a.max_iter, o);
   } else {
-    hipLaunchKernelGGL(nnls_prep_kernel, dim3(H), dim3(256), 0, st, s, status);
-    for (int k = 0; k < kPow; ++k)
-      hipLaunchKernelGGL(nnls_power_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
-    for (int k = 0; k < a.max_iter; ++k)
-      hipLaunchKernelGGL(nnls_step_kernel, dim3(s.nblk, H), dim3(256), 0, st, s, k);
-    hipLaunchKernelGGL(nnls_finish_kernel, dim3(H), dim3(256), 0, st, s, a.max_iter, a.w, a.beta,
-                       status);
+    const int ncu = device_cu_count();
+    if (ncu < 1) return hipErrorInvalidDevice;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(H, 256)), dim3(256), 0, st, pl.bar, H);
+    if (a.kkt)
+      hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv((long long)H * s.nblk * 2, 256)), dim3(256), 0,
+                         st, (int32_t*)pl.kktp, H * s.nblk * 2);
+    const NnlsSchedule sc = nnls_schedule(H, t, ncu);
+    int max_iter = a.max_iter;
+    for (int h0 = 0; h0 < H; h0 += sc.heads_per_launch) {
+      int hb = std::min(sc.heads_per_launch, H - h0);
+      const NnlsParts pp = nnls_parts(hb, t, ncu);
+      int P = pp.P, nlds = pp.nlds;
+      void* args[] = {&s, &h0, &hb, &P, &max_iter, &nlds, &o};
+      (void)hipFuncSetAttribute((const void*)nnls_coop_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)pp.shmem);
+      const hipError_t e = launch_all_resident((const void*)nnls_coop_kernel, dim3(hb * P),
+                                               dim3(256), args, pp.shmem, st);
+      if (e != hipSuccess) return e;
+    }
+    if (a.kkt)
+      hipLaunchKernelGGL(nnls_kkt_final_kernel, dim3(H), dim3(64), 0, st,
+                         (const float2*)pl.kktp, s.nblk, a.kkt);
   }
   // mass residual from the biased compacted pass: Z_cmp / Z = 2^(lc - lse2); the pass's row
   // statistics are also what the value fit needs, so they are kept when asked for
@@ -1853,15 +1784,18 @@ hipError_t launch_fit_values(const FitArgs& a) {
   // Cholesky, with the forward solve L Z = R folded into each step's panel and update
   // launches; then the backward solve L^T C = Z
   // (the diagonal blocks after the first are factored inside the previous step's update)
-  hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv, ld, 0, nb,
-                     status);
+  hipLaunchKernelGGL(diag_copy_kernel, dim3(cdiv(ld, 256), H), dim3(256), 0, st,
+                     (const double*)pl.A, pl.Dg, ld);
+  hipLaunchKernelGGL(chol_diag_kernel, dim3(H), dim3(256), 0, st, pl.A, pl.Linv,
+                     (const double*)pl.Dg, ld, 0, nb, status);
   for (int kb = 0; kb < nb; ++kb) {
     const int m = nb - kb - 1;
     hipLaunchKernelGGL(chol_panel_kernel, dim3(m + d / 32, H), dim3(256), 0, st, pl.A,
                        (const double*)pl.Linv, pl.R, ld, d, kb, nb);
     if (m > 0)
       hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2 + m * (d / 32), H), dim3(256),
-                         0, st, pl.A, pl.R, pl.Linv, status, ld, d, kb, nb);
+                         0, st, pl.A, pl.R, pl.Linv, (const double*)pl.Dg, status, ld, d, kb,
+                         nb);
   }
   // (each update launch also forms the next block row's diagonal product)
   hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,

@@ -3,6 +3,7 @@ tolerance checks (normwise output rows, selection near-tie rule)."""
 import numpy as np
 
 from kv_cache_compaction_amd import synth
+from oracle import am_oracle as O
 
 
 def to_dev(x: np.ndarray, dtype: str):
@@ -40,3 +41,15 @@ def check_selection(idx_gpu: np.ndarray, score_ref: np.ndarray, t: int, rel: flo
     assert not missing, f"keys clearly above threshold not selected: {missing[:10]}"
     assert not extra, f"keys clearly below threshold selected: {extra[:10]}"
     return len(S & set(order[:t].tolist())) / t
+
+
+def oracle_optimum_on(q, k, r, idx_gpu, w):
+    """The oracle's fitted cache on the GPU's key set: r itself when the GPU selected the
+    oracle's keys, else the oracle's S4-S7 refitted on idx_gpu (reading of "residuals within
+    1% of the oracle's" when the sets differ by near ties). Returns (r_mass, r_out, refit)."""
+    idx_gpu = np.asarray(idx_gpu, dtype=np.int64)
+    if np.array_equal(idx_gpu, r["idx"]):
+        return r["r_mass"], r["r_out"], False
+    rr = O.fit_selected(q, k, r["lse"], r["O"], idx_gpu, w.scale, w.causal, w.group,
+                        ridge_lambda=w.ridge_lambda)
+    return rr["r_mass"], rr["r_out"], True

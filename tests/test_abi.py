@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert amc.lib().am_abi_version() == amc.ABI_VERSION == 3
+    assert amc.lib().am_abi_version() == amc.ABI_VERSION == 4
     assert amc.status_str(0) == "ok"
     assert amc.status_str(-3) == "workspace too small"
     assert amc.status_str(7) == "unknown status"
@@ -96,7 +96,8 @@ def test_fit_validation():
     o = amc.make_options()
     fb = lambda t, opt, nb=1 << 40, **kw: L.am_fit_beta_nnls(
         ctypes.byref(p), FAKE, FAKE, FAKE, kw.get("lse", FAKE), t, ctypes.byref(opt)
-        if opt is not None else None, FAKE, None, None, None, FAKE, nb, None)
+        if opt is not None else None, FAKE, None, None, kw.get("kkt"), kw.get("iters"), None,
+        FAKE, nb, None)
     assert fb(0, o) == amc.AM_ERR_INVALID_ARG
     assert fb(4, None) == amc.AM_ERR_INVALID_ARG
     assert fb(4, o, lse=None) == amc.AM_ERR_INVALID_ARG
@@ -105,6 +106,14 @@ def test_fit_validation():
     assert fb(4, amc.make_options(nnls_max_iter=0)) == amc.AM_ERR_INVALID_ARG
     assert fb(4, amc.make_options(score="max", mass="absolute", ridge_lambda=-1.0)) == amc.AM_ERR_INVALID_ARG
     assert fb(4, o, nb=8) == amc.AM_ERR_WORKSPACE
+    assert fb(4, o, kkt=FAKE + 4) == amc.AM_ERR_INVALID_ARG     # misaligned diagnostics
+    assert fb(4, o, iters=FAKE + 8) == amc.AM_ERR_INVALID_ARG
+    assert fb(4, o, nb=8, kkt=FAKE, iters=FAKE) == amc.AM_ERR_WORKSPACE
+    plan = amc.AmNnlsPlan()
+    assert L.am_fit_beta_plan(ctypes.byref(p), 0, ctypes.byref(plan)) == amc.AM_ERR_INVALID_ARG
+    assert L.am_fit_beta_plan(ctypes.byref(p), 4, None) == amc.AM_ERR_INVALID_ARG
+    assert L.am_fit_beta_plan(ctypes.byref(P(d=96)), 4, ctypes.byref(plan)) == \
+        amc.AM_ERR_UNSUPPORTED
     fv = lambda t, lam, nb=1 << 40: L.am_fit_values_ols(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE,
                                                        FAKE, t, lam, FAKE, None, None, FAKE, nb,
                                                        None)
