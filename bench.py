@@ -9,8 +9,10 @@ value = causally visible query-key pairs of the batch / step time (pairs/s).
 roofline = the flash pass (the dominant kernel): 4 d flops per visible pair (Q K^T and
 P V on bf16 MFMA) over its average duration, timed with HIP events on the stream the
 library launches on, against the bf16 dense MFMA peak.
-cpu_baseline = the float64 oracle's full-cache statistics on a bounded sample of query
-rows of head 0 (pairs/s), on the host cores.
+cpu_baseline = the float64 oracle, stage by stage (S1 targets, S2 scores, S3 selection,
+S4+S5 beta fit, S6+S7 value fit), on a bounded sample: 24576 evenly spaced query rows of
+head 0 with every key they see; its whole-step rate is reported beside the GPU's, with the
+host's CPU model, BLAS thread count and library versions.
 next = the adjacent rows, timed on the same inputs: the fast pipeline (redistributed beta,
 direct values), the two-pass method (256-query subset, shortlist of 4t keys, then the fast
 fits), the anchor + diversifier initialization of a t/4-slot budget, the held-out
@@ -78,9 +80,39 @@ def time_calls(torch, fn, reps, warm=True):
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(w, Q, K, V, target_s=12.0):
-    """Oracle (float64 numpy) S1+S2 on a bounded, evenly spaced sample of query rows of
-    head 0 against its full key set; returns pairs/s and the sample description."""
+def host_info():
+    """CPU model, BLAS library and thread count, numpy/scipy versions of the host."""
+    import numpy as np
+    import scipy
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        import threadpoolctl
+        for d in threadpoolctl.threadpool_info():
+            if d.get("user_api") == "blas":
+                blas = {"blas": f"{d.get('internal_api')} {d.get('version')}",
+                        "blas_threads": d.get("num_threads")}
+                break
+    except Exception:   # threadpoolctl missing or failing: report what is known
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), **blas,
+            "numpy": np.__version__, "scipy": scipy.__version__}
+
+
+def cpu_baseline(w, Q, K, V, rows_max=24576):
+    """The float64 oracle stage by stage on a bounded sample of the workload: m evenly
+    spaced query rows of head 0 with every key they see. S1 = lse and outputs
+    (attention_rows), S2 = the per-key statistics (a second pass over the same scores, as
+    the device does), S3 = top-t on the sample's RMS scores, S4+S5 = mass design + NNLS,
+    S6+S7 = value design + ridge solve, both on the sample rows. Returns the whole-step
+    rate (sample pairs / the five stages' time), per-stage seconds and host metadata."""
     import numpy as np
 
     from kv_cache_compaction_amd import synth
@@ -89,23 +121,37 @@ def cpu_baseline(w, Q, K, V, target_s=12.0):
     q = synth.as_f64(Q[0], w.dtype)
     k = synth.as_f64(K[0], w.dtype)
     v = synth.as_f64(V[0], w.dtype)
-
-    def run(m):
-        rows = np.linspace(0, w.n - 1, m).astype(np.int64)
+    m = min(w.n, rows_max)
+    rows = np.linspace(0, w.n - 1, m).astype(np.int64)
+    pairs = int((rows // w.group + 1).sum()) if w.causal else m * w.T
+    st = {}
+    t0 = time.perf_counter()
+    lse, Oo = O.attention_rows(q, k, v, w.scale, rows, w.causal, w.group)
+    st["S1"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _, _, stats = O.full_cache_stats(q[rows], k, k, w.scale, w.causal, w.group, want_O=False,
+                                     rows=rows)
+    st["S2"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx = O.select_top(O.key_score(stats, "rms", m), w.t)
+    st["S3"] = time.perf_counter() - t0
+    fits = m >= 8 * w.t   # fewer rows than that leave the NNLS rank-deficient and slow
+    if fits:
         t0 = time.perf_counter()
-        O.full_cache_stats(q[rows], k, v, w.scale, w.causal, w.group, rows=rows)
-        vis_pairs = int((rows // w.group + 1).sum()) if w.causal else m * w.T
-        return time.perf_counter() - t0, vis_pairs
-
-    dt, pairs = run(256)
-    m = int(min(w.n, max(256, 256 * target_s / max(dt, 1e-3))))
-    m = max(256, m // 256 * 256)
-    dt, pairs = run(m)
-    threads = int(os.environ.get("OPENBLAS_NUM_THREADS", os.environ.get("OMP_NUM_THREADS", "0")) or 0)
-    return {"value": pairs / dt, "unit": "pairs/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle",
-            "sample": f"full-cache statistics (lse, outputs, per-key p^2) of {m} evenly spaced "
-                      f"query rows of head 0 against all {w.T} keys, float64 numpy, {dt:.1f} s"}
+        M, b = O.mass_design(q[rows], k[idx], idx, lse, w.scale, w.causal, w.group, rows=rows)
+        wv, _ = O.fit_beta(M, b)
+        st["S4+S5"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.fit_values(O.value_design(M, wv), Oo, w.ridge_lambda)
+        st["S6+S7"] = time.perf_counter() - t0
+    total = sum(st.values())
+    info = host_info()
+    return {"value": pairs / total, "unit": "pairs/s",
+            "cores": info.get("blas_threads") or info["cpu_count"], "kind": "oracle",
+            "sample": f"head 0, {m} evenly spaced query rows with every key they see "
+                      f"({pairs} visible pairs), all five stages in float64 "
+                      f"({'S1-S7' if fits else 'S1-S3 only'}), {total:.1f} s",
+            "stages_s": st, "host": info}
 
 
 def main():
@@ -239,6 +285,7 @@ def main():
         print("[bench] timing the float64 oracle on a bounded sample (host cores)",
               file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, Q, K, V)
+        cpu["gpu_over_oracle"] = (pairs / (ms * 1e-3)) / cpu["value"]
 
     out = {
         "metric": METRIC,

@@ -163,17 +163,19 @@ def select_top(score: np.ndarray, t: int) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 # S4: the mass design
 # --------------------------------------------------------------------------------------
-def mass_design(Q, Ck, idx, lse, scale, causal=False, group=1, mode="relative"):
+def mass_design(Q, Ck, idx, lse, scale, causal=False, group=1, mode="relative", rows=None):
     """Design matrix M [n, t] and target b [n] of the mass equations.
 
     Mass equation for query i: sum_j exp(s_i,c_j + beta_j) ~= Z_i (blog, §Choosing beta).
     relative: divide by Z_i  -> M_ij = exp(s_i,c_j - lse_i), b_i = 1.
     absolute: divide by exp(c), c = max_i lse_i -> M_ij = exp(s_i,c_j - c), b_i = exp(lse_i - c).
-    Compacted keys keep their positions, so the causal mask uses idx.
+    Compacted keys keep their positions, so the causal mask uses idx. `rows` gives the query
+    indices of the rows of Q when Q is a subset of a problem's queries.
     """
     Q = np.asarray(Q, np.float64)
     s = scale * (Q @ np.asarray(Ck, np.float64).T)
-    vis = visible(np.arange(Q.shape[0]), np.asarray(idx), causal, group)
+    rows = np.arange(Q.shape[0]) if rows is None else np.asarray(rows)
+    vis = visible(rows, np.asarray(idx), causal, group)
     if mode == "relative":
         M = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[:, None]), 0.0)
         b = np.ones(Q.shape[0])
@@ -650,13 +652,14 @@ def output_residual_from_stats(A, Cv, AtY, yy) -> float:
 # the whole per-head pipeline
 # --------------------------------------------------------------------------------------
 def fit_selected(Q, K, lse, O, idx, scale, causal=False, group=1, mass="relative", w_lo=0.0,
-                 w_hi=np.inf, ridge_lambda=1e-3):
+                 w_hi=np.inf, ridge_lambda=1e-3, rows=None):
     """S4..S7 on a given key set: the mass design and beta (NNLS on w), then the value
-    design and C_v (ridge), with both residuals. lse and O are the full-cache targets."""
+    design and C_v (ridge), with both residuals. lse and O are the full-cache targets of
+    the rows of Q (query indices `rows` when Q is a subset of a problem's queries)."""
     Q = np.asarray(Q, np.float64)
     idx = np.asarray(idx, np.int64)
     Ck = np.asarray(K, np.float64)[idx]
-    M, b = mass_design(Q, Ck, idx, lse, scale, causal, group, mass)
+    M, b = mass_design(Q, Ck, idx, lse, scale, causal, group, mass, rows)
     w, beta = fit_beta(M, b, w_lo, w_hi)
     A = value_design(M, w)
     Cv = fit_values(A, O, ridge_lambda)

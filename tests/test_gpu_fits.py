@@ -313,12 +313,14 @@ def test_nnls_diagnostics(w):
     assert np.all(kkt1 > 10 * kkt)
 
 
-@pytest.mark.parametrize("lo,hi,binds", [(math.exp(-3), math.exp(3), False), (1.0, 1.2, True)],
+@pytest.mark.parametrize("lo,hi,binds", [(math.exp(-3), math.exp(3), False), (1.1, 1.2, True)],
                          ids=["am_box", "tight_box"])
 def test_bounded_nnls_multiworkgroup(lo, hi, binds):
     """Box bounds on the multi-workgroup solver: the AM baseline's [e^-3, e^3] (Latent
     Compaction App. A.3), which these synthetic designs leave inactive (their free weights
-    lie in about [0.9, 2.9]), and a tight box that binds at both ends."""
+    lie in about [0.9, 2.9]), and a tight box that binds at both ends. The bounds are
+    float32 in the library, so both sides use their float32 values."""
+    lo, hi = float(np.float32(lo)), float(np.float32(hi))
     w = Workload("box_t384", 2, 128, 2048, 2048, 384, "bf16", False, 1)
     assert amc.fit_beta_plan(w.heads, w.n, w.T, w.d, w.t)["workgroups_per_head"] > 1
     opts = amc.make_options(w_lo=lo, w_hi=hi, nnls_max_iter=2000)
