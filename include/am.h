@@ -293,6 +293,24 @@ am_status am_compact_head(const am_problem* p, const void* Q, const void* K, con
                           void* ws, size_t ws_bytes, am_stream_t stream);
 
 /*
+ * am_compact_head_noalloc - am_compact_head for callers that cannot allocate device memory
+ * (work captured into graphs, tight serving loops, harnesses that forbid allocation): the
+ * same computation and outputs, with the scratch taken from a fixed array of
+ * AM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on (from the first
+ * call on that GPU until the process ends) instead of a workspace argument. Problems whose
+ * am_workspace_bytes(p, t, AM_CALL_COMPACT) exceeds that size return AM_ERR_WORKSPACE and
+ * launch nothing; invalid arguments return what am_compact_head returns. Every call on one
+ * GPU uses the same array: calls that overlap on one GPU (other streams or host threads)
+ * race and must be serialized by the caller. No allocation is made by the call.
+ */
+#define AM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+am_status am_compact_head_noalloc(const am_problem* p, const void* Q, const void* K,
+                                  const void* V, int64_t t, const am_options* opt, int32_t* idx,
+                                  void* Ck, float* beta, float* Cv, float* lse_out, float* O_out,
+                                  float* score_out, float* resid_out, int32_t* head_status,
+                                  am_stream_t stream);
+
+/*
  * am_cache_attention - attention of queries through a compacted cache whose slots carry
  * learned biases, optionally followed by ordinary entries appended after it (Latent
  * Compaction §3.1 Eq. 2-5; App. A.2, normalizer-aware cache attention: a biased,

@@ -75,6 +75,9 @@ _PROTOS = {
     "am_compact_head": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, ctypes.c_int64,
                                        ctypes.POINTER(AmOptions), _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, ctypes.c_size_t, _P]),
+    "am_compact_head_noalloc": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P,
+                                               ctypes.c_int64, ctypes.POINTER(AmOptions), _P, _P,
+                                               _P, _P, _P, _P, _P, _P, _P, _P]),
     "am_cache_attention": (ctypes.c_int, [ctypes.POINTER(AmProblem), _P, _P, _P, _P, _P, _P,
                                           ctypes.c_int64, _P, _P, ctypes.c_int32, _P, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
@@ -336,6 +339,41 @@ def compact_head(Q, K, V, t, *, causal=False, group=1, scale=None, options=None,
                                  _ptr(out["Cv"]), _ptr(g("lse")), _ptr(g("O")), _ptr(g("score")),
                                  _ptr(out["resid"]), _ptr(out["status"]), _ptr(ws), nb, _stream()),
            "am_compact_head")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # AM_NOALLOC_SCRATCH_BYTES of include/am.h
+
+
+def compact_head_noalloc(Q, K, V, t, *, causal=False, group=1, scale=None, options=None,
+                         want_stats=True):
+    """compact_head through am_compact_head_noalloc: the library's fixed scratch array
+    instead of a workspace (the outputs are still allocated here, by the caller)."""
+    torch = _torch()
+    _need(Q, "Q"); _need(K, "K"); _need(V, "V", dtype=K.dtype, shape=K.shape)
+    p = make_problem(Q, K, causal=causal, group=group, scale=scale)
+    o = options or make_options()
+    dev = Q.device
+    h, n, T, d = p.heads, p.n, p.T, p.d
+    out = dict(
+        idx=torch.empty((h, t), dtype=torch.int32, device=dev),
+        Ck=torch.empty((h, t, d), dtype=Q.dtype, device=dev),
+        beta=torch.empty((h, t), dtype=torch.float32, device=dev),
+        Cv=torch.empty((h, t, d), dtype=torch.float32, device=dev),
+        resid=torch.empty((2, h), dtype=torch.float32, device=dev),
+        status=torch.empty((h,), dtype=torch.int32, device=dev),
+    )
+    if want_stats:
+        out["lse"] = torch.empty((h, n), dtype=torch.float32, device=dev)
+        out["O"] = torch.empty((h, n, d), dtype=torch.float32, device=dev)
+        out["score"] = torch.empty((h, T), dtype=torch.float32, device=dev)
+    g = out.get
+    _check(lib().am_compact_head_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), t,
+                                         ctypes.byref(o), _ptr(out["idx"]), _ptr(out["Ck"]),
+                                         _ptr(out["beta"]), _ptr(out["Cv"]), _ptr(g("lse")),
+                                         _ptr(g("O")), _ptr(g("score")), _ptr(out["resid"]),
+                                         _ptr(out["status"]), _stream()),
+           "am_compact_head_noalloc")
     return out
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libamc.so")
-SOURCES = ["am_api.cpp", "k_targets.hip", "k_select.hip", "k_fit.hip", "k_syrk.hip", "k_twopass.hip", "k_diverse.hip", "k_stage1.hip"]
+SOURCES = ["am_api.cpp", "k_targets.hip", "k_select.hip", "k_fit.hip", "k_syrk.hip", "k_twopass.hip", "k_diverse.hip", "k_stage1.hip", "am_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -126,6 +126,16 @@ def test_fit_validation():
                                          FAKE, nb, None)
     assert fc(4, 8) == amc.AM_ERR_WORKSPACE
     assert fc(0, 1 << 40) == amc.AM_ERR_INVALID_ARG
+    # the allocation-free variant: problems beyond its fixed scratch are refused, invalid
+    # ones get am_compact_head's error, and neither launches anything
+    fn = lambda pp, t: L.am_compact_head_noalloc(ctypes.byref(pp), FAKE, FAKE, FAKE, t,
+                                                 ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None,
+                                                 None, None, None, None, None)
+    big = P(heads=8, n=1 << 20, T=1 << 16, causal=1, group=16)
+    assert amc.workspace_bytes(big, 64, amc.CALL_COMPACT) > amc.NOALLOC_SCRATCH_BYTES
+    assert fn(big, 64) == amc.AM_ERR_WORKSPACE
+    assert fn(p, 0) == amc.AM_ERR_INVALID_ARG
+    assert fn(P(d=96), 4) == amc.AM_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():
