@@ -122,6 +122,7 @@ TargetsArgs targets_args(const am_problem* p, const void* Q, const void* K, cons
   a.Q = Q; a.K = K; a.V = V;
   a.Vt = ws;
   a.rowstat = (char*)ws + targets_vt_bytes(p->heads, p->T, p->d, esize(p));
+  a.colpart = (float*)((char*)a.rowstat + align_up((size_t)p->heads * p->n * 8));
   a.lse = lse; a.O = O; a.score = score; a.mode = mode;
   a.heads = (int)p->heads; a.n = (int)p->n; a.T = (int)p->T; a.d = (int)p->d;
   a.group = p->group; a.causal = p->causal != 0; a.bf16 = p->dtype == AM_BF16;

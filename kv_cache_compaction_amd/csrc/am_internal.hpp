@@ -28,8 +28,12 @@ struct TargetsArgs {
   float scale;
   hipStream_t stream;
   const int32_t* qpos = nullptr;   // query subset: positions [h, n], ascending per head
+  float* colpart = nullptr;        // workspace for the causal column pass's query-chunk
+                                   // partials [kColSplit, h, T] (null: one chunk)
 };
 hipError_t launch_targets(const TargetsArgs& a);
+constexpr int kColSplit = 8;       // query chunks of the causal column-score pass
+size_t targets_colpart_bytes(int64_t heads, int64_t T);
 size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize);
 size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize);
 

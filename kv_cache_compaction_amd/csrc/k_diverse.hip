@@ -485,6 +485,7 @@ hipError_t launch_init_anchor_diverse(const InitArgs& a) {
   TargetsArgs ta;
   ta.Q = a.Q; ta.K = a.K; ta.V = nullptr; ta.Vt = pl.tws;
   ta.rowstat = (char*)pl.tws + targets_vt_bytes(H, a.T, a.d, es);
+  ta.colpart = (float*)((char*)ta.rowstat + align_up((size_t)H * a.n * 8));
   ta.lse = pl.lse; ta.O = nullptr; ta.score = pl.score; ta.mode = 2;
   ta.heads = H; ta.n = a.n; ta.T = a.T; ta.d = a.d; ta.group = a.group; ta.causal = a.causal;
   ta.bf16 = a.bf16; ta.scale = a.scale; ta.stream = st;

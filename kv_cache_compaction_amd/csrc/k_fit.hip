@@ -1458,6 +1458,74 @@ __global__ void resid_final_kernel(const double2* __restrict__ part, float* __re
   out[head] = (float)(y > 0.0 ? x / y : 0.0);
 }
 
+// Sums of squares of Y [h, count] (count a multiple of 4) over kResBlk contiguous slices per
+// head, each summed in a fixed order in fp64
+__global__ __launch_bounds__(256) void sumsq_part_kernel(const float* __restrict__ Y,
+                                                         double* __restrict__ part,
+                                                         long long count) {
+  __shared__ double red[256];
+  const int head = blockIdx.y;
+  const long long per = ((count + kResBlk - 1) / kResBlk + 3) / 4 * 4;
+  const long long a0 = min(count, (long long)blockIdx.x * per), a1 = min(count, a0 + per);
+  const float* y = Y + (size_t)head * count;
+  double acc = 0.0;
+  for (long long e = a0 + 4 * (long long)threadIdx.x; e < a1; e += 1024) {
+    const float4 v = *(const float4*)(y + e);
+    acc += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (threadIdx.x < s2) red[threadIdx.x] += red[threadIdx.x + s2];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[(size_t)head * kResBlk + blockIdx.x] = red[0];
+}
+
+// The ridge fit's output residual ||A C - Y||^2 / ||Y||^2 without another pass over the
+// queries: with C solving (A^T A + lambda I) C = A^T Y, A^T A C = A^T Y - lambda C, so
+// ||A C - Y||^2 = ||Y||^2 - <C, A^T Y> - lambda ||C||^2. C is the fp64 solution [h, ld, D],
+// R0 the right-hand side A^T Y kept before the solve, yyp the partial sums of ||Y||^2.
+// A rounding-level negative value is reported as 0.
+__global__ __launch_bounds__(256) void resid_gram_kernel(const double* __restrict__ C,
+                                                         const double* __restrict__ R0,
+                                                         const double* __restrict__ yyp,
+                                                         float lambda, int t, int ld, int D,
+                                                         float* __restrict__ out) {
+  __shared__ double r1[256], r2[256];
+  const int head = blockIdx.x;
+  const double* c = C + (size_t)head * ld * D;
+  const double* r = R0 + (size_t)head * ld * D;
+  double a1 = 0.0, a2 = 0.0;
+  for (int e = threadIdx.x; e < t * D; e += 256) {
+    const double x = c[e];
+    a1 += x * r[e];
+    a2 += x * x;
+  }
+  r1[threadIdx.x] = a1;
+  r2[threadIdx.x] = a2;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (threadIdx.x < s2) {
+      r1[threadIdx.x] += r1[threadIdx.x + s2];
+      r2[threadIdx.x] += r2[threadIdx.x + s2];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double yy = 0.0;
+    for (int b = 0; b < kResBlk; ++b) yy += yyp[(size_t)head * kResBlk + b];
+    const double res = yy > 0.0 ? (yy - r1[0] - (double)lambda * r2[0]) / yy : 0.0;
+    out[head] = (float)fmax(res, 0.0);
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_f64_kernel(const double* __restrict__ src,
+                                                       double* __restrict__ dst, long long count) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) dst[i] = src[i];
+}
+
 __global__ void zero_i32_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -1535,14 +1603,14 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
 
 struct ValuePlan {
   float2* rowstat_cmp; double2* part; float* shift2; float* Gpart; float* Rpart; double* A;
-  double* R; double* Linv; double* Dg; void* Vt; int2* tstat; float2* rowres; int32_t* status;
+  double* R; double* R0; double* Linv; double* Dg; double* yyp; int2* tstat; int32_t* status;
   SyrkBuffers sy;
   size_t bytes;
 };
 
 static int chol_ld(int t) { return round_up(t, kNB); }
 
-static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, int64_t d, int esize) {
+static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, int64_t d) {
   Carve c{base, 0};
   const int tpad = gram_ntile((int)t) * kGT;
   const int nch = gram_nch((int)heads, (int)n, (int)t);
@@ -1564,9 +1632,9 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   p.R = c.take<double>((size_t)heads * ld * d);
   p.Linv = c.take<double>((size_t)heads * (ld / kNB) * kNB * kNB);
   p.Dg = c.take<double>((size_t)heads * ld);
-  p.Vt = c.take<char>(cmp_vt_bytes(heads, t, d, esize));
+  p.R0 = c.take<double>((size_t)heads * ld * d);
+  p.yyp = c.take<double>((size_t)heads * kResBlk);
   p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
-  p.rowres = c.take<float2>(heads * n);
   p.status = c.take<int32_t>(heads);
   p.bytes = c.off;
   return p;
@@ -1576,7 +1644,7 @@ size_t fit_beta_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d) {
   return plan_beta(nullptr, heads, n, t, d).bytes;
 }
 size_t fit_values_ws_bytes(int64_t heads, int64_t n, int64_t t, int64_t d) {
-  return plan_values(nullptr, heads, n, t, d, 4).bytes;
+  return plan_values(nullptr, heads, n, t, d).bytes;
 }
 
 template <typename T, int D, bool VALUE>
@@ -1738,7 +1806,7 @@ hipError_t launch_fit_beta(const FitArgs& a) {
 hipError_t launch_fit_values(const FitArgs& a) {
   const hipStream_t st = a.stream;
   const int H = a.heads, n = a.n, t = a.t, d = a.d;
-  ValuePlan pl = plan_values((char*)a.ws, H, n, t, d, a.bf16 ? 2 : 4);
+  ValuePlan pl = plan_values((char*)a.ws, H, n, t, d);
   int32_t* status = a.head_status ? a.head_status : pl.status;
   if (!a.head_status || !a.keep_status)
     hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(H, 256)), dim3(256), 0, st, status, H);
@@ -1747,7 +1815,7 @@ hipError_t launch_fit_values(const FitArgs& a) {
   // compacted log-normalizer per query (biased pass, statistics only)
   CmpAttnArgs ca;
   ca.Q = a.Q; ca.Ck = a.Ck; ca.Cv = nullptr; ca.bias = a.beta_in; ca.keypos = a.idx; ca.Y = nullptr;
-  ca.Vt = pl.Vt; ca.tstat = pl.tstat;
+  ca.Vt = nullptr; ca.tstat = pl.tstat;
   ca.lse = nullptr; ca.rowstat = pl.rowstat_cmp; ca.O = nullptr; ca.rowres = nullptr;
   ca.heads = H; ca.n = n; ca.t = t; ca.d = d; ca.group = a.group; ca.causal = a.causal;
   ca.bf16 = a.bf16; ca.scale = a.scale; ca.stream = st;
@@ -1781,6 +1849,10 @@ hipError_t launch_fit_values(const FitArgs& a) {
     hipLaunchKernelGGL((vec_reduce_kernel<double>), dim3(cdiv((long long)ld * d, 256), H),
                        dim3(256), 0, st, pl.Rpart, pl.R, t, tpad, ld, d, nch);
   }
+  // the right-hand side A^T Y is kept for the residual (the solve overwrites R with C)
+  if (a.out_resid)
+    hipLaunchKernelGGL(copy_f64_kernel, dim3(cdiv((long long)H * ld * d, 256)), dim3(256), 0, st,
+                       (const double*)pl.R, pl.R0, (long long)H * ld * d);
   // Cholesky, with the forward solve L Z = R folded into each step's panel and update
   // launches; then the backward solve L^T C = Z
   // (the diagonal blocks after the first are factored inside the previous step's update)
@@ -1806,14 +1878,11 @@ hipError_t launch_fit_values(const FitArgs& a) {
   hipLaunchKernelGGL(store_cv_kernel, dim3(cdiv((long long)t * d, 256), H), dim3(256), 0, st,
                      (const double*)pl.R, a.Cv, t, ld, d, status);
   if (a.out_resid) {
-    CmpAttnArgs cr = ca;
-    cr.Cv = a.Cv; cr.Y = a.O; cr.rowstat = nullptr; cr.rowres = pl.rowres;
-    e = launch_cmp_attention(cr);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(out_resid_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, pl.rowres,
-                       pl.part, n);
-    hipLaunchKernelGGL(resid_final_kernel, dim3(cdiv(H, 64)), dim3(64), 0, st,
-                       (const double2*)pl.part, a.out_resid, H);
+    hipLaunchKernelGGL(sumsq_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, a.O, pl.yyp,
+                       (long long)n * d);
+    hipLaunchKernelGGL(resid_gram_kernel, dim3(H), dim3(256), 0, st, (const double*)pl.R,
+                       (const double*)pl.R0, (const double*)pl.yyp, a.lambda, t, ld, d,
+                       a.out_resid);
   }
   return hipGetLastError();
 }

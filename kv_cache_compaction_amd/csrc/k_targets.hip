@@ -484,7 +484,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
       bk[kb][kc] = *(const v8*)(Kh + (size_t)krow * D + kc * 16 + hh * 8);
   }
 
-  const int split = blockIdx.y, nsplit = gridDim.y;
+  // query chunks are dealt last first: under the causal mask the last chunk is the one
+  // every key block sees, so the heavy workgroups start first
+  const int nsplit = gridDim.y, split = nsplit - 1 - (int)blockIdx.y;
   const int qlo = split * qchunk, qend = min(n, qlo + qchunk);
   int qbeg = qlo;
   if (CAUSAL && !QPOS) qbeg = max(qlo, (min(n, kpos(k0) * group) / kBQ) * kBQ);
@@ -671,12 +673,21 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.score) return e;
   const int BK = kScoreWaves * 32 * colscore_kb<T, D>();
-  const dim3 gs(((a.T + BK - 1) / BK) * a.heads), bs(kScoreWaves * 64);
+  // causal: the query range is cut into up to kColSplit chunks (partial sums in a fixed
+  // order), so the long key blocks near the start do not leave their CUs busy long after
+  // the others have finished
+  int nsplit = 1, qchunk = a.n;
+  if (a.causal && !a.qpos && a.colpart) {
+    qchunk = round_up((a.n + kColSplit - 1) / kColSplit, kBQ);
+    nsplit = (a.n + qchunk - 1) / qchunk;
+  }
+  float* sdst = nsplit > 1 ? a.colpart : a.score;
+  const dim3 gs(((a.T + BK - 1) / BK) * a.heads, nsplit), bs(kScoreWaves * 64);
 #define AM_SCORE(C, M)                                                                          \
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, C, M, false>), gs, bs, 0, a.stream,   \
-                     (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, a.score, a.n, a.T, \
+                     (const T*)a.Q, (const T*)a.K, (const float2*)a.rowstat, sdst, a.n, a.T,   \
                      a.group, c2, a.heads, (const int32_t*)nullptr, (const float*)nullptr,     \
-                     (const float*)nullptr, a.n, (const int32_t*)nullptr)
+                     (const float*)nullptr, qchunk, (const int32_t*)nullptr)
   if (a.causal && a.qpos) {   // a query subset with its positions: every tile masked
 #define AM_SCORE_Q(M)                                                                           \
   hipLaunchKernelGGL((colscore_kernel<T, D, kScoreWaves, true, M, false, true>), gs, bs, 0,     \
@@ -687,6 +698,10 @@ static hipError_t launch_targets_t(const TargetsArgs& a) {
 #undef AM_SCORE_Q
   } else if (a.causal) {
     if (a.mode == 0) AM_SCORE(true, 0); else if (a.mode == 1) AM_SCORE(true, 1); else AM_SCORE(true, 2);
+    if (nsplit > 1)
+      hipLaunchKernelGGL(colscore_reduce_kernel, dim3((a.T + 255) / 256, a.heads), dim3(256), 0,
+                         a.stream, (const float*)a.colpart, a.score, a.heads, a.T, nsplit, a.n,
+                         a.mode);
   } else {
     if (a.mode == 0) AM_SCORE(false, 0); else if (a.mode == 1) AM_SCORE(false, 1); else AM_SCORE(false, 2);
   }
@@ -903,7 +918,11 @@ hipError_t launch_cmp_attention(const CmpAttnArgs& a) {
 size_t targets_ws_bytes(int64_t heads, int64_t n, int64_t T, int64_t d, int esize) {
   const size_t vt = align_up((size_t)heads * d * round_up((int)T, kBN) * esize);
   const size_t rs = align_up((size_t)heads * n * sizeof(float2));
-  return vt + rs;
+  return vt + rs + targets_colpart_bytes(heads, T);
+}
+
+size_t targets_colpart_bytes(int64_t heads, int64_t T) {
+  return align_up((size_t)kColSplit * heads * T * sizeof(float));
 }
 
 size_t targets_vt_bytes(int64_t heads, int64_t T, int64_t d, int esize) {
