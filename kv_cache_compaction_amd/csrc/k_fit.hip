@@ -43,7 +43,7 @@ constexpr int kGT = 128;  // Gram tile (keys per side)
 constexpr int kGQ = 32;   // queries per Gram step
 constexpr int kRB = 16;   // NNLS rows per workgroup
 constexpr int kNB = 64;   // Cholesky block
-constexpr int kPow = 24;  // power iterations for the NNLS step size
+constexpr int kPow = 12;  // power iterations for the NNLS step size (L taken 1.25x their estimate)
 
 template <typename T> constexpr int epcf() { return 16 / (int)sizeof(T); }
 
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
     nrm = sqrtf(bsum(y * y));
     x = nrm > 0.f ? y / nrm : 0.f;
   }
-  const float L = 1.1f * nrm + 1e-30f;
+  const float L = 1.25f * nrm + 1e-30f;
 
   float v = lo_i, vp = lo_i, tk = 1.f, dot = 0.f, gm = INFINITY;
   const float thr = s.tol * fmaxf(hsmax, 1e-30f);
@@ -797,7 +797,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
     if (tid == 0) st_dev(s.PN + ((size_t)head * 2 + ((k + 1) & 1)) * ps + part, part2);
     barrier();
   }
-  const float L = 1.1f * sqrtf(head_norm(kPow & 1)) + 1e-30f;
+  const float L = 1.25f * sqrtf(head_norm(kPow & 1)) + 1e-30f;
 
   // accelerated projected gradient; iterate v_k in ring slot k % 3
   float tk = 1.f, gm = INFINITY;
