@@ -15,13 +15,23 @@ constexpr int kAbiVersion = 4;
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// An enum argument or field as the int the caller passed, read through its bytes: in C++ a
+// load of an enum-typed value outside the enumeration's range is undefined, and the C
+// callers of this ABI may pass any int (validation must reject it, not depend on it).
+template <typename E> int ival(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "the ABI's enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 int esize(const am_problem* p) { return p->dtype == AM_BF16 ? 2 : 4; }
 
 am_status check_problem(const am_problem* p) {
   if (!p) return AM_ERR_INVALID_ARG;
   if (p->heads < 1 || p->n < 1 || p->T < 1 || p->d < 1) return AM_ERR_INVALID_ARG;
   if (p->group < 1 || (p->causal != 0 && p->causal != 1)) return AM_ERR_INVALID_ARG;
-  if (p->dtype != AM_F32 && p->dtype != AM_BF16) return AM_ERR_INVALID_ARG;
+  if (ival(p->dtype) != AM_F32 && ival(p->dtype) != AM_BF16) return AM_ERR_INVALID_ARG;
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return AM_ERR_INVALID_ARG;
   if (p->causal && p->n != (int64_t)p->group * p->T) return AM_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return AM_ERR_UNSUPPORTED;
@@ -42,15 +52,15 @@ am_status check_fit_t(int64_t t) { return t > kMaxFitT ? AM_ERR_UNSUPPORTED : AM
 
 am_status check_opts(const am_options* o) {
   if (!o) return AM_ERR_INVALID_ARG;
-  if (o->score < AM_SCORE_RMS || o->score > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
-  if (o->mass != AM_MASS_RELATIVE && o->mass != AM_MASS_ABSOLUTE) return AM_ERR_INVALID_ARG;
+  if (ival(o->score) < AM_SCORE_RMS || ival(o->score) > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (ival(o->mass) != AM_MASS_RELATIVE && ival(o->mass) != AM_MASS_ABSOLUTE) return AM_ERR_INVALID_ARG;
   if (!(o->w_lo >= 0.f) || isnan(o->w_hi) || !(o->w_hi > o->w_lo) || isinf(o->w_lo))
     return AM_ERR_INVALID_ARG;
   if (o->nnls_max_iter < 1 || !(o->nnls_tol >= 0.f) || !(o->ridge_lambda >= 0.f) ||
       !isfinite(o->ridge_lambda))
     return AM_ERR_INVALID_ARG;
-  if (o->beta != AM_BETA_NNLS && o->beta != AM_BETA_REDISTRIBUTE) return AM_ERR_INVALID_ARG;
-  if (o->values != AM_VALUES_FIT && o->values != AM_VALUES_DIRECT) return AM_ERR_INVALID_ARG;
+  if (ival(o->beta) != AM_BETA_NNLS && ival(o->beta) != AM_BETA_REDISTRIBUTE) return AM_ERR_INVALID_ARG;
+  if (ival(o->values) != AM_VALUES_FIT && ival(o->values) != AM_VALUES_DIRECT) return AM_ERR_INVALID_ARG;
   return AM_OK;
 }
 
@@ -70,7 +80,7 @@ am_status check_cache_problem(const am_problem* p) {
   if (!p) return AM_ERR_INVALID_ARG;
   if (p->heads < 1 || p->n < 1 || p->T < 1 || p->d < 1) return AM_ERR_INVALID_ARG;
   if (p->group < 1 || (p->causal != 0 && p->causal != 1)) return AM_ERR_INVALID_ARG;
-  if (p->dtype != AM_F32 && p->dtype != AM_BF16) return AM_ERR_INVALID_ARG;
+  if (ival(p->dtype) != AM_F32 && ival(p->dtype) != AM_BF16) return AM_ERR_INVALID_ARG;
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return AM_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return AM_ERR_UNSUPPORTED;
   if (p->n > (int64_t)1 << 30 || p->T > (int64_t)1 << 30 || p->heads > 65535)
@@ -148,7 +158,7 @@ extern "C" {
 int am_abi_version(void) { return kAbiVersion; }
 
 const char* am_status_str(am_status s) {
-  switch (s) {
+  switch (ival(s)) {
     case AM_OK: return "ok";
     case AM_ERR_INVALID_ARG: return "invalid argument";
     case AM_ERR_UNSUPPORTED: return "unsupported problem";
@@ -171,7 +181,8 @@ void am_default_options(am_options* o) {
   o->values = AM_VALUES_FIT;
 }
 
-size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which) {
+size_t am_workspace_bytes(const am_problem* p, int64_t t, am_call which_arg) {
+  const int which = ival(which_arg);
   if (which == AM_CALL_CACHE_ATTENTION) {
     if (check_cache_problem(p) != AM_OK || t < 0 || t > ((int64_t)1 << 30)) return 0;
     return cache_ws(p, t).total;
@@ -199,7 +210,7 @@ am_status am_targets(const am_problem* p, const void* Q, const void* K, const vo
   am_status st = check_problem(p);
   if (st != AM_OK) return st;
   if (!Q || !K || !lse || (O && !V)) return AM_ERR_INVALID_ARG;
-  if (mode < AM_SCORE_RMS || mode > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (ival(mode) < AM_SCORE_RMS || ival(mode) > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(K) || (V && !al16(V)) || !al16(lse) || (O && !al16(O)) ||
       (key_score && !al16(key_score)) || (ws && !al16(ws)))
     return AM_ERR_INVALID_ARG;
@@ -416,7 +427,7 @@ am_status am_select_two_pass(const am_problem* p, const void* Q, const void* K, 
                              float* lse_short, void* ws, size_t ws_bytes, am_stream_t stream) {
   am_status st = check_two_pass(p, s, t, k_mult);
   if (st != AM_OK) return st;
-  if (mode < AM_SCORE_RMS || mode > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (ival(mode) < AM_SCORE_RMS || ival(mode) > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
   if (!Q || !K || !sub || !idx || !Ck || !lse_short || (V_sel && !V)) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(K) || (V && !al16(V)) || !al16(sub) || !al16(idx) || !al16(Ck) ||
       (V_sel && !al16(V_sel)) || !al16(lse_short) || (ws && !al16(ws)))
@@ -433,7 +444,7 @@ am_status am_compact_two_pass(const am_problem* p, const void* Q, const void* K,
                               float* resid_out, void* ws, size_t ws_bytes, am_stream_t stream) {
   am_status st = check_two_pass(p, s, t, k_mult);
   if (st != AM_OK) return st;
-  if (mode < AM_SCORE_RMS || mode > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
+  if (ival(mode) < AM_SCORE_RMS || ival(mode) > AM_SCORE_MAX) return AM_ERR_INVALID_ARG;
   if (!Q || !K || !V || !sub || !idx || !Ck || !beta || !Cv) return AM_ERR_INVALID_ARG;
   if (!al16(Q) || !al16(K) || !al16(V) || !al16(sub) || !al16(idx) || !al16(Ck) ||
       !al16(beta) || !al16(Cv) || (resid_out && !al16(resid_out)) || (ws && !al16(ws)))

@@ -1550,7 +1550,7 @@ static int gram_chunk(int n, int nch) { return round_up((n + nch - 1) / nch, kGQ
 struct Carve {
   char* base; size_t off;
   template <typename X> X* take(size_t count) {
-    X* p = (X*)(base + off);
+    X* p = base ? (X*)(base + off) : nullptr;   // sizing only: no address
     off = align_up(off + count * sizeof(X));
     return p;
   }

@@ -413,7 +413,7 @@ namespace {
 struct Carve4 {
   char* base; size_t off;
   template <typename X> X* take(size_t count) {
-    X* q = (X*)(base + off);
+    X* q = base ? (X*)(base + off) : nullptr;   // sizing only: no address
     off = align_up(off + count * sizeof(X));
     return q;
   }

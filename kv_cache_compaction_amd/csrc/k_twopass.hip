@@ -57,7 +57,7 @@ struct TwoPassPlan {
 struct Carve2 {
   char* base; size_t off;
   template <typename X> X* take(size_t count) {
-    X* p = (X*)(base + off);
+    X* p = base ? (X*)(base + off) : nullptr;   // sizing only: no address
     off = align_up(off + count * sizeof(X));
     return p;
   }
