@@ -32,17 +32,18 @@ __device__ __forceinline__ void st_dev_i(int* q, int v) {
 }
 
 // Barrier among the workgroups of one head (the m-th completes when the counter reaches
-// m * P): every wave waits until its stores have completed (vmcnt 0), then one thread adds
-// to the counter and polls it with device-scope loads; readers load the slots only after
-// the poll has seen the count. No release/acquire fences: they would write back and
-// invalidate the whole L2 (about 10 us a barrier against 4 us), and the slots are written
-// and read at device scope. A wait longer than kFftSpin polls marks the workgroup as timed
-// out; it then stops.
+// m * P): every wave waits until its stores have completed (vmcnt 0), the workgroup's
+// barrier orders its threads' writes before thread 0's counter add, which has release
+// semantics at device scope; thread 0 polls the counter and ends its wait with an acquire
+// fence at device scope, and the closing barrier orders the other threads' reads after it
+// (the language memory model's release/acquire pattern). The candidate slots are still
+// written and read with device-scope accesses. A wait longer than kFftSpin polls marks the
+// workgroup as timed out; it then stops.
 __device__ __forceinline__ void fft_barrier(int* ctr, int target, int* timed_out) {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0) only
   __syncthreads();
   if (threadIdx.x == 0 && !*timed_out) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(2);
@@ -51,6 +52,7 @@ __device__ __forceinline__ void fft_barrier(int* ctr, int target, int* timed_out
         break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }

@@ -660,23 +660,21 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 }
 
 // Barrier among the workgroups of one head: the m-th completes when the head's counter
-// reaches m * P. Every wave first waits until its own stores have completed (vmcnt 0);
-// then one thread per workgroup adds to the counter and polls it with device-scope loads.
-// FENCED: the add has release semantics and the wait ends with an acquire fence (an L2
-// write-back before, an invalidate after: about 10 us per barrier), so data written and
-// read with ordinary accesses is seen. Otherwise the counter is relaxed (about 4 us): the
-// data that crosses workgroups must then be written with st_dev and read with ld_dev; the
-// vmcnt wait makes those stores complete before the add, and the readers issue their
-// loads only after the poll has seen the count (the barrier's closing __syncthreads).
-// A wait longer than kNnlsSpin polls (seconds) marks the workgroup as timed out, after
-// which it waits no more and stops.
-template <bool FENCED>
+// reaches m * P. Every wave first waits until its own stores have completed (vmcnt 0), and
+// the workgroup's barrier orders all of its threads' writes before thread 0's counter add,
+// which has release semantics at device (agent) scope; thread 0 polls the counter and ends
+// its wait with an acquire fence at device scope, and the closing barrier orders the other
+// threads' later reads after it. This is the language memory model's release/acquire
+// pattern, so the data exchanged through memory is visible whatever caches it passed
+// (on this chip the release writes back the XCD's L2 and the acquire invalidates it; about
+// 10 us per barrier). The exchanged vectors are still written and read with device-scope
+// accesses (st_dev, ld_dev). A wait longer than kNnlsSpin polls (about a second) marks the
+// workgroup as timed out, after which it waits no more and stops.
 __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_out) {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0) only
   __syncthreads();
   if (threadIdx.x == 0 && !*timed_out) {
-    if (FENCED) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    else __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(2);
@@ -685,7 +683,7 @@ __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_ou
         break;
       }
     }
-    if (FENCED) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -714,10 +712,10 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
   const size_t ps = (size_t)s.nblk;   // partial slots per head and parity
   int* bar = s.bar + head;
   int nbar = 0;
-  // after the set-up (one fenced barrier) G's diagonal scaling dinv and hs stay fixed and
-  // are read with ordinary loads; the vectors and partials that change per step go through
-  // st_dev / ld_dev, so the steps' barriers need no fences
-  auto barrier = [&]() { head_barrier<false>(bar, ++nbar * P, &timed_out); };
+  // G's diagonal scaling dinv and hs are written once before the first barrier and read
+  // with ordinary loads after it; the vectors and partials that change per step go through
+  // st_dev / ld_dev
+  auto barrier = [&]() { head_barrier(bar, ++nbar * P, &timed_out); };
   // the head's P partials (float2) staged once, one load per thread
   auto stage = [&](const float2* src) {
     for (int b = tid; b < P; b += 256) {
@@ -751,7 +749,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
     s.PN[((size_t)head * 2 + 0) * ps + part] = part == 0 ? (float)t : 0.f;
     s.P[((size_t)head * 2 + 0) * ps + part] = make_float2(0.f, INFINITY);
   }
-  head_barrier<true>(bar, ++nbar * P, &timed_out);
+  head_barrier(bar, ++nbar * P, &timed_out);
   stage(s.init + (size_t)head * ps);
   float hsmax = 0.f;
   bool bad = false;
