@@ -187,6 +187,8 @@ struct SyrkBuffers {
   float* hpart;   // mass: [h, tpad, npad / 128] partials of M^T b
 };
 bool syrk_path(int t);
+// value fit: number of per-head partials of ||Y||^2 the Y^T rows kernel writes
+int syrk_yy_blocks(int64_t heads, int64_t n, int64_t t, int64_t d);
 // carve the buffers at base + off (base null: sizing only); off advances past them
 SyrkBuffers syrk_carve(char* base, size_t& off, int64_t heads, int64_t n, int64_t t, int64_t d,
                        bool value);
@@ -197,6 +199,7 @@ struct SyrkGramArgs {
   const float* target;   // mass: right-hand side (null = 1)
   const float* Y;        // value: targets [h, n, d]
   SyrkBuffers buf;
+  double* yyp = nullptr;  // value: partials of ||Y||^2 [h, syrk_yy_blocks] (null: not formed)
   float* Gf; float* hv;   // mass outputs: G [h, t, t], M^T b [h, t]
   double* Gd; double* R;  // value outputs: A^T A + lambda I [h, ld, ld], A^T Y [h, ld, d]
   int heads, n, t, d, group, ld;

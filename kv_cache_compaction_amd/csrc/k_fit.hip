@@ -1377,14 +1377,36 @@ __global__ __launch_bounds__(256) void trsm_back_update_kernel(double* R, const 
   }
 }
 
-__global__ __launch_bounds__(256) void store_cv_kernel(const double* R, float* Cv, int t, int ld,
-                                                       int D, int32_t* status) {
+// C_v = float(C); with cpart set, the workgroup also writes the fp64 partial sums of
+// C . R0 and C . C over its 256 entries to cpart[head, block] (for the output residual)
+__global__ __launch_bounds__(256) void store_cv_kernel(const double* R, const double* R0,
+                                                       float* Cv, int t, int ld, int D,
+                                                       int32_t* status, double2* cpart) {
+  __shared__ double r1[256], r2[256];
   const int head = blockIdx.y;
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (long long)t * D) return;
-  const double v = R[(size_t)head * ld * D + e];
-  Cv[(size_t)head * t * D + e] = (float)v;
-  if (!isfinite(v) && status) atomicOr(&status[head], AM_HEAD_NONFINITE_BIT);
+  double cr = 0.0, cc = 0.0;
+  if (e < (long long)t * D) {
+    const double v = R[(size_t)head * ld * D + e];
+    Cv[(size_t)head * t * D + e] = (float)v;
+    if (!isfinite(v) && status) atomicOr(&status[head], AM_HEAD_NONFINITE_BIT);
+    if (cpart) {
+      cr = v * R0[(size_t)head * ld * D + e];
+      cc = v * v;
+    }
+  }
+  if (!cpart) return;   // (uniform over the workgroup)
+  r1[threadIdx.x] = cr;
+  r2[threadIdx.x] = cc;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (threadIdx.x < s2) {
+      r1[threadIdx.x] += r1[threadIdx.x + s2];
+      r2[threadIdx.x] += r2[threadIdx.x + s2];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) cpart[(size_t)head * gridDim.x + blockIdx.x] = make_double2(r1[0], r2[0]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1482,37 +1504,37 @@ __global__ __launch_bounds__(256) void sumsq_part_kernel(const float* __restrict
 
 // The ridge fit's output residual ||A C - Y||^2 / ||Y||^2 without another pass over the
 // queries: with C solving (A^T A + lambda I) C = A^T Y, A^T A C = A^T Y - lambda C, so
-// ||A C - Y||^2 = ||Y||^2 - <C, A^T Y> - lambda ||C||^2. C is the fp64 solution [h, ld, D],
-// R0 the right-hand side A^T Y kept before the solve, yyp the partial sums of ||Y||^2.
-// A rounding-level negative value is reported as 0.
-__global__ __launch_bounds__(256) void resid_gram_kernel(const double* __restrict__ C,
-                                                         const double* __restrict__ R0,
-                                                         const double* __restrict__ yyp,
-                                                         float lambda, int t, int ld, int D,
-                                                         float* __restrict__ out) {
-  __shared__ double r1[256], r2[256];
-  const int head = blockIdx.x;
-  const double* c = C + (size_t)head * ld * D;
-  const double* r = R0 + (size_t)head * ld * D;
-  double a1 = 0.0, a2 = 0.0;
-  for (int e = threadIdx.x; e < t * D; e += 256) {
-    const double x = c[e];
-    a1 += x * r[e];
-    a2 += x * x;
+// ||A C - Y||^2 = ||Y||^2 - <C, A^T Y> - lambda ||C||^2. yyp holds nyy partials of ||Y||^2 per
+// head, cpart ncp partials of (<C, A^T Y>, ||C||^2); each is summed in a fixed order. A
+// rounding-level negative value is reported as 0.
+__global__ __launch_bounds__(256) void resid_values_final_kernel(const double* __restrict__ yyp,
+                                                                 int nyy,
+                                                                 const double2* __restrict__ cpart,
+                                                                 int ncp, float lambda,
+                                                                 float* __restrict__ out) {
+  __shared__ double r0[256], r1[256], r2[256];
+  const int head = blockIdx.x, tid = threadIdx.x;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0;
+  for (int i = tid; i < nyy; i += 256) a0 += yyp[(size_t)head * nyy + i];
+  for (int i = tid; i < ncp; i += 256) {
+    const double2 v = cpart[(size_t)head * ncp + i];
+    a1 += v.x;
+    a2 += v.y;
   }
-  r1[threadIdx.x] = a1;
-  r2[threadIdx.x] = a2;
+  r0[tid] = a0;
+  r1[tid] = a1;
+  r2[tid] = a2;
   __syncthreads();
   for (int s2 = 128; s2 > 0; s2 >>= 1) {
-    if (threadIdx.x < s2) {
-      r1[threadIdx.x] += r1[threadIdx.x + s2];
-      r2[threadIdx.x] += r2[threadIdx.x + s2];
+    if (tid < s2) {
+      r0[tid] += r0[tid + s2];
+      r1[tid] += r1[tid + s2];
+      r2[tid] += r2[tid + s2];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    double yy = 0.0;
-    for (int b = 0; b < kResBlk; ++b) yy += yyp[(size_t)head * kResBlk + b];
+  if (tid == 0) {
+    const double yy = r0[0];
     const double res = yy > 0.0 ? (yy - r1[0] - (double)lambda * r2[0]) / yy : 0.0;
     out[head] = (float)fmax(res, 0.0);
   }
@@ -1601,7 +1623,8 @@ static BetaPlan plan_beta(char* base, int64_t heads, int64_t n, int64_t t, int64
 
 struct ValuePlan {
   float2* rowstat_cmp; double2* part; float* shift2; float* Gpart; float* Rpart; double* A;
-  double* R; double* R0; double* Linv; double* Dg; double* yyp; int2* tstat; int32_t* status;
+  double* R; double* R0; double* Linv; double* Dg; double* yyp; double2* cpart; int2* tstat;
+  int32_t* status; int nyy, ncp;
   SyrkBuffers sy;
   size_t bytes;
 };
@@ -1631,7 +1654,11 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   p.Linv = c.take<double>((size_t)heads * (ld / kNB) * kNB * kNB);
   p.Dg = c.take<double>((size_t)heads * ld);
   p.R0 = c.take<double>((size_t)heads * ld * d);
-  p.yyp = c.take<double>((size_t)heads * kResBlk);
+  // partials of ||Y||^2: one per 64 queries from the Y^T rows kernel, else kResBlk slices
+  p.nyy = syrk_path((int)t) ? syrk_yy_blocks(heads, n, t, d) : kResBlk;
+  p.yyp = c.take<double>((size_t)heads * p.nyy);
+  p.ncp = (int)((t * d + 255) / 256);
+  p.cpart = c.take<double2>((size_t)heads * p.ncp);
   p.tstat = (int2*)c.take<char>(cmp_tstat_bytes(heads, t));
   p.status = c.take<int32_t>(heads);
   p.bytes = c.off;
@@ -1827,7 +1854,7 @@ hipError_t launch_fit_values(const FitArgs& a) {
   if (syrk_path(t)) {
     SyrkGramArgs sa;
     sa.Q = a.Q; sa.Ck = a.Ck; sa.keypos = a.idx; sa.bias = a.beta_in; sa.shift2 = pl.shift2;
-    sa.target = nullptr; sa.Y = a.O; sa.buf = pl.sy;
+    sa.target = nullptr; sa.Y = a.O; sa.buf = pl.sy; sa.yyp = a.out_resid ? pl.yyp : nullptr;
     sa.Gf = nullptr; sa.hv = nullptr; sa.Gd = pl.A; sa.R = pl.R;
     sa.heads = H; sa.n = n; sa.t = t; sa.d = d; sa.group = a.group; sa.ld = ld;
     sa.causal = a.causal; sa.bf16 = a.bf16; sa.value = true;
@@ -1873,13 +1900,16 @@ hipError_t launch_fit_values(const FitArgs& a) {
   for (int kb = nb - 1; kb > 0; --kb)
     hipLaunchKernelGGL(trsm_back_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
                        (const double*)pl.A, (const double*)pl.Linv, ld, d, kb, nb);
-  hipLaunchKernelGGL(store_cv_kernel, dim3(cdiv((long long)t * d, 256), H), dim3(256), 0, st,
-                     (const double*)pl.R, a.Cv, t, ld, d, status);
+  hipLaunchKernelGGL(store_cv_kernel, dim3(pl.ncp, H), dim3(256), 0, st, (const double*)pl.R,
+                     (const double*)pl.R0, a.Cv, t, ld, d, status,
+                     a.out_resid ? pl.cpart : nullptr);
   if (a.out_resid) {
-    hipLaunchKernelGGL(sumsq_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, a.O, pl.yyp,
-                       (long long)n * d);
-    hipLaunchKernelGGL(resid_gram_kernel, dim3(H), dim3(256), 0, st, (const double*)pl.R,
-                       (const double*)pl.R0, (const double*)pl.yyp, a.lambda, t, ld, d,
+    // (on the stored-design path the Y^T rows kernel has already summed ||Y||^2)
+    if (!syrk_path(t))
+      hipLaunchKernelGGL(sumsq_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, a.O, pl.yyp,
+                         (long long)n * d);
+    hipLaunchKernelGGL(resid_values_final_kernel, dim3(H), dim3(256), 0, st,
+                       (const double*)pl.yyp, pl.nyy, (const double2*)pl.cpart, pl.ncp, a.lambda,
                        a.out_resid);
   }
   return hipGetLastError();

@@ -187,21 +187,36 @@ __global__ __launch_bounds__(256) void design_kernel(const DesignParams p) {
 }
 
 // Y^T rows of the value design: X[tpad + c][i] = bf16(Y[i][c]) for c < D and i < n; rows
-// c in [D, 256) and queries past n are zero. One workgroup per 64 queries.
+// c in [D, 256) and queries past n are zero. One workgroup per 64 queries. With yyp set, the
+// workgroup also writes the fp64 sum of squares of its fp32 Y entries to yyp[head, block]
+// (partials of ||Y||^2 for the output residual; fixed order).
 template <int D>
 __global__ __launch_bounds__(256) void design_yt_kernel(const float* __restrict__ Y, bf16* X,
-                                                        int n, int npad, int tpad, int xrows) {
+                                                        int n, int npad, int tpad, int xrows,
+                                                        double* __restrict__ yyp) {
   __shared__ float ys[64][D + 1];
+  __shared__ double red[256];
   const int q0 = blockIdx.x * 64, head = blockIdx.y, tid = threadIdx.x;
   const float* Yh = Y + (size_t)head * n * D;
+  double sq = 0.0;
   for (int e = tid; e < 64 * D / 4; e += 256) {
     const int row = e / (D / 4), col = (e % (D / 4)) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (q0 + row < n) v = *(const float4*)(Yh + (size_t)(q0 + row) * D + col);
+    sq += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
     ys[row][col] = v.x;
     ys[row][col + 1] = v.y;
     ys[row][col + 2] = v.z;
     ys[row][col + 3] = v.w;
+  }
+  if (yyp) {   // (uniform over the workgroup)
+    red[tid] = sq;
+    __syncthreads();
+    for (int s2 = 128; s2 > 0; s2 >>= 1) {
+      if (tid < s2) red[tid] += red[tid + s2];
+      __syncthreads();
+    }
+    if (tid == 0) yyp[(size_t)head * gridDim.x + blockIdx.x] = red[0];
   }
   __syncthreads();
   static_assert(D <= kSyYRows, "Y^T rows exceed the part of the block the products read");
@@ -529,6 +544,10 @@ SyrkShape syrk_shape(int heads, int n, int t, int d, bool value) {
 
 bool syrk_path(int t) { return t > kSyrkMinT; }
 
+int syrk_yy_blocks(int64_t heads, int64_t n, int64_t t, int64_t d) {
+  return syrk_shape((int)heads, (int)n, (int)t, (int)d, true).npad / 64;
+}
+
 SyrkBuffers syrk_carve(char* base, size_t& off, int64_t heads, int64_t n, int64_t t, int64_t d,
                        bool value) {
   const SyrkShape s = syrk_shape((int)heads, (int)n, (int)t, (int)d, value);
@@ -572,10 +591,10 @@ hipError_t launch_syrk_gram(const SyrkGramArgs& a) {
     const dim3 g(s.npad / 64, H);
     if (d == 128)
       hipLaunchKernelGGL((design_yt_kernel<128>), g, dim3(256), 0, st, a.Y, (bf16*)a.buf.X, n, s.npad,
-                         s.tpad, s.xrows);
+                         s.tpad, s.xrows, a.yyp);
     else
       hipLaunchKernelGGL((design_yt_kernel<64>), g, dim3(256), 0, st, a.Y, (bf16*)a.buf.X, n, s.npad,
-                         s.tpad, s.xrows);
+                         s.tpad, s.xrows, a.yyp);
   }
   SyrkParams sp;
   sp.X = (const bf16*)a.buf.X; sp.part = a.buf.part; sp.keypos = a.keypos;
