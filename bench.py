@@ -213,8 +213,9 @@ def main():
     idx, Ck, _ = amc.select_keys(sc, dK, w.t)
     ms_beta = time_calls(torch, lambda: amc.fit_beta_nnls(dQ, Ck, idx, lse, causal=w.causal,
                                                           group=w.group, options=opts, T=w.T), 2)
-    beta, _, _, _ = amc.fit_beta_nnls(dQ, Ck, idx, lse, causal=w.causal, group=w.group,
-                                      options=opts, T=w.T)
+    beta, _, _, _, nnls_kkt, nnls_steps = amc.fit_beta_nnls(dQ, Ck, idx, lse, causal=w.causal,
+                                                            group=w.group, options=opts, T=w.T,
+                                                            diagnostics=True)
     ms_values = time_calls(torch, lambda: amc.fit_values_ols(dQ, Ck, idx, beta, Og,
                                                              causal=w.causal, group=w.group,
                                                              ridge_lambda=w.ridge_lambda, T=w.T), 2)
@@ -287,6 +288,13 @@ def main():
         cpu = cpu_baseline(w, Q, K, V)
         cpu["gpu_over_oracle"] = (pairs / (ms * 1e-3)) / cpu["value"]
 
+    def per_head(x, digits):
+        v = x.detach().double().cpu().numpy()
+        f = (lambda a: int(a)) if digits == 0 else (lambda a: float(f"{a:.{digits}g}"))
+        if v.size <= 16:
+            return [f(a) for a in v.tolist()]
+        return {"min": f(v.min()), "mean": float(f"{v.mean():.4g}"), "max": f(v.max())}
+
     out = {
         "metric": METRIC,
         "value": pairs / (ms * 1e-3),
@@ -310,6 +318,14 @@ def main():
                       "fit_beta": ms_beta, "fit_values": ms_values},
         "score_passes": {"pairs_per_s": pairs / (ms_targets * 1e-3),
                          "tflops": score_tflops, "mfma_frac": score_tflops / peak},
+        # from the library's own outputs on this workload: the fits' relative residuals and
+        # status, and the NNLS's relative KKT residual and step count (per head up to 16
+        # heads, else min / mean / max)
+        "fits": {"mass_resid": per_head(full["resid"][0], 7),
+                 "out_resid": per_head(full["resid"][1], 7),
+                 "status_nonzero": int((full["status"] != 0).sum().item()),
+                 "nnls_kkt_rel": per_head(nnls_kkt, 3),
+                 "nnls_steps": per_head(nnls_steps, 0)},
         "next": {
             "fast_pipeline": {"ms_per_step": ms_fast, "pairs_per_s": pairs / (ms_fast * 1e-3),
                               "options": "beta=redistribute, values=direct",
