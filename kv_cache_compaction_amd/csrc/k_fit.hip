@@ -65,6 +65,9 @@ struct GramParams {
   const float* Y;       // values: targets [h, n, D]
   float* Gpart;         // [h, nch, ntri, 128, 128]
   float* Vpart;         // mass: [h, nch, tpad]; values: [h, nch, tpad, D]
+  // values without the causal mask: tile 0, which stages every target row of its chunk,
+  // also writes the chunk's fp64 sum of squares of Y here [h, nch] (null: not formed)
+  double* yyp = nullptr;
   int n, t, tpad, group, ntri, nch, chunk;
   int causal;
   float c2;
@@ -96,8 +99,13 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
   __shared__ __align__(16) bf16x8 mb[2][8][QH][2][64];
   __shared__ __align__(16) bf16 yts[VALUE ? 2 : 1][VALUE ? D * YP : 8];
   __shared__ float hl[8][32];
+  __shared__ double yyw[8];
 
   const int tri = blockIdx.x, chunk = blockIdx.y, head = blockIdx.z;
+  // (uniform over the workgroup; tile 0 is diagonal and, without the mask, starts its chunk
+  // at the chunk's first query)
+  const bool want_yy = VALUE && p.yyp != nullptr && tri == 0 && !p.causal;
+  double yy = 0.0;
   int ta, tb;
   tri_index(tri, ta, tb);
   const bool diag = ta == tb;
@@ -182,6 +190,10 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
         if (YCH % NT == 0 || c < YCH) {
           const int row = c / (D / 4), col = (c % (D / 4)) * 4;
           yreg[i] = *(const float4*)(Yh + (size_t)min(q0 + row, n - 1) * D + col);
+          if (want_yy && q0 + row < qb) {
+            const float4 v = yreg[i];
+            yy += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+          }
         }
       }
     }
@@ -351,6 +363,18 @@ __global__ __launch_bounds__(512, 2) void gram_kernel(const GramParams p) {
             p.Vpart[(((size_t)head * p.nch + chunk) * p.tpad + row) * D + (gy0 + i) * 32 + r] =
                 racc[i][j];
           }
+    }
+  }
+  if (want_yy) {   // fixed order: lanes by xor tree, then the eight waves in turn
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) yy += __shfl_xor(yy, o, 64);
+    if (lane == 0) yyw[wave] = yy;
+    __syncthreads();
+    if (tid == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) tot += yyw[w];
+      p.yyp[(size_t)head * p.nch + chunk] = tot;
     }
   }
 }
@@ -1655,7 +1679,8 @@ static ValuePlan plan_values(char* base, int64_t heads, int64_t n, int64_t t, in
   p.Dg = c.take<double>((size_t)heads * ld);
   p.R0 = c.take<double>((size_t)heads * ld * d);
   // partials of ||Y||^2: one per 64 queries from the Y^T rows kernel, else kResBlk slices
-  p.nyy = syrk_path((int)t) ? syrk_yy_blocks(heads, n, t, d) : kResBlk;
+  p.nyy = syrk_path((int)t) ? syrk_yy_blocks(heads, n, t, d)
+                            : std::max(kResBlk, gram_nch((int)heads, (int)n, (int)t));
   p.yyp = c.take<double>((size_t)heads * p.nyy);
   p.ncp = (int)((t * d + 255) / 256);
   p.cpart = c.take<double2>((size_t)heads * p.ncp);
@@ -1868,6 +1893,7 @@ hipError_t launch_fit_values(const FitArgs& a) {
     gp.Gpart = pl.Gpart; gp.Vpart = pl.Rpart;
     gp.n = n; gp.t = t; gp.tpad = tpad; gp.group = a.group; gp.ntri = ntri; gp.nch = nch;
     gp.chunk = gram_chunk(n, nch); gp.causal = a.causal; gp.c2 = a.scale * kLog2e;
+    gp.yyp = (a.out_resid && !a.causal) ? pl.yyp : nullptr;
     launch_gram_any(gp, H, d, a.bf16, true, st);
     hipLaunchKernelGGL((gram_reduce_kernel<double>), dim3(cdiv((long long)ld * ld, 256), H),
                        dim3(256), 0, st, pl.Gpart, pl.A, t, ld, ntri, nch, a.lambda);
@@ -1904,12 +1930,21 @@ hipError_t launch_fit_values(const FitArgs& a) {
                      (const double*)pl.R0, a.Cv, t, ld, d, status,
                      a.out_resid ? pl.cpart : nullptr);
   if (a.out_resid) {
-    // (on the stored-design path the Y^T rows kernel has already summed ||Y||^2)
-    if (!syrk_path(t))
-      hipLaunchKernelGGL(sumsq_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, a.O, pl.yyp,
-                         (long long)n * d);
+    // ||Y||^2: on the stored-design path the Y^T rows kernel has summed it (one partial per
+    // 64 queries), without the causal mask the Gram kernel's tile 0 (one per chunk); else a
+    // pass over Y (kResBlk slices)
+    int nyy = pl.nyy;
+    if (!syrk_path(t)) {
+      if (a.causal) {
+        hipLaunchKernelGGL(sumsq_part_kernel, dim3(kResBlk, H), dim3(256), 0, st, a.O, pl.yyp,
+                           (long long)n * d);
+        nyy = kResBlk;
+      } else {
+        nyy = nch;
+      }
+    }
     hipLaunchKernelGGL(resid_values_final_kernel, dim3(H), dim3(256), 0, st,
-                       (const double*)pl.yyp, pl.nyy, (const double2*)pl.cpart, pl.ncp, a.lambda,
+                       (const double*)pl.yyp, nyy, (const double2*)pl.cpart, pl.ncp, a.lambda,
                        a.out_resid);
   }
   return hipGetLastError();
