@@ -106,6 +106,22 @@ struct FlashParams {
 // d = 128, for LDS) in a ring of four LDS buffers with one barrier per tile; the running
 // max is rescaled lazily.
 constexpr int kFlashWaves = 8;
+
+// Workgroup b -> (head, item) for a grid of heads x nper workgroups. Linear id b runs on
+// XCD b % 8; when the heads split evenly over the eight XCDs, each XCD takes whole heads
+// (head = 8 j + b % 8) and walks one head's items before the next, so the workgroups that
+// run together on an XCD share that head's K, V^T or Q tiles in its L2. Otherwise heads
+// are interleaved (head = b % heads). Items run in ascending order per head either way.
+__device__ __forceinline__ void head_major(int b, int heads, int nper, int& head, int& item) {
+  if ((heads & 7) == 0) {
+    const int slot = b >> 3;
+    head = (slot / nper) * 8 + (b & 7);
+    item = slot % nper;
+  } else {
+    head = b % heads;
+    item = b / heads;
+  }
+}
 template <typename T, int D> constexpr int flash_bn() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
 constexpr float kLazyTau = 8.f;  // rescale only when the row max grows by more than 2^8
 
@@ -133,8 +149,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void flash_fwd_kernel(const FlashPar
 
   const int n = p.n, Tk = p.Tk, group = p.group;
   const int b = blockIdx.x;
-  const int head = b % p.heads;
-  const int tile = p.n_qtiles - 1 - b / p.heads;  // late (longest under the causal mask) first
+  int head, item;
+  head_major(b, p.heads, p.n_qtiles, head, item);
+  const int tile = p.n_qtiles - 1 - item;  // late (longest under the causal mask) first
   const int q0 = tile * BM;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -459,8 +476,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void colscore_kernel(
   __shared__ int qps[QPOS ? 2 : 1][QPOS ? kBQ : 1];   // query positions of a subset
 
   const int b = blockIdx.x;
-  const int head = b % heads;
-  const int k0 = (b / heads) * BK;  // key block 0 (most queries under the causal mask) first
+  int head, kblk;
+  head_major(b, heads, gridDim.x / heads, head, kblk);
+  const int k0 = kblk * BK;  // key block 0 (most queries under the causal mask) first
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const T* Qh = Q + (size_t)head * n * D;
