@@ -714,7 +714,7 @@ __device__ __forceinline__ void head_barrier(int* ctr, int target, int* timed_ou
 
 __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int Hb, int P,
                                                         int max_iter, int nlds, NnlsOut o) {
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   __shared__ float red[4];
   __shared__ float2 pst[256];   // staged partials of the head's workgroups (P <= 256)
   __shared__ int timed_out;
@@ -730,7 +730,38 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
   const float* G = s.G + (size_t)head * t * t;
   // the first nlds of this workgroup's rows of G are held in LDS, the others read each step
   for (int e = tid; e < min(nlds, r1 - r0) * t; e += 256) Gs[e] = G[(size_t)r0 * t + e];
-  auto grow = [&](int i) { return i - r0 < nlds ? Gs + (size_t)(i - r0) * t : G + (size_t)i * t; };
+  // G_i . xs for this workgroup's row i, one wave (the sum over lanes by xor tree). With t a
+  // multiple of 4, 16-byte reads: rows in LDS directly, rows in memory four reads in flight
+  // per lane (latency-bound otherwise: a row is 64 dependent steps of one read each).
+  auto row_dot = [&](int i) -> float {
+    float acc = 0.f;
+    if ((t & 3) == 0) {
+      const int t4 = t >> 2;
+      const float4* x4 = (const float4*)xs;
+      auto dot4 = [](const float4 a, const float4 c) {
+        return a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
+      };
+      if (i - r0 < nlds) {
+        const float4* g4 = (const float4*)(Gs + (size_t)(i - r0) * t);
+        for (int j = lane; j < t4; j += 64) acc += dot4(g4[j], x4[j]);
+      } else {
+        const float4* g4 = (const float4*)(G + (size_t)i * t);
+        int j = lane;
+        for (; j + 192 < t4; j += 256) {
+          const float4 a0 = g4[j], a1 = g4[j + 64], a2 = g4[j + 128], a3 = g4[j + 192];
+          acc += dot4(a0, x4[j]) + dot4(a1, x4[j + 64]) + dot4(a2, x4[j + 128]) +
+                 dot4(a3, x4[j + 192]);
+        }
+        for (; j < t4; j += 64) acc += dot4(g4[j], x4[j]);
+      }
+    } else {
+      const float* gr = i - r0 < nlds ? Gs + (size_t)(i - r0) * t : G + (size_t)i * t;
+      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
+    }
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, 64);
+    return acc;
+  };
   float* dinv = s.dinv + (size_t)head * t;
   float* hs = s.hs + (size_t)head * t;
   const size_t ps = (size_t)s.nblk;   // partial slots per head and parity
@@ -804,11 +835,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
     __syncthreads();
     float part2 = 0.f;
     for (int i = r0 + wave; i < r1; i += 4) {
-      const float* gr = grow(i);
-      float acc = 0.f;
-      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const float acc = row_dot(i);
       const float y = acc * dinv[i];
       if (lane == 0) {
         st_dev(xout + i, y);
@@ -853,11 +880,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
     __syncthreads();
     float pdot = 0.f, pgm = 0.f;
     for (int i = r0 + wave; i < r1; i += 4) {
-      const float* gr = grow(i);
-      float acc = 0.f;
-      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const float acc = row_dot(i);
       const float di = dinv[i];
       const float vc = vr[i - r0], y = yr[i - r0];
       const float g = acc * di - hs[i];
@@ -908,11 +931,7 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
   if (o.kkt) {   // KKT residual of the returned w on the system solved, own rows
     float pv = 0.f, ph = 0.f;
     for (int i = r0 + wave; i < r1; i += 4) {
-      const float* gr = grow(i);
-      float acc = 0.f;
-      for (int j = lane; j < t; j += 64) acc += gr[j] * xs[j];
-#pragma unroll
-      for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, 64);
+      const float acc = row_dot(i);
       const float hi = s.hv[(size_t)head * t + i];
       if (lane == 0) {
         pv = fmaxf(pv, kkt_violation(acc - hi, xs[i], s.lo, s.hi));
