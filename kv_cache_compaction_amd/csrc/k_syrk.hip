@@ -7,9 +7,11 @@
 // equations with A_i the biased compacted softmax of "Latent Compaction with Test-Time
 // Training", §3.1 Eq. 2-3): the normal-equation matrices M^T M, M^T b, A^T A and A^T Y.
 //
-// Design kernel. X [h, xrows, npad] bf16, key-major (one row per selected key, the queries
-// of a row contiguous): X[j][i] = 2^(s_ij scale log2 e + bias_j - shift_i) under the causal
-// mask of the key's original position, 0 for padded queries. A workgroup forms 128 queries
+// Design kernel. X [h, xrows / 256, npad / 32, 256, 32] bf16: one row per selected key, in
+// blocks of 256 rows, each block stored as 32-query stages of 256 rows x 32 queries (16 KB,
+// contiguous), so a stage of a block, the unit the Gram product loads, is one run of memory:
+// X[j][i] = 2^(s_ij scale log2 e + bias_j - shift_i) under the causal mask of the key's
+// original position, 0 for padded queries. A workgroup forms 128 queries
 // x 256 keys: its query tile sits in LDS (rows in the kperm order) and every wave keeps the
 // C_k fragments of its 64 keys in registers, so a lane's share of a 32 x 32 score block is
 // 8 + 8 consecutive queries of one key: two 16-byte stores per block. The mass variant also
@@ -40,6 +42,12 @@ constexpr int kDsK = 256;   // keys per design workgroup (4 waves x 64)
 // Rows of the Y^T block that are written and multiplied (d <= 128 of them hold Y^T, the rest
 // of these zeros); its other 128 rows are neither written nor read.
 constexpr int kSyYRows = 128;
+
+// Element (row R of a 256-row block, query q) within that block of the stored design: the
+// stage q / 32 is 256 rows x 32 queries, row-major.
+__device__ __forceinline__ size_t xoff(int R, int q) {
+  return (size_t)(q >> 5) * (kSyT * kSyK) + (size_t)R * kSyK + (q & 31);
+}
 
 __device__ __forceinline__ void sy_tri(int k, int& a, int& b) {
   int x = (int)((sqrtf(8.f * (float)k + 1.f) - 1.f) * 0.5f);
@@ -172,7 +180,8 @@ __global__ __launch_bounds__(256) void design_kernel(const DesignParams p) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) hsum[kb] += v[j] * tg[j];
       }
-      bf16* row = Xh + (size_t)key[kb] * p.npad + qbase;
+      // key j: block j / 256 (its base is j / 256 * 256 rows of npad), row j % 256
+      bf16* row = Xh + (size_t)(key[kb] / kSyT) * kSyT * p.npad + xoff(key[kb] % kSyT, qbase);
       *(bf16x8*)row = AM_PACK8(bf16, v, 0);
       *(bf16x8*)(row + 16) = AM_PACK8(bf16, v, 8);
     }
@@ -220,14 +229,14 @@ __global__ __launch_bounds__(256) void design_yt_kernel(const float* __restrict_
   }
   __syncthreads();
   static_assert(D <= kSyYRows, "Y^T rows exceed the part of the block the products read");
-  bf16* Xh = X + ((size_t)head * xrows + tpad) * npad + q0;
+  bf16* Xh = X + ((size_t)head * xrows + tpad) * npad;   // the Y^T block
   // kSyYRows rows x 64 queries, 8 queries (16 bytes) per store
   for (int e = tid; e < kSyYRows * 8; e += 256) {
     const int c = e / 8, qq = (e % 8) * 8;
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = c < D ? ys[qq + i][c] : 0.f;
-    *(bf16x8*)(Xh + (size_t)c * npad + qq) = AM_PACK8(bf16, v, 0);
+    *(bf16x8*)(Xh + xoff(c, q0 + qq)) = AM_PACK8(bf16, v, 0);
   }
 }
 
@@ -311,7 +320,7 @@ __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p)
   for (int i = 0; i < kSyLoads; ++i) {
     const int R = 16 * (kSyLoads * wave + i) + (lane >> 2);
     const int c = (lane & 3) ^ ((R >> 2) & 3);
-    soff[i] = (size_t)R * p.npad + kbeg + c * 8;
+    soff[i] = xoff(R, kbeg) + c * 8;   // (kbeg is a stage boundary)
   }
   // fragment reads: row base + 32 i + r, logical chunk 2 kk + hh
   const int swz = (r >> 2) & 3;
@@ -328,7 +337,8 @@ __global__ __launch_bounds__(kSyWaves * 64) void syrk_kernel(const SyrkParams p)
   auto run = [&](auto diag_tag) __attribute__((always_inline)) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     auto issue = [&](int st) {
-      const int buf = st % kSyS, k = st * kSyK;
+      const int buf = st % kSyS;
+      const size_t k = (size_t)st * (kSyT * kSyK);   // next stage: the next 16 KB run
 #pragma unroll
       for (int i = 0; i < kSyLoads; ++i) {
         const int R0 = 16 * (kSyLoads * wave + i);
