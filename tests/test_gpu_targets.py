@@ -35,6 +35,8 @@ CASES = [
     (Workload("ragged_f32_d128", 1, 128, 200, 200, 7, "f32", True, 1), [0]),
     (Workload("tiny", 1, 64, 1, 1, 1, "bf16", False, 1), [0]),
     (Workload("tiny_causal", 1, 128, 3, 12, 2, "f32", True, 4), [0]),
+    # a head count that splits evenly over the eight XCDs (whole heads per XCD), every head
+    (Workload("heads16_causal_g2", 16, 64, 300, 600, 20, "bf16", True, 2), list(range(16))),
 ]
 
 
