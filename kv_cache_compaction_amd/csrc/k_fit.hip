@@ -1420,6 +1420,105 @@ __global__ __launch_bounds__(256) void trsm_back_update_kernel(double* R, const 
   }
 }
 
+// The whole backward solve in one launch when the factor has at most kBsMaxLd rows: each
+// workgroup owns kBsW columns of one head's right-hand side, holds them in LDS from the
+// first block step to the last and runs every step itself, so no two workgroups share
+// data. Step kb: Z_kb <- Linv_kk^T Z_kb (one entry per thread, Linv_kk staged in LDS and
+// fetched one step ahead), then Z_j -= sum_b L(kb*64 + b, j) Z_kb(b) for every row j < 64 kb
+// (one row per thread; the row's column of the block row of L streamed from memory,
+// coalesced along j, in four batches of 16 loads, each batch issued before the previous
+// one's products). The broadcast reads of Z_kb from LDS bound the row loop, hence few
+// columns per workgroup and many workgroups. The sums run over b in the same order, and
+// each row's updates land in the same order, as in the per-step launches.
+constexpr int kBsW = 4;
+constexpr int kBsMaxLd = 1024;
+__global__ __launch_bounds__(512) void trsm_back_cols_kernel(double* R, const double* A,
+                                                             const double* Linv, int ld, int D,
+                                                             int nb, int H) {
+  __shared__ __align__(16) double zs[kBsMaxLd * kBsW];
+  __shared__ __align__(16) double li[kNB * kNB];
+  __shared__ __align__(16) double xs[kNB * kBsW];
+  const int head = blockIdx.x % H, c0 = (blockIdx.x / H) * kBsW;
+  const int tid = threadIdx.x;
+  double* Rh = R + (size_t)head * ld * D + c0;
+  const double* Ah = A + (size_t)head * ld * ld;
+  for (int e = tid; e < ld * (kBsW / 2); e += 512) {
+    const int row = e / (kBsW / 2), q = e % (kBsW / 2);
+    *(double2*)&zs[row * kBsW + 2 * q] = *(const double2*)&Rh[(size_t)row * D + 2 * q];
+  }
+  const double2* Lh = (const double2*)(Linv + (size_t)head * nb * kNB * kNB);
+  constexpr int kLi2 = kNB * kNB / 2;   // 16-byte pieces per Linv block
+  double2 lin0 = Lh[(size_t)(nb - 1) * kLi2 + tid], lin1 = Lh[(size_t)(nb - 1) * kLi2 + tid + 512];
+  double2 lin2 = Lh[(size_t)(nb - 1) * kLi2 + tid + 1024];
+  double2 lin3 = Lh[(size_t)(nb - 1) * kLi2 + tid + 1536];
+  for (int kb = nb - 1; kb >= 0; --kb) {
+    ((double2*)li)[tid] = lin0;
+    ((double2*)li)[tid + 512] = lin1;
+    ((double2*)li)[tid + 1024] = lin2;
+    ((double2*)li)[tid + 1536] = lin3;
+    __syncthreads();   // (and the previous step's row updates are complete)
+    if (tid < kNB * kBsW) {
+      const int a = tid / kBsW, c = tid % kBsW;
+      double acc = 0.0;
+#pragma unroll 16
+      for (int b = 0; b < kNB; ++b) acc += li[b * kNB + a] * zs[(kb * kNB + b) * kBsW + c];
+      xs[a * kBsW + c] = acc;
+    }
+    __syncthreads();   // every read of Z_kb is done; X is complete
+    if (tid < kNB * kBsW) zs[(kb * kNB + tid / kBsW) * kBsW + tid % kBsW] = xs[tid];
+    if (kb > 0) {   // (after the barrier, whose fence would wait for the loads)
+      const double2* Lk = Lh + (size_t)(kb - 1) * kLi2;
+      lin0 = Lk[tid];
+      lin1 = Lk[tid + 512];
+      lin2 = Lk[tid + 1024];
+      lin3 = Lk[tid + 1536];
+    }
+    const double* P = Ah + (size_t)kb * kNB * ld;
+    // (at most two rows per thread: ld <= 1024; unrolled, so no per-row address streams)
+#pragma unroll
+    for (int rr = 0; rr < kBsMaxLd / 512; ++rr) {
+      const int j = tid + 512 * rr;
+      if (j >= kb * kNB) break;
+      double acc[kBsW];
+#pragma unroll
+      for (int c = 0; c < kBsW; ++c) acc[c] = 0.0;
+      double la[16], lb[16];
+#define AM_BS_LOAD(buf, b0)                                                  \
+  _Pragma("unroll") for (int i = 0; i < 16; ++i) buf[i] = (P + (size_t)((b0) + i) * ld)[(unsigned)j]; \
+  __builtin_amdgcn_sched_barrier(0);
+#define AM_BS_FMA(buf, b0)                                                   \
+  _Pragma("unroll") for (int i = 0; i < 16; ++i) {                           \
+    _Pragma("unroll") for (int q = 0; q < kBsW / 2; ++q) {                   \
+      const double2 v = *(const double2*)&xs[((b0) + i) * kBsW + 2 * q];     \
+      acc[2 * q] += buf[i] * v.x;                                            \
+      acc[2 * q + 1] += buf[i] * v.y;                                        \
+    }                                                                        \
+  }                                                                          \
+  __builtin_amdgcn_sched_barrier(0);
+      AM_BS_LOAD(la, 0)
+      AM_BS_LOAD(lb, 16)
+      AM_BS_FMA(la, 0)
+      AM_BS_LOAD(la, 32)
+      AM_BS_FMA(lb, 16)
+      AM_BS_LOAD(lb, 48)
+      AM_BS_FMA(la, 32)
+      AM_BS_FMA(lb, 48)
+#undef AM_BS_LOAD
+#undef AM_BS_FMA
+#pragma unroll
+      for (int c = 0; c < kBsW; ++c) zs[j * kBsW + c] -= acc[c];
+    }
+    // keeps the next step's store of the prefetched Linv below the row updates (hoisted
+    // above them, it would wait for the prefetch at once)
+    asm volatile("" ::: "memory");
+  }
+  __syncthreads();
+  for (int e = tid; e < ld * (kBsW / 2); e += 512) {
+    const int row = e / (kBsW / 2), q = e % (kBsW / 2);
+    *(double2*)&Rh[(size_t)row * D + 2 * q] = *(const double2*)&zs[row * kBsW + 2 * q];
+  }
+}
+
 // C_v = float(C); with cpart set, the workgroup also writes the fp64 partial sums of
 // C . R0 and C . C over its 256 entries to cpart[head, block] (for the output residual)
 __global__ __launch_bounds__(256) void store_cv_kernel(const double* R, const double* R0,
@@ -1939,12 +2038,19 @@ hipError_t launch_fit_values(const FitArgs& a) {
                          0, st, pl.A, pl.R, pl.Linv, (const double*)pl.Dg, status, ld, d, kb,
                          nb);
   }
-  // (each update launch also forms the next block row's diagonal product)
-  hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
-                     (const double*)pl.Linv, ld, d, nb - 1, nb);
-  for (int kb = nb - 1; kb > 0; --kb)
-    hipLaunchKernelGGL(trsm_back_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
-                       (const double*)pl.A, (const double*)pl.Linv, ld, d, kb, nb);
+  if (ld <= kBsMaxLd && d % kBsW == 0) {
+    // one launch: each workgroup runs every step for its columns
+    hipLaunchKernelGGL(trsm_back_cols_kernel, dim3(H * (d / kBsW)), dim3(512), 0, st, pl.R,
+                       (const double*)pl.A, (const double*)pl.Linv, ld, d, nb, H);
+  } else {
+    // one launch per step (each update launch also forms the next block row's diagonal
+    // product)
+    hipLaunchKernelGGL(trsm_back_diag_kernel, dim3(d / 32, H), dim3(256), 0, st, pl.R,
+                       (const double*)pl.Linv, ld, d, nb - 1, nb);
+    for (int kb = nb - 1; kb > 0; --kb)
+      hipLaunchKernelGGL(trsm_back_update_kernel, dim3(kb, d / 32, H), dim3(256), 0, st, pl.R,
+                         (const double*)pl.A, (const double*)pl.Linv, ld, d, kb, nb);
+  }
   hipLaunchKernelGGL(store_cv_kernel, dim3(pl.ncp, H), dim3(256), 0, st, (const double*)pl.R,
                      (const double*)pl.R0, a.Cv, t, ld, d, status,
                      a.out_resid ? pl.cpart : nullptr);
