@@ -17,7 +17,8 @@
 // floating-point atomics, bit-reproducible.
 //
 // NNLS. Accelerated projected gradient with Jacobi scaling (v = sqrt(diag G) * w),
-// step 1/L with L from power iteration, momentum restarted when the step turns back
+// step 1/L with L an upper bound on the largest eigenvalue of the scaled G (below),
+// momentum restarted when the step turns back
 // (gradient-mapping test), stopped on the scaled gradient-mapping norm. t <= 256: one
 // workgroup per head. Larger t: P workgroups per head, all resident at once (the launch
 // is refused otherwise), each owning a slice of rows (of G too when they fit in LDS),
@@ -43,7 +44,16 @@ constexpr int kGT = 128;  // Gram tile (keys per side)
 constexpr int kGQ = 32;   // queries per Gram step
 constexpr int kRB = 16;   // NNLS rows per workgroup
 constexpr int kNB = 64;   // Cholesky block
-constexpr int kPow = 12;  // power iterations for the NNLS step size (L taken 1.25x their estimate)
+// NNLS step size. G = M^T M has no negative entry (M >= 0), nor has A = D^-1 G D^-1, so for
+// any positive vector u the largest ratio (A u)_i / u_i bounds A's largest eigenvalue from
+// above (Collatz-Wielandt). u starts at all ones and takes kCw - 1 steps u <- A u + kCwShift u
+// (the small shift keeps u positive where A has an empty row) toward the dominant
+// eigenvector; the bound from the last product, times 1 + 2^-10 for rounding, is L. Three
+// products bring it within about 1.1x of the eigenvalue on the mass designs (1.47x with
+// one), so every step 1/L is safe with no estimate to pad.
+constexpr int kCw = 3;
+constexpr float kCwShift = 0x1p-10f;
+constexpr float kCwPad = 1.f + 0x1p-10f;
 
 template <typename T> constexpr int epcf() { return 16 / (int)sizeof(T); }
 
@@ -489,8 +499,8 @@ struct NnlsState {
   float* dinv;      // [h, t]   1 / sqrt(G_jj) (0 for empty columns)
   float* hs;        // [h, t]   scaled right-hand side
   float* V;         // [h, 3, t] iterates (ring of three)
-  float* X;         // [h, 2, t] power-iteration vectors
-  float* PN;        // [h, 2, nblk] power-iteration partial squared norms
+  float* X;         // [h, 2, t] step-size iteration vectors
+  float* PN;        // [h, 2, nblk] step-size partials (largest ratio of a workgroup's rows)
   float2* P;        // [h, 2, nblk] (restart dot, gradient-mapping max) partials
   float2* init;     // [h, nblk] (max |hs|, non-finite flag) partials
   float2* kktp;     // [h, nblk] (largest KKT violation, largest |h|) partials, zero-filled
@@ -538,7 +548,7 @@ __device__ __forceinline__ float kkt_violation(float g, float w, float lo, float
 }
 
 // One workgroup per head for t <= kNnlsSingle (thread i owns row i): Jacobi scaling
-// v = sqrt(diag G) w, step 1/L with L from power iteration, momentum restarted when the
+// v = sqrt(diag G) w, step 1/L with L the Collatz-Wielandt bound, momentum restarted when the
 // step turns back, stop on the scaled gradient-mapping norm; all vectors in LDS. By
 // symmetry thread i forms (G z)_i as sum_j G[j][i] z_j, so every step of j reads one row of
 // G coalesced; G itself is staged in LDS when it fits (t <= 128), otherwise read from L2.
@@ -600,18 +610,17 @@ __global__ __launch_bounds__(kNnlsSingle) void nnls_single_kernel(NnlsState s, i
   const float lo_i = di > 0.f ? s.lo / di : 0.f;
   const float hi_i = di > 0.f ? (isinf(s.hi) ? INFINITY : s.hi / di) : 0.f;
 
-  // power iteration for L = lambda_max(D^-1 G D^-1)
-  float x = own ? rsqrtf((float)t) : 0.f;
-  float nrm = 1.f;
-  for (int k = 0; k < kPow; ++k) {
+  // L: the Collatz-Wielandt bound on lambda_max(D^-1 G D^-1) (kCw)
+  float u = own ? 1.f : 0.f, ratio = 0.f;
+  for (int k = 0; k < kCw; ++k) {
     __syncthreads();
-    zs[i] = x * di;
+    zs[i] = u * di;
     __syncthreads();
     const float y = row(di);
-    nrm = sqrtf(bsum(y * y));
-    x = nrm > 0.f ? y / nrm : 0.f;
+    if (k + 1 < kCw) u = y + kCwShift * u;
+    else ratio = u > 0.f ? y / u : 0.f;
   }
-  const float L = 1.25f * nrm + 1e-30f;
+  const float L = kCwPad * bmax2(ratio) + 1e-30f;
 
   float v = lo_i, vp = lo_i, tk = 1.f, dot = 0.f, gm = INFINITY;
   const float thr = s.tol * fmaxf(hsmax, 1e-30f);
@@ -801,7 +810,6 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
   if (tid == 0) {
     if (part == 0 && o.status) o.status[head] = 0;   // parts OR their flags in at the end
     s.init[(size_t)head * ps + part] = make_float2(hm, nb);
-    s.PN[((size_t)head * 2 + 0) * ps + part] = part == 0 ? (float)t : 0.f;
     s.P[((size_t)head * 2 + 0) * ps + part] = make_float2(0.f, INFINITY);
   }
   head_barrier(bar, ++nbar * P, &timed_out);
@@ -815,38 +823,42 @@ __global__ __launch_bounds__(256) void nnls_coop_kernel(NnlsState s, int h0, int
   __syncthreads();
   const float thr = s.tol * fmaxf(hsmax, 1e-30f);
 
-  // power iteration for L = lambda_max(D^-1 G D^-1)
-  float* pnl = (float*)pst;
-  auto head_norm = [&](int parity) {
-    const float* pn = s.PN + ((size_t)head * 2 + parity) * ps;
-    for (int b = tid; b < P; b += 256) pnl[b] = ld_dev(pn + b);
-    __syncthreads();
-    float nrm = 0.f;
-    for (int b = 0; b < P; ++b) nrm += pnl[b];
-    __syncthreads();
-    return nrm;
-  };
-  for (int k = 0; k < kPow && !timed_out; ++k) {
-    const float nrm = head_norm(k & 1);
-    const float sc = nrm > 0.f ? rsqrtf(nrm) : 0.f;
+  // L: the Collatz-Wielandt bound on lambda_max(D^-1 G D^-1) (kCw); the iterate u lives in
+  // X (parity k & 1), the own rows' entries also in vr
+  float pmax = 0.f;
+  for (int k = 0; k < kCw && !timed_out; ++k) {
     const float* xin = s.X + ((size_t)head * 2 + (k & 1)) * t;
     float* xout = s.X + ((size_t)head * 2 + ((k + 1) & 1)) * t;
-    for (int j = tid; j < t; j += 256) xs[j] = ld_dev(xin + j) * sc * dinv[j];
+    for (int j = tid; j < t; j += 256) {
+      const float u = ld_dev(xin + j);
+      xs[j] = u * dinv[j];
+      if (j >= r0 && j < r1) vr[j - r0] = u;
+    }
     __syncthreads();
-    float part2 = 0.f;
     for (int i = r0 + wave; i < r1; i += 4) {
-      const float acc = row_dot(i);
-      const float y = acc * dinv[i];
+      const float y = row_dot(i) * dinv[i];
+      const float u = vr[i - r0];
       if (lane == 0) {
-        st_dev(xout + i, y);
-        part2 += y * y;
+        if (k + 1 < kCw) st_dev(xout + i, y + kCwShift * u);
+        else pmax = fmaxf(pmax, u > 0.f ? y / u : 0.f);
       }
     }
-    part2 = block_sum(part2, red);
-    if (tid == 0) st_dev(s.PN + ((size_t)head * 2 + ((k + 1) & 1)) * ps + part, part2);
+    if (k + 1 == kCw) {
+      pmax = block_max(pmax, red);
+      if (tid == 0) st_dev(s.PN + ((size_t)head * 2 + (kCw & 1)) * ps + part, pmax);
+    }
     barrier();
   }
-  const float L = 1.25f * sqrtf(head_norm(kPow & 1)) + 1e-30f;
+  float Lmax = 0.f;
+  {
+    float* pnl = (float*)pst;
+    const float* pn = s.PN + ((size_t)head * 2 + (kCw & 1)) * ps;
+    for (int b = tid; b < P; b += 256) pnl[b] = ld_dev(pn + b);
+    __syncthreads();
+    for (int b = 0; b < P; ++b) Lmax = fmaxf(Lmax, pnl[b]);
+    __syncthreads();
+  }
+  const float L = kCwPad * Lmax + 1e-30f;
 
   // accelerated projected gradient; iterate v_k in ring slot k % 3
   float tk = 1.f, gm = INFINITY;
