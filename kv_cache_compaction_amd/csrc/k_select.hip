@@ -21,6 +21,7 @@ namespace amc {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelB = 8;   // scores a thread has in flight at once (latency, not bandwidth, bounds the passes)
 
 __device__ __forceinline__ unsigned order_key(float f) {
   const unsigned u = __float_as_uint(f);
@@ -65,9 +66,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < Tk; j += kSelThreads) {
-      const unsigned u = order_key(sc[j]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    for (int j0 = tid; j0 < Tk; j0 += kSelThreads * kSelB) {
+      float f[kSelB];
+#pragma unroll
+      for (int b = 0; b < kSelB; ++b) {
+        const int j = j0 + b * kSelThreads;
+        f[b] = j < Tk ? sc[j] : 0.f;
+      }
+#pragma unroll
+      for (int b = 0; b < kSelB; ++b) {
+        const unsigned u = order_key(f[b]);
+        if (j0 + b * kSelThreads < Tk && (u & mask) == prefix)
+          atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     // the digit: the largest dg whose count from the top, sum_{k >= dg} hist[k], reaches
@@ -97,23 +108,36 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   const int seg = (Tk + kSelThreads - 1) / kSelThreads;
   const int j0 = min(Tk, tid * seg), j1 = min(Tk, j0 + seg);
   unsigned n_eq = 0, n_gt = 0;
-  for (int j = j0; j < j1; ++j) {
-    const unsigned u = order_key(sc[j]);
-    n_eq += u == prefix;
-    n_gt += u > prefix;
+  for (int jb = j0; jb < j1; jb += kSelB) {
+    float f[kSelB];
+#pragma unroll
+    for (int b = 0; b < kSelB; ++b) f[b] = jb + b < j1 ? sc[jb + b] : 0.f;
+#pragma unroll
+    for (int b = 0; b < kSelB; ++b) {
+      const unsigned u = order_key(f[b]);
+      n_eq += jb + b < j1 && u == prefix;
+      n_gt += jb + b < j1 && u > prefix;
+    }
   }
   unsigned eq_total, take_total;
   const unsigned eq_before = block_excl_scan(n_eq, &eq_total, wsum);
   const unsigned eq_take = eq_before >= remaining ? 0u : min(n_eq, remaining - eq_before);
   unsigned pos = block_excl_scan(n_gt + eq_take, &take_total, wsum);
   unsigned eq_seen = 0;
-  for (int j = j0; j < j1; ++j) {
-    const unsigned u = order_key(sc[j]);
-    bool take = u > prefix;
-    if (u == prefix) take = eq_seen++ < eq_take;
-    if (take) {
-      if (pos < (unsigned)t) out[pos] = j;
-      ++pos;
+  for (int jb = j0; jb < j1; jb += kSelB) {
+    float f[kSelB];
+#pragma unroll
+    for (int b = 0; b < kSelB; ++b) f[b] = jb + b < j1 ? sc[jb + b] : 0.f;
+#pragma unroll
+    for (int b = 0; b < kSelB; ++b) {
+      if (jb + b >= j1) break;
+      const unsigned u = order_key(f[b]);
+      bool take = u > prefix;
+      if (u == prefix) take = eq_seen++ < eq_take;
+      if (take) {
+        if (pos < (unsigned)t) out[pos] = jb + b;
+        ++pos;
+      }
     }
   }
 }
