@@ -1432,7 +1432,8 @@ __global__ __launch_bounds__(256) void trsm_back_update_kernel(double* R, const 
   }
 }
 
-// The whole backward solve in one launch when the factor has at most kBsMaxLd rows: each
+// The whole backward solve in one launch, for factors of at most kBsMaxLd rows and few heads
+// (the launcher's choice, below): each
 // workgroup owns kBsW columns of one head's right-hand side, holds them in LDS from the
 // first block step to the last and runs every step itself, so no two workgroups share
 // data. Step kb: Z_kb <- Linv_kk^T Z_kb (one entry per thread, Linv_kk staged in LDS and
@@ -2050,7 +2051,13 @@ hipError_t launch_fit_values(const FitArgs& a) {
                          0, st, pl.A, pl.R, pl.Linv, (const double*)pl.Dg, status, ld, d, kb,
                          nb);
   }
-  if (ld <= kBsMaxLd && d % kBsW == 0) {
+  // One launch pays while its workgroups fill the device about once: with few heads the
+  // per-step launches are a chain of short dependent launches, but with many heads every one
+  // of its workgroups re-reads its head's factor (8x the traffic of the per-step form, whose
+  // workgroups each take 32 columns), and the per-step launches are the faster form
+  const int ncu = device_cu_count();
+  const long long nbw = (long long)H * (d / kBsW);
+  if (ld <= kBsMaxLd && d % kBsW == 0 && nb >= 2 && ncu > 0 && nbw <= 2LL * ncu) {
     // one launch: each workgroup runs every step for its columns
     hipLaunchKernelGGL(trsm_back_cols_kernel, dim3(H * (d / kBsW)), dim3(512), 0, st, pl.R,
                        (const double*)pl.A, (const double*)pl.Linv, ld, d, nb, H);
