@@ -21,7 +21,10 @@ namespace amc {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelB = 8;   // scores a thread has in flight at once (latency, not bandwidth, bounds the passes)
+// Scores a thread has in flight at once: 8 where every thread has at least 16 keys (latency,
+// not bandwidth, bounds the passes), else 1 (with a few keys per thread the guarded batch
+// costs more than it hides: 26 against 16 us for 512 heads of 2048 keys)
+constexpr int kSelBatchMinKeys = 16 * kSelThreads;
 
 __device__ __forceinline__ unsigned order_key(float f) {
   const unsigned u = __float_as_uint(f);
@@ -51,6 +54,7 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* total,
   return before + x - v;
 }
 
+template <int kSelB>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ score,
                                                                   int32_t* __restrict__ idx,
                                                                   int Tk, int t) {
@@ -170,8 +174,12 @@ static void launch_gather(const SelectArgs& a) {
 }
 
 hipError_t launch_select(const SelectArgs& a) {
-  hipLaunchKernelGGL(topk_select_kernel, dim3(a.heads), dim3(kSelThreads), 0, a.stream, a.score,
-                     a.idx, a.T, a.t);
+  if (a.T >= kSelBatchMinKeys)
+    hipLaunchKernelGGL(topk_select_kernel<8>, dim3(a.heads), dim3(kSelThreads), 0, a.stream, a.score,
+                       a.idx, a.T, a.t);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<1>, dim3(a.heads), dim3(kSelThreads), 0, a.stream, a.score,
+                       a.idx, a.T, a.t);
   if (a.bf16) {
     if (a.d == 128) launch_gather<bf16, 128>(a); else launch_gather<bf16, 64>(a);
   } else {
